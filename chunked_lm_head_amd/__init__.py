@@ -1,0 +1,329 @@
+"""Python binding of liblmhead.so, the deterministic chunked LM-head + loss
+library for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI (include/lmhead.h). PyTorch supplies device memory
+and the current stream. There is no CPU fallback: if the library is missing,
+every entry raises.
+
+Two layers:
+
+* ``lmhead_workspace_size``, ``lmhead_loss_fwd``, ``lmhead_logprob``,
+  ``lmhead_support_logprob_kl``, ``lmhead_loss_bwd``,
+  ``lmhead_status_string``, ``lmhead_read_device_error``: the C entry points
+  under the same names. Pointer arguments accept a torch tensor, an integer
+  address or None; the return value is the C status code.
+* ``ce_loss``, ``logprob``, ``support_logprob_kl`` (and their autograd
+  functions): allocate outputs and workspace with torch, call the entry
+  points and raise ``LMHeadError`` on a nonzero status.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblmhead.so")
+
+LMHEAD_OK = 0
+LMHEAD_ERR_ARG = 1
+LMHEAD_ERR_SHAPE = 2
+LMHEAD_ERR_ALIGN = 3
+LMHEAD_ERR_WORKSPACE = 4
+LMHEAD_ERR_DEVICE = 5
+LMHEAD_ERR_HIP = 6
+
+ENTRY_CE_MEAN = 0
+ENTRY_CE_SUM = 1
+ENTRY_LOGPROB = 2
+ENTRY_SUPPORT = 3
+
+DEVERR_LABEL = 1
+DEVERR_CANDIDATE = 2
+
+IGNORE_INDEX = -100
+
+
+class lmhead_problem(ctypes.Structure):
+    _fields_ = [
+        ("n", ctypes.c_int64),
+        ("hidden", ctypes.c_int64),
+        ("vocab", ctypes.c_int64),
+        ("chunk", ctypes.c_int64),
+        ("num_valid", ctypes.c_int64),
+        ("k", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
+    ]
+
+
+def problem(n: int, hidden: int, vocab: int, chunk: int, num_valid: int = -1, k: int = 1,
+            flags: int = 0) -> lmhead_problem:
+    return lmhead_problem(n, hidden, vocab, chunk, num_valid, k, flags)
+
+
+class LMHeadError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lmhead_status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load liblmhead.so; raises if it has not been built (no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m chunked_lm_head_amd.build` "
+                "(or __graft_entry__.build()); there is no CPU fallback")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(lmhead_problem)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        L.lmhead_workspace_size.argtypes = [P, i32, i32]
+        L.lmhead_workspace_size.restype = sz
+        L.lmhead_loss_fwd.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.lmhead_logprob.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.lmhead_support_logprob_kl.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.lmhead_loss_bwd.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.lmhead_status_string.argtypes = [i32]
+        L.lmhead_status_string.restype = ctypes.c_char_p
+        L.lmhead_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32),
+                                               ctypes.POINTER(ctypes.c_int64)]
+        for f in (L.lmhead_loss_fwd, L.lmhead_logprob, L.lmhead_support_logprob_kl,
+                  L.lmhead_loss_bwd, L.lmhead_read_device_error):
+            f.restype = i32
+        _lib = L
+    return _lib
+
+
+def _p(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+# ----------------------------------------------------------- C entry points
+
+def lmhead_workspace_size(p: lmhead_problem, entry: int, with_backward: int) -> int:
+    return int(lib().lmhead_workspace_size(ctypes.byref(p), entry, int(with_backward)))
+
+
+def lmhead_loss_fwd(p, entry, H, W, targets, loss, lse, workspace, workspace_bytes, stream=None) -> int:
+    return lib().lmhead_loss_fwd(ctypes.byref(p), entry, _p(H), _p(W), _p(targets), _p(loss),
+                                 _p(lse), _p(workspace), workspace_bytes, _stream(stream))
+
+
+def lmhead_logprob(p, H, W, targets, logp, lse, workspace, workspace_bytes, stream=None) -> int:
+    return lib().lmhead_logprob(ctypes.byref(p), _p(H), _p(W), _p(targets), _p(logp), _p(lse),
+                                _p(workspace), workspace_bytes, _stream(stream))
+
+
+def lmhead_support_logprob_kl(p, H, W, ids, ref_logq, lp, kl, lse, workspace, workspace_bytes,
+                              stream=None) -> int:
+    return lib().lmhead_support_logprob_kl(ctypes.byref(p), _p(H), _p(W), _p(ids), _p(ref_logq),
+                                           _p(lp), _p(kl), _p(lse), _p(workspace), workspace_bytes,
+                                           _stream(stream))
+
+
+def lmhead_loss_bwd(p, entry, H, W, targets_or_ids, ref_logq, lse, saved_lp, grad, grad_kl, dH, dW,
+                    workspace, workspace_bytes, stream=None) -> int:
+    return lib().lmhead_loss_bwd(ctypes.byref(p), entry, _p(H), _p(W), _p(targets_or_ids),
+                                 _p(ref_logq), _p(lse), _p(saved_lp), _p(grad), _p(grad_kl), _p(dH),
+                                 _p(dW), _p(workspace), workspace_bytes, _stream(stream))
+
+
+def lmhead_status_string(status: int) -> str:
+    return lib().lmhead_status_string(int(status)).decode()
+
+
+def lmhead_read_device_error(workspace, stream=None):
+    code = ctypes.c_int32(0)
+    row = ctypes.c_int64(0)
+    st = lib().lmhead_read_device_error(_p(workspace), _stream(stream), ctypes.byref(code),
+                                        ctypes.byref(row))
+    if st != LMHEAD_OK:
+        raise LMHeadError(st, "lmhead_read_device_error")
+    return int(code.value), int(row.value)
+
+
+# ------------------------------------------------------------- torch helpers
+
+def _check_inputs(H: torch.Tensor, W: torch.Tensor, idx: torch.Tensor):
+    for name, t in (("H", H), ("W", W), ("targets/ids", idx)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a tensor on a GPU device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if H.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
+        raise ValueError("H and W must be bfloat16")
+    if idx.dtype != torch.int32:
+        raise ValueError("targets / candidate ids must be int32")
+    if H.dim() != 2 or W.dim() != 2 or H.shape[1] != W.shape[1]:
+        raise ValueError("expected H [n, hidden] and W [vocab, hidden]")
+
+
+def workspace(p: lmhead_problem, entry: int, with_backward: bool, device) -> torch.Tensor:
+    nbytes = lmhead_workspace_size(p, entry, int(with_backward))
+    if nbytes == 0:
+        raise LMHeadError(LMHEAD_ERR_SHAPE, "lmhead_workspace_size")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _ok(status: int, where: str):
+    if status != LMHEAD_OK:
+        raise LMHeadError(status, where)
+
+
+def ce_loss_forward(H, W, targets, chunk: int, reduction: str = "mean", num_valid: int = -1,
+                    ws: Optional[torch.Tensor] = None):
+    """Returns (loss fp32 [], lse fp32 [n], workspace)."""
+    _check_inputs(H, W, targets)
+    entry = ENTRY_CE_MEAN if reduction == "mean" else ENTRY_CE_SUM
+    p = problem(H.shape[0], H.shape[1], W.shape[0], chunk, num_valid)
+    if ws is None:
+        ws = workspace(p, entry, False, H.device)
+    loss = torch.empty(1, dtype=torch.float32, device=H.device)
+    lse = torch.empty(H.shape[0], dtype=torch.float32, device=H.device)
+    _ok(lmhead_loss_fwd(p, entry, H, W, targets, loss, lse, ws, ws.numel()), "lmhead_loss_fwd")
+    return loss[0], lse, ws
+
+
+def logprob_forward(H, W, targets, chunk: int, ws: Optional[torch.Tensor] = None):
+    """Returns (logp fp32 [n], lse fp32 [n], workspace)."""
+    _check_inputs(H, W, targets)
+    p = problem(H.shape[0], H.shape[1], W.shape[0], chunk)
+    if ws is None:
+        ws = workspace(p, ENTRY_LOGPROB, False, H.device)
+    logp = torch.empty(H.shape[0], dtype=torch.float32, device=H.device)
+    lse = torch.empty(H.shape[0], dtype=torch.float32, device=H.device)
+    _ok(lmhead_logprob(p, H, W, targets, logp, lse, ws, ws.numel()), "lmhead_logprob")
+    return logp, lse, ws
+
+
+def support_forward(H, W, ids, ref_logq, chunk: int, ws: Optional[torch.Tensor] = None):
+    """Returns (lp fp32 [n, k], kl fp32 [n] or None, lse fp32 [n], workspace)."""
+    _check_inputs(H, W, ids)
+    n, k = ids.shape
+    p = problem(n, H.shape[1], W.shape[0], chunk, -1, k)
+    if ws is None:
+        ws = workspace(p, ENTRY_SUPPORT, False, H.device)
+    lp = torch.empty(n, k, dtype=torch.float32, device=H.device)
+    kl = torch.empty(n, dtype=torch.float32, device=H.device) if ref_logq is not None else None
+    lse = torch.empty(n, dtype=torch.float32, device=H.device)
+    _ok(lmhead_support_logprob_kl(p, H, W, ids, ref_logq, lp, kl, lse, ws, ws.numel()),
+        "lmhead_support_logprob_kl")
+    return lp, kl, lse, ws
+
+
+def backward(entry: int, H, W, idx, lse, grad, chunk: int, *, ref_logq=None, saved_lp=None,
+             grad_kl=None, num_valid: int = -1, need_dH: bool = True, need_dW: bool = True,
+             ws: Optional[torch.Tensor] = None, dH=None, dW=None):
+    """Returns (dH bf16 [n, hidden] or None, dW bf16 [vocab, hidden] or None)."""
+    _check_inputs(H, W, idx)
+    k = idx.shape[1] if entry == ENTRY_SUPPORT else 1
+    p = problem(H.shape[0], H.shape[1], W.shape[0], chunk, num_valid, k)
+    if ws is None:
+        ws = workspace(p, entry, True, H.device)
+    if need_dH and dH is None:
+        dH = torch.empty_like(H)
+    if need_dW and dW is None:
+        dW = torch.empty_like(W)
+    _ok(lmhead_loss_bwd(p, entry, H, W, idx, ref_logq, lse, saved_lp, grad, grad_kl,
+                        dH if need_dH else None, dW if need_dW else None, ws, ws.numel()),
+        "lmhead_loss_bwd")
+    return (dH if need_dH else None), (dW if need_dW else None)
+
+
+# --------------------------------------------------------------- autograd
+
+class ChunkedLMHeadCE(torch.autograd.Function):
+    """Cross-entropy of softmax(H W^T) against targets, mean or sum over valid rows."""
+
+    @staticmethod
+    def forward(ctx, H, W, targets, chunk, reduction="mean", num_valid=-1):
+        loss, lse, _ = ce_loss_forward(H, W, targets, chunk, reduction, num_valid)
+        ctx.save_for_backward(H, W, targets, lse)
+        ctx.cfg = (chunk, reduction, num_valid)
+        return loss
+
+    @staticmethod
+    def backward(ctx, g):
+        H, W, targets, lse = ctx.saved_tensors
+        chunk, reduction, num_valid = ctx.cfg
+        entry = ENTRY_CE_MEAN if reduction == "mean" else ENTRY_CE_SUM
+        grad = g.reshape(1).to(torch.float32).contiguous()
+        dH, dW = backward(entry, H, W, targets, lse, grad, chunk, num_valid=num_valid,
+                          need_dH=ctx.needs_input_grad[0], need_dW=ctx.needs_input_grad[1])
+        return dH, dW, None, None, None, None
+
+
+class ChunkedLMHeadLogprob(torch.autograd.Function):
+    """Per-token log-probability of the target under softmax(H W^T)."""
+
+    @staticmethod
+    def forward(ctx, H, W, targets, chunk):
+        logp, lse, _ = logprob_forward(H, W, targets, chunk)
+        ctx.save_for_backward(H, W, targets, lse)
+        ctx.chunk = chunk
+        return logp
+
+    @staticmethod
+    def backward(ctx, g):
+        H, W, targets, lse = ctx.saved_tensors
+        dH, dW = backward(ENTRY_LOGPROB, H, W, targets, lse, g.to(torch.float32).contiguous(),
+                          ctx.chunk, need_dH=ctx.needs_input_grad[0],
+                          need_dW=ctx.needs_input_grad[1])
+        return dH, dW, None, None
+
+
+class ChunkedLMHeadSupport(torch.autograd.Function):
+    """Full-vocabulary log-probabilities of K candidates per row and KL(q || p_hat)."""
+
+    @staticmethod
+    def forward(ctx, H, W, ids, ref_logq, chunk):
+        lp, kl, lse, _ = support_forward(H, W, ids, ref_logq, chunk)
+        ctx.save_for_backward(H, W, ids, ref_logq, lse, lp)
+        ctx.chunk = chunk
+        ctx.has_kl = kl is not None
+        if kl is None:
+            kl = torch.zeros(H.shape[0], dtype=torch.float32, device=H.device)
+        return lp, kl
+
+    @staticmethod
+    def backward(ctx, g_lp, g_kl):
+        H, W, ids, ref_logq, lse, lp = ctx.saved_tensors
+        gl = g_lp.to(torch.float32).contiguous() if g_lp is not None else None
+        gk = g_kl.to(torch.float32).contiguous() if (g_kl is not None and ctx.has_kl) else None
+        dH, dW = backward(ENTRY_SUPPORT, H, W, ids, lse, gl, ctx.chunk,
+                          ref_logq=ref_logq if ctx.has_kl else None,
+                          saved_lp=lp if ctx.has_kl else None, grad_kl=gk,
+                          need_dH=ctx.needs_input_grad[0], need_dW=ctx.needs_input_grad[1])
+        return dH, dW, None, None, None
+
+
+def ce_loss(H, W, targets, chunk: int = 8192, reduction: str = "mean", num_valid: int = -1):
+    return ChunkedLMHeadCE.apply(H, W, targets, chunk, reduction, num_valid)
+
+
+def logprob(H, W, targets, chunk: int = 8192):
+    return ChunkedLMHeadLogprob.apply(H, W, targets, chunk)
+
+
+def support_logprob_kl(H, W, ids, ref_logq, chunk: int = 8192):
+    return ChunkedLMHeadSupport.apply(H, W, ids, ref_logq, chunk)

@@ -1,0 +1,358 @@
+// lmhead_api.hip — host side of the C ABI declared in include/lmhead.h:
+// argument validation, the workspace plan and the launch sequence of each
+// entry. Host-checkable errors return before anything is enqueued; nothing
+// here allocates device memory or synchronises (except
+// lmhead_read_device_error).
+#include <limits.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "lmhead.h"
+#include "lmhead_kernels.h"
+
+namespace {
+
+using namespace lmhead;
+
+constexpr int64_t kMaxRows = int64_t(1) << 30;
+constexpr int64_t kMaxVocab = int64_t(1) << 30;
+constexpr int64_t kMaxHidden = 65536;
+constexpr int kMaxCandidates = 1024;
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+struct Layout {
+    int64_t n, n_pad, hidden, vocab, chunk, w_pad, tiles_v, k;
+    // forward regions
+    size_t hdr, lse, part, zg, rows;
+    // backward regions
+    size_t coef_a, coef_c, Ht, G, Gt, Wt, dh_acc;
+    size_t fwd_total, bwd_total;
+};
+
+int validate_problem(const lmhead_problem* p, int entry) {
+    if (p == nullptr) return LMHEAD_ERR_ARG;
+    if (entry < LMHEAD_ENTRY_CE_MEAN || entry > LMHEAD_ENTRY_SUPPORT) return LMHEAD_ERR_ARG;
+    if (p->flags != 0) return LMHEAD_ERR_ARG;
+    if (p->n < 0 || p->n > kMaxRows) return LMHEAD_ERR_SHAPE;
+    if (p->hidden < 64 || p->hidden > kMaxHidden || p->hidden % 64 != 0) return LMHEAD_ERR_SHAPE;
+    if (p->vocab < 1 || p->vocab > kMaxVocab) return LMHEAD_ERR_SHAPE;
+    if (p->chunk < 256 || p->chunk % 256 != 0 || p->chunk > kMaxVocab + 256) return LMHEAD_ERR_SHAPE;
+    if (p->num_valid < -1) return LMHEAD_ERR_SHAPE;
+    if (entry == LMHEAD_ENTRY_SUPPORT && (p->k < 1 || p->k > kMaxCandidates)) return LMHEAD_ERR_SHAPE;
+    // one workgroup per 256 x 256 tile: keep every grid within 2^31 - 1
+    if (cdiv(p->n, kTile) * cdiv(p->vocab, kTile) > INT_MAX) return LMHEAD_ERR_SHAPE;
+    return LMHEAD_OK;
+}
+
+Layout plan(const lmhead_problem& p, int entry) {
+    Layout L{};
+    L.n = p.n;
+    L.n_pad = round_up(p.n > 0 ? p.n : 1, kTile);
+    L.hidden = p.hidden;
+    L.vocab = p.vocab;
+    L.chunk = p.chunk;
+    L.w_pad = round_up(p.chunk < p.vocab ? p.chunk : p.vocab, kTile);
+    L.tiles_v = cdiv(p.vocab, kTile);
+    L.k = entry == LMHEAD_ENTRY_SUPPORT ? p.k : 1;
+    size_t off = 0;
+    auto take = [&off](int64_t bytes) {
+        const size_t o = off;
+        off += (size_t)round_up(bytes > 0 ? bytes : 0, 256);
+        return o;
+    };
+    L.hdr = take(256);
+    const size_t after_hdr = off;
+    L.lse = take(4 * L.n);
+    L.part = take(8 * L.tiles_v * L.n);
+    L.zg = take(4 * L.n * L.k);
+    L.rows = take(4 * L.n);
+    L.fwd_total = off;
+    off = after_hdr;
+    L.coef_a = take(4 * L.n_pad);
+    L.coef_c = take(4 * L.n * L.k);
+    L.Ht = take(2 * L.hidden * L.n_pad);
+    L.G = take(2 * L.n_pad * L.w_pad);
+    L.Gt = take(2 * L.w_pad * L.n_pad);
+    L.Wt = take(2 * L.hidden * L.w_pad);
+    L.dh_acc = take(4 * L.n * L.hidden);
+    L.bwd_total = off > L.fwd_total ? off : L.fwd_total;
+    return L;
+}
+
+bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return LMHEAD_ERR_DEVICE;
+    static int cache[256];  // 0 unknown, 1 gfx950, 2 other
+    if (dev < 256 && cache[dev] != 0) return cache[dev] == 1 ? LMHEAD_OK : LMHEAD_ERR_DEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return LMHEAD_ERR_DEVICE;
+    const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 256) cache[dev] = ok ? 1 : 2;
+    return ok ? LMHEAD_OK : LMHEAD_ERR_DEVICE;
+}
+
+int launched() { return hipGetLastError() == hipSuccess ? LMHEAD_OK : LMHEAD_ERR_HIP; }
+
+int grid_1d(int64_t items, int per_block, int cap) {
+    int64_t g = cdiv(items, per_block);
+    if (g < 1) g = 1;
+    return (int)(g < cap ? g : cap);
+}
+
+void fill_u32(void* p, int64_t count, uint32_t value, hipStream_t s) {
+    if (count <= 0) return;
+    fill_u32_kernel<<<grid_1d(count, kThreads, 4096), kThreads, 0, s>>>((uint32_t*)p, count, value);
+}
+
+// Validation shared by the three forward entries.
+int forward(const lmhead_problem* p, int entry, const void* H, const void* W, const int32_t* ids,
+            const float* ref_logq, float* row_out, float* kl, float* lse_out, float* loss,
+            void* ws, size_t ws_bytes, void* stream) {
+    int st = validate_problem(p, entry);
+    if (st != LMHEAD_OK) return st;
+    const bool ce = entry == LMHEAD_ENTRY_CE_MEAN || entry == LMHEAD_ENTRY_CE_SUM;
+    if (ws == nullptr) return LMHEAD_ERR_ARG;
+    if (ce && loss == nullptr) return LMHEAD_ERR_ARG;
+    if (p->n > 0) {
+        if (H == nullptr || W == nullptr || ids == nullptr) return LMHEAD_ERR_ARG;
+        if (!ce && row_out == nullptr) return LMHEAD_ERR_ARG;
+    }
+    if (kl != nullptr && ref_logq == nullptr) return LMHEAD_ERR_ARG;
+    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(ws, 256)) return LMHEAD_ERR_ALIGN;
+    const Layout L = plan(*p, entry);
+    if (ws_bytes < L.fwd_total) return LMHEAD_ERR_WORKSPACE;
+    st = check_device();
+    if (st != LMHEAD_OK) return st;
+
+    hipStream_t s = (hipStream_t)stream;
+    char* w = (char*)ws;
+    int32_t* hdr = (int32_t*)(w + L.hdr);
+    init_header_kernel<<<1, 64, 0, s>>>(hdr);
+    if (L.n == 0) {
+        if (loss) fill_u32(loss, 1, 0u, s);
+        return launched();
+    }
+    const bool support = entry == LMHEAD_ENTRY_SUPPORT;
+    scan_labels_kernel<<<grid_1d(L.n, kThreads, 1024), kThreads, 0, s>>>(ids, L.n, (int)L.k, L.vocab,
+                                                                          support ? 1 : 0, hdr);
+    FwdTilesArgs fa;
+    fa.H = (const bf16_bits*)H;
+    fa.W = (const bf16_bits*)W;
+    fa.n = L.n;
+    fa.hidden = L.hidden;
+    fa.vocab = L.vocab;
+    fa.tiles_m = cdiv(L.n, kTile);
+    fa.tiles_n = L.tiles_v;
+    fa.ids = ids;
+    fa.k = (int)L.k;
+    fa.part = (float2*)(w + L.part);
+    fa.zg = (float*)(w + L.zg);
+    fwd_tiles_kernel<<<(unsigned)(fa.tiles_m * fa.tiles_n), kThreads, 0, s>>>(fa);
+
+    FinalizeArgs fin;
+    fin.part = fa.part;
+    fin.n = L.n;
+    fin.tiles_n = L.tiles_v;
+    fin.vocab = L.vocab;
+    fin.ids = ids;
+    fin.k = (int)L.k;
+    fin.entry = entry;
+    fin.zg = fa.zg;
+    fin.ref_logq = ref_logq;
+    fin.lse = lse_out != nullptr ? lse_out : (float*)(w + L.lse);
+    fin.row_out = ce ? (float*)(w + L.rows) : row_out;
+    fin.kl = kl;
+    finalize_rows_kernel<<<grid_1d(L.n, kThreads, INT_MAX), kThreads, 0, s>>>(fin);
+    if (ce)
+        ce_reduce_kernel<<<1, kThreads, 0, s>>>(fin.row_out, L.n, hdr, p->num_valid,
+                                                entry == LMHEAD_ENTRY_CE_MEAN ? 1 : 0, loss);
+    return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lmhead_workspace_size(const lmhead_problem* p, int entry, int with_backward) {
+    if (validate_problem(p, entry) != LMHEAD_OK) return 0;
+    const Layout L = plan(*p, entry);
+    return with_backward ? L.bwd_total : L.fwd_total;
+}
+
+int lmhead_loss_fwd(const lmhead_problem* p, int entry, const void* H, const void* W,
+                    const int32_t* targets, float* loss, float* lse, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    if (entry != LMHEAD_ENTRY_CE_MEAN && entry != LMHEAD_ENTRY_CE_SUM) return LMHEAD_ERR_ARG;
+    return forward(p, entry, H, W, targets, nullptr, nullptr, nullptr, lse, loss, workspace,
+                   workspace_bytes, stream);
+}
+
+int lmhead_logprob(const lmhead_problem* p, const void* H, const void* W, const int32_t* targets,
+                   float* logp, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    return forward(p, LMHEAD_ENTRY_LOGPROB, H, W, targets, nullptr, logp, nullptr, lse, nullptr,
+                   workspace, workspace_bytes, stream);
+}
+
+int lmhead_support_logprob_kl(const lmhead_problem* p, const void* H, const void* W,
+                              const int32_t* ids, const float* ref_logq, float* lp, float* kl,
+                              float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    return forward(p, LMHEAD_ENTRY_SUPPORT, H, W, ids, ref_logq, lp, kl, lse, nullptr, workspace,
+                   workspace_bytes, stream);
+}
+
+int lmhead_loss_bwd(const lmhead_problem* p, int entry, const void* H, const void* W,
+                    const int32_t* ids, const float* ref_logq, const float* lse,
+                    const float* saved_lp, const float* grad, const float* grad_kl, void* dH,
+                    void* dW, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = validate_problem(p, entry);
+    if (st != LMHEAD_OK) return st;
+    const bool support = entry == LMHEAD_ENTRY_SUPPORT;
+    if (workspace == nullptr) return LMHEAD_ERR_ARG;
+    if (p->n > 0) {
+        if (H == nullptr || W == nullptr || ids == nullptr || lse == nullptr) return LMHEAD_ERR_ARG;
+        if (!support && grad == nullptr) return LMHEAD_ERR_ARG;
+        if (support && grad_kl != nullptr && (ref_logq == nullptr || saved_lp == nullptr))
+            return LMHEAD_ERR_ARG;
+    }
+    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16) ||
+        !aligned(workspace, 256))
+        return LMHEAD_ERR_ALIGN;
+    const Layout L = plan(*p, entry);
+    if (workspace_bytes < L.bwd_total) return LMHEAD_ERR_WORKSPACE;
+    st = check_device();
+    if (st != LMHEAD_OK) return st;
+    if (dH == nullptr && dW == nullptr) return LMHEAD_OK;
+
+    hipStream_t s = (hipStream_t)stream;
+    char* w = (char*)workspace;
+    int32_t* hdr = (int32_t*)(w + L.hdr);
+    init_header_kernel<<<1, 64, 0, s>>>(hdr);
+    if (L.n == 0) {
+        if (dW != nullptr) fill_u32(dW, L.vocab * L.hidden / 2, 0u, s);
+        return launched();
+    }
+    scan_labels_kernel<<<grid_1d(L.n, kThreads, 1024), kThreads, 0, s>>>(ids, L.n, (int)L.k, L.vocab,
+                                                                          support ? 1 : 0, hdr);
+    CoeffArgs ca;
+    ca.entry = entry;
+    ca.n = L.n;
+    ca.n_pad = L.n_pad;
+    ca.vocab = L.vocab;
+    ca.k = (int)L.k;
+    ca.ids = ids;
+    ca.ref_logq = ref_logq;
+    ca.saved_lp = saved_lp;
+    ca.grad = grad;
+    ca.grad_kl = (support && ref_logq != nullptr && saved_lp != nullptr) ? grad_kl : nullptr;
+    ca.hdr = hdr;
+    ca.num_valid = p->num_valid;
+    ca.coef_a = (float*)(w + L.coef_a);
+    ca.coef_c = (float*)(w + L.coef_c);
+    coeffs_kernel<<<grid_1d(L.n_pad, kThreads, INT_MAX), kThreads, 0, s>>>(ca);
+
+    bf16_bits* Ht = (bf16_bits*)(w + L.Ht);
+    bf16_bits* G = (bf16_bits*)(w + L.G);
+    bf16_bits* Gt = (bf16_bits*)(w + L.Gt);
+    bf16_bits* Wt = (bf16_bits*)(w + L.Wt);
+    if (dW != nullptr) {
+        dim3 grid((unsigned)(L.hidden / 64), (unsigned)(L.n_pad / 64));
+        transpose_kernel<<<grid, kThreads, 0, s>>>((const bf16_bits*)H, L.hidden, L.n, L.hidden, Ht,
+                                                   L.n_pad);
+    }
+    const int64_t nchunks = cdiv(L.vocab, L.chunk);
+    const int64_t tiles_rows = L.n_pad / kTile;
+    const int64_t tiles_hidden = cdiv(L.hidden, kTile);
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const int64_t v0 = c * L.chunk;
+        const int64_t width = (L.vocab - v0) < L.chunk ? (L.vocab - v0) : L.chunk;
+        const int64_t w_pad = round_up(width, kTile);
+        const bf16_bits* Wc = (const bf16_bits*)W + v0 * L.hidden;
+
+        LogitGradArgs ga;
+        ga.H = (const bf16_bits*)H;
+        ga.Wc = Wc;
+        ga.n = L.n;
+        ga.n_pad = L.n_pad;
+        ga.hidden = L.hidden;
+        ga.v0 = v0;
+        ga.width = width;
+        ga.w_pad = w_pad;
+        ga.tiles_m = tiles_rows;
+        ga.tiles_n = w_pad / kTile;
+        ga.coef_a = ca.coef_a;
+        ga.coef_c = ca.coef_c;
+        ga.ids = ids;
+        ga.k = (int)L.k;
+        ga.lse = lse;
+        ga.G = dH != nullptr ? G : nullptr;
+        ga.Gt = dW != nullptr ? Gt : nullptr;
+        bwd_logit_grad_kernel<<<(unsigned)(ga.tiles_m * ga.tiles_n), kThreads, 0, s>>>(ga);
+
+        if (dW != nullptr) {
+            DwArgs da;
+            da.Gt = Gt;
+            da.Ht = Ht;
+            da.n_pad = L.n_pad;
+            da.hidden = L.hidden;
+            da.v0 = v0;
+            da.width = width;
+            da.w_pad = w_pad;
+            da.tiles_m = w_pad / kTile;
+            da.tiles_n = tiles_hidden;
+            da.dW = (bf16_bits*)dW;
+            bwd_dw_kernel<<<(unsigned)(da.tiles_m * da.tiles_n), kThreads, 0, s>>>(da);
+        }
+        if (dH != nullptr) {
+            dim3 grid((unsigned)(L.hidden / 64), (unsigned)(w_pad / 64));
+            transpose_kernel<<<grid, kThreads, 0, s>>>(Wc, L.hidden, width, L.hidden, Wt, w_pad);
+            DhArgs ha;
+            ha.G = G;
+            ha.Wt = Wt;
+            ha.n = L.n;
+            ha.n_pad = L.n_pad;
+            ha.hidden = L.hidden;
+            ha.w_pad = w_pad;
+            ha.tiles_m = tiles_rows;
+            ha.tiles_n = tiles_hidden;
+            ha.first = c == 0;
+            ha.last = c == nchunks - 1;
+            ha.dh_acc = (float*)(w + L.dh_acc);
+            ha.dH = (bf16_bits*)dH;
+            bwd_dh_kernel<<<(unsigned)(ha.tiles_m * ha.tiles_n), kThreads, 0, s>>>(ha);
+        }
+    }
+    return launched();
+}
+
+const char* lmhead_status_string(int status) {
+    switch (status) {
+        case LMHEAD_OK: return "ok";
+        case LMHEAD_ERR_ARG: return "invalid argument (NULL pointer, unknown entry or nonzero flags)";
+        case LMHEAD_ERR_SHAPE: return "unsupported problem size";
+        case LMHEAD_ERR_ALIGN: return "misaligned pointer (16 bytes; workspace 256 bytes)";
+        case LMHEAD_ERR_WORKSPACE: return "workspace too small";
+        case LMHEAD_ERR_DEVICE: return "no gfx950 (MI355X) device is current";
+        case LMHEAD_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int lmhead_read_device_error(const void* workspace, void* stream, int32_t* code, int64_t* row) {
+    if (workspace == nullptr || code == nullptr || row == nullptr) return LMHEAD_ERR_ARG;
+    if (!aligned(workspace, 256)) return LMHEAD_ERR_ALIGN;
+    int st = check_device();
+    if (st != LMHEAD_OK) return st;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return LMHEAD_ERR_HIP;
+    int32_t h[3];
+    if (hipMemcpy(h, workspace, sizeof h, hipMemcpyDeviceToHost) != hipSuccess) return LMHEAD_ERR_HIP;
+    *code = h[kHdrErrCode];
+    *row = h[kHdrErrRow] == INT_MAX ? -1 : (int64_t)h[kHdrErrRow];
+    return LMHEAD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// lmhead_kernels.h — kernel argument blocks and launch declarations shared by
+// the kernels and the host-side plan (lmhead_api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_core.h"
+
+namespace lmhead {
+
+// entry kinds (same values as enum lmhead_entry)
+constexpr int kEntryCeMean = 0;
+constexpr int kEntryCeSum = 1;
+constexpr int kEntryLogprob = 2;
+constexpr int kEntrySupport = 3;
+
+// int32 words at the start of every workspace
+constexpr int kHdrErrCode = 0;
+constexpr int kHdrErrRow = 1;
+constexpr int kHdrCount = 2;
+constexpr int kDevErrLabel = 1;
+constexpr int kDevErrCandidate = 2;
+
+struct FwdTilesArgs {
+    const bf16_bits* H;
+    const bf16_bits* W;
+    int64_t n, hidden, vocab;
+    int64_t tiles_m, tiles_n;
+    const int32_t* ids;   // labels [n] (k = 1) or candidate ids [n, k]
+    int k;
+    float2* part;         // [tiles_n, n] (max, sum) per (tile, row)
+    float* zg;            // [n, k] logits at the ids
+};
+
+struct FinalizeArgs {
+    const float2* part;
+    int64_t n, tiles_n, vocab;
+    const int32_t* ids;
+    int k;
+    int entry;
+    const float* zg;
+    const float* ref_logq;  // support KL only
+    float* lse;             // [n]
+    float* row_out;         // CE: loss rows; logprob: logp [n]; support: lp [n, k]
+    float* kl;              // support: [n] or null
+};
+
+struct CoeffArgs {
+    int entry;
+    int64_t n, n_pad, vocab;
+    int k;
+    const int32_t* ids;
+    const float* ref_logq;
+    const float* saved_lp;
+    const float* grad;
+    const float* grad_kl;
+    const int32_t* hdr;
+    int64_t num_valid;
+    float* coef_a;   // [n_pad]
+    float* coef_c;   // [n, k]
+};
+
+struct LogitGradArgs {
+    const bf16_bits* H;
+    const bf16_bits* Wc;   // first row of the chunk
+    int64_t n, n_pad, hidden;
+    int64_t v0, width, w_pad;
+    int64_t tiles_m, tiles_n;
+    const float* coef_a;
+    const float* coef_c;
+    const int32_t* ids;
+    int k;
+    const float* lse;
+    bf16_bits* G;          // [n_pad, w_pad] or null
+    bf16_bits* Gt;         // [w_pad, n_pad] or null
+};
+
+struct DwArgs {
+    const bf16_bits* Gt;   // [w_pad, n_pad]
+    const bf16_bits* Ht;   // [hidden, n_pad]
+    int64_t n_pad, hidden, v0, width, w_pad;
+    int64_t tiles_m, tiles_n;
+    bf16_bits* dW;         // [vocab, hidden]
+};
+
+struct DhArgs {
+    const bf16_bits* G;    // [n_pad, w_pad]
+    const bf16_bits* Wt;   // [hidden, w_pad]
+    int64_t n, n_pad, hidden, w_pad;
+    int64_t tiles_m, tiles_n;
+    int first, last;
+    float* dh_acc;         // [n, hidden]
+    bf16_bits* dH;         // [n, hidden]
+};
+
+__global__ void init_header_kernel(int32_t* hdr);
+__global__ void scan_labels_kernel(const int32_t* ids, int64_t n, int k, int64_t vocab, int support,
+                                   int32_t* hdr);
+__global__ void fill_u32_kernel(uint32_t* p, int64_t count, uint32_t value);
+__global__ void fwd_tiles_kernel(FwdTilesArgs a);
+__global__ void finalize_rows_kernel(FinalizeArgs a);
+__global__ void ce_reduce_kernel(const float* rows, int64_t n, const int32_t* hdr, int64_t num_valid,
+                                 int mean, float* loss);
+__global__ void coeffs_kernel(CoeffArgs a);
+__global__ void bwd_logit_grad_kernel(LogitGradArgs a);
+__global__ void bwd_dw_kernel(DwArgs a);
+__global__ void bwd_dh_kernel(DhArgs a);
+__global__ void transpose_kernel(const bf16_bits* in, int64_t ld_in, int64_t rows, int64_t cols,
+                                 bf16_bits* out, int64_t rows_pad);
+
+}  // namespace lmhead

@@ -1,0 +1,474 @@
+// lmhead_kernels.hip — HIP kernels of the deterministic chunked LM-head + loss
+// path for gfx950.
+//
+// Method (FlashInfer PR #8059, "feat(cake_lm_head_det_loss): det names for the
+// chunked LM-head + loss backend", PR description and CodeRabbit summary): the
+// hidden states are projected through the vocabulary matrix a vocabulary block
+// at a time, each row keeps what logsumexp and the requested logits need, the
+// n x V logits are never stored, and the backward recomputes each chunk's
+// logits to form dL/dz for the dH and dW contractions. Determinism (same PR,
+// description): every output element and every partial has exactly one writer,
+// merges run in a fixed order, and no floating-point atomic is used; integer
+// atomics (valid-row count, lowest error row) are order-independent.
+#include "lmhead_kernels.h"
+
+#include <limits.h>
+
+namespace lmhead {
+
+namespace {
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+__device__ __forceinline__ float quiet_nan() { return __builtin_nanf(""); }
+}  // namespace
+
+// ---------------------------------------------------------------- header words
+
+__global__ void init_header_kernel(int32_t* hdr) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        hdr[kHdrErrCode] = 0;
+        hdr[kHdrErrRow] = INT_MAX;
+        hdr[kHdrCount] = 0;
+    }
+}
+
+// Count valid rows (0 <= t < V) and record data errors. Labels: any negative
+// value is an ignored row, t >= V is an error (miles-ext-kernels PR #14, the
+// commit declaring the lm_head op). Candidate ids must lie in [0, V).
+__global__ void scan_labels_kernel(const int32_t* ids, int64_t n, int k, int64_t vocab,
+                                   int support, int32_t* hdr) {
+    __shared__ int32_t s_count, s_row, s_code;
+    if (threadIdx.x == 0) { s_count = 0; s_row = INT_MAX; s_code = 0; }
+    __syncthreads();
+    int32_t count = 0, row_min = INT_MAX, code = 0;
+    for (int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; row < n;
+         row += (int64_t)gridDim.x * blockDim.x) {
+        if (!support) {
+            const int64_t t = ids[row];
+            if (t >= vocab) { code |= kDevErrLabel; row_min = row_min < row ? row_min : (int32_t)row; }
+            else if (t >= 0) ++count;
+        } else {
+            const int32_t* r = ids + row * k;
+            for (int kk = 0; kk < k; ++kk) {
+                const int64_t id = r[kk];
+                if (id < 0 || id >= vocab) {
+                    code |= kDevErrCandidate;
+                    row_min = row_min < row ? row_min : (int32_t)row;
+                }
+            }
+        }
+    }
+    if (count) atomicAdd(&s_count, count);
+    if (code) { atomicOr(&s_code, code); atomicMin(&s_row, row_min); }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        if (s_count) atomicAdd(hdr + kHdrCount, s_count);
+        if (s_code) { atomicOr(hdr + kHdrErrCode, s_code); atomicMin(hdr + kHdrErrRow, s_row); }
+    }
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, int64_t count, uint32_t value) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = value;
+}
+
+// ------------------------------------------------------------- forward tiles
+
+// One 256-row x 256-column logits tile: z = H W^T on MFMA, then per row the
+// tile's max and sum of exp(z - max) over the columns below V, and the logits
+// at the row's ids that fall inside the tile. Every (row, tile) partial and
+// every gathered logit has exactly one writer.
+__global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTilesArgs a) {
+    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+    int64_t tm, tn;
+    map_tile(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    const int64_t m0 = tm * kTile, n0 = tn * kTile;
+
+    floatx16 acc[4][4];
+    gemm_mainloop(Operand{a.H, a.hidden, a.n}, m0, Operand{a.W, a.hidden, a.vocab}, n0, a.hidden,
+                  smem, acc);
+
+    float* S = reinterpret_cast<float*>(smem);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+    const int64_t row = m0 + tid;
+    const bool row_ok = row < a.n;
+    const float* Sr = S + tid;
+    float run_m = neg_inf(), run_s = 0.0f;
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+        if (wc == half) stage_half(S, acc, wr, lane);
+        __syncthreads();
+        const int64_t col0 = n0 + half * 128;
+        const int64_t rem = a.vocab - col0;
+        const int ncol = rem <= 0 ? 0 : (rem >= 128 ? 128 : (int)rem);
+        float m = neg_inf();
+        for (int c = 0; c < ncol; ++c) m = fmaxf(m, Sr[c * kEpiStride]);
+        const float mb = m * kLog2e;
+        float s = 0.0f;
+        for (int c = 0; c < ncol; ++c) s += exp2_fast(__builtin_fmaf(Sr[c * kEpiStride], kLog2e, -mb));
+        if (half == 0) {
+            run_m = m;
+            run_s = s;
+        } else if (ncol > 0) {
+            const float M = fmaxf(run_m, m);
+            run_s = run_s * exp2_fast((run_m - M) * kLog2e) + s * exp2_fast((m - M) * kLog2e);
+            run_m = M;
+        }
+        if (row_ok) {
+            const int32_t* idr = a.ids + row * a.k;
+            for (int kk = 0; kk < a.k; ++kk) {
+                const int64_t j = (int64_t)idr[kk] - col0;
+                if (j >= 0 && j < ncol) a.zg[row * a.k + kk] = Sr[j * kEpiStride];
+            }
+        }
+        __syncthreads();
+    }
+    if (row_ok) a.part[tn * a.n + row] = make_float2(run_m, run_s);
+}
+
+// Per row: merge the tiles' (max, sum) pairs in ascending tile order into
+// lse = M + log(sum_t s_t exp(m_t - M)), then the entry's per-row outputs.
+__global__ void finalize_rows_kernel(FinalizeArgs a) {
+    const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= a.n) return;
+    const float2* p = a.part + row;
+    float M = neg_inf();
+    for (int64_t t = 0; t < a.tiles_n; ++t) M = fmaxf(M, p[t * a.n].x);
+    float S = 0.0f;
+    const float Mb = M * kLog2e;
+    for (int64_t t = 0; t < a.tiles_n; ++t) {
+        const float2 v = p[t * a.n];
+        S += v.y * exp2_fast(__builtin_fmaf(v.x, kLog2e, -Mb));
+    }
+    const float lse = M + logf(S);
+    a.lse[row] = lse;
+    if (a.entry == kEntryCeMean || a.entry == kEntryCeSum || a.entry == kEntryLogprob) {
+        const int64_t t = a.ids[row];
+        const bool bad = t >= a.vocab;
+        const bool valid = t >= 0 && !bad;
+        const float zt = valid ? a.zg[row] : 0.0f;
+        float out;
+        if (a.entry == kEntryLogprob) out = valid ? zt - lse : 0.0f;
+        else out = valid ? lse - zt : 0.0f;
+        a.row_out[row] = bad ? quiet_nan() : out;
+        return;
+    }
+    // support entry
+    const int k = a.k;
+    const int32_t* idr = a.ids + row * k;
+    const float* zc = a.zg + row * k;
+    bool bad = false;
+    for (int kk = 0; kk < k; ++kk) {
+        const int64_t id = idr[kk];
+        bad = bad || id < 0 || id >= a.vocab;
+    }
+    float* lp = a.row_out + row * k;
+    for (int kk = 0; kk < k; ++kk) lp[kk] = bad ? quiet_nan() : zc[kk] - lse;
+    if (a.kl != nullptr) {
+        if (bad) {
+            a.kl[row] = quiet_nan();
+            return;
+        }
+        // log p_hat_k = z_k - log sum_j exp z_j over the listed candidates
+        float mx = neg_inf();
+        for (int kk = 0; kk < k; ++kk) mx = fmaxf(mx, zc[kk]);
+        float se = 0.0f;
+        for (int kk = 0; kk < k; ++kk) se += expf(zc[kk] - mx);
+        const float ls = mx + logf(se);
+        const float* r = a.ref_logq + row * k;
+        float kl = 0.0f;
+        for (int kk = 0; kk < k; ++kk) {
+            const float q = expf(r[kk]);
+            if (q > 0.0f) kl += q * (r[kk] - (zc[kk] - ls));
+        }
+        a.kl[row] = kl;
+    }
+}
+
+// loss = sum of the per-row losses (fixed strided order per thread, then a
+// fixed LDS tree), divided by the valid count for the mean.
+__global__ void ce_reduce_kernel(const float* rows, int64_t n, const int32_t* hdr,
+                                 int64_t num_valid, int mean, float* loss) {
+    __shared__ float red[kThreads];
+    const int tid = threadIdx.x;
+    float s = 0.0f;
+    for (int64_t i = tid; i < n; i += kThreads) s += rows[i];
+    red[tid] = s;
+    __syncthreads();
+    for (int w = kThreads / 2; w > 0; w >>= 1) {
+        if (tid < w) red[tid] += red[tid + w];
+        __syncthreads();
+    }
+    if (tid == 0) {
+        const float total = red[0];
+        if (!mean) {
+            loss[0] = total;
+        } else {
+            const int64_t cnt = num_valid >= 0 ? num_valid : (int64_t)hdr[kHdrCount];
+            loss[0] = cnt > 0 ? total / (float)cnt : (total != total ? total : 0.0f);
+        }
+    }
+}
+
+// --------------------------------------------------------------- backward
+
+// Per-row coefficients of dL/dz = a_n softmax(z_n) + sum_k c_nk onehot(id_nk).
+//   CE mean:  a = valid g / count,  c = -a (at the label)
+//   CE sum:   a = valid g,          c = -a
+//   logprob:  a = -valid gamma_n,   c = valid gamma_n
+//   support:  a = -sum_k gamma_nk,  c_k = gamma_nk + beta_n (Q p_hat_k - q_k), Q = sum q
+// Rows past n (tile padding) and rows with a data error get a = c = 0.
+__global__ void coeffs_kernel(CoeffArgs a) {
+    const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= a.n_pad) return;
+    if (row >= a.n) {
+        a.coef_a[row] = 0.0f;
+        return;
+    }
+    const int k = a.k;
+    if (a.entry != kEntrySupport) {
+        const int64_t t = a.ids[row];
+        const bool valid = t >= 0 && t < a.vocab;
+        float ca = 0.0f, cc = 0.0f;
+        if (a.entry == kEntryCeMean) {
+            const int64_t cnt = a.num_valid >= 0 ? a.num_valid : (int64_t)a.hdr[kHdrCount];
+            ca = (valid && cnt > 0) ? a.grad[0] / (float)cnt : 0.0f;
+            cc = -ca;
+        } else if (a.entry == kEntryCeSum) {
+            ca = valid ? a.grad[0] : 0.0f;
+            cc = -ca;
+        } else {
+            const float g = (a.grad != nullptr && valid) ? a.grad[row] : 0.0f;
+            ca = -g;
+            cc = g;
+        }
+        a.coef_a[row] = ca;
+        a.coef_c[row] = cc;
+        return;
+    }
+    const int32_t* idr = a.ids + row * k;
+    bool bad = false;
+    for (int kk = 0; kk < k; ++kk) {
+        const int64_t id = idr[kk];
+        bad = bad || id < 0 || id >= a.vocab;
+    }
+    float* c = a.coef_c + row * k;
+    if (bad) {
+        a.coef_a[row] = 0.0f;
+        for (int kk = 0; kk < k; ++kk) c[kk] = 0.0f;
+        return;
+    }
+    const float* g = a.grad != nullptr ? a.grad + row * k : nullptr;
+    float gsum = 0.0f;
+    for (int kk = 0; kk < k; ++kk) {
+        const float gk = g ? g[kk] : 0.0f;
+        gsum += gk;
+        c[kk] = gk;
+    }
+    a.coef_a[row] = -gsum;
+    if (a.grad_kl != nullptr) {
+        const float beta = a.grad_kl[row];
+        const float* lp = a.saved_lp + row * k;
+        const float* r = a.ref_logq + row * k;
+        float mx = neg_inf();
+        for (int kk = 0; kk < k; ++kk) mx = fmaxf(mx, lp[kk]);
+        float se = 0.0f, Q = 0.0f;
+        for (int kk = 0; kk < k; ++kk) {
+            se += expf(lp[kk] - mx);
+            Q += expf(r[kk]);
+        }
+        const float inv = 1.0f / se;
+        for (int kk = 0; kk < k; ++kk) {
+            const float phat = expf(lp[kk] - mx) * inv;
+            c[kk] += beta * (Q * phat - expf(r[kk]));
+        }
+    }
+}
+
+// Recompute one chunk's logits tile and write dL/dz in bf16: G[n, j] = a_n
+// exp(z - lse_n) for chunk columns j < width, plus c_nk where v0 + j = id_nk;
+// zero elsewhere. G is written row-major [n_pad, w_pad] (operand of dH) and
+// transposed [w_pad, n_pad] (operand of dW).
+__global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradArgs a) {
+    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+    int64_t tm, tn;
+    map_tile(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    const int64_t m0 = tm * kTile, n0 = tn * kTile;
+
+    floatx16 acc[4][4];
+    gemm_mainloop(Operand{a.H, a.hidden, a.n}, m0, Operand{a.Wc, a.hidden, a.width}, n0, a.hidden,
+                  smem, acc);
+
+    float* S = reinterpret_cast<float*>(smem);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+    const int64_t row = m0 + tid;   // < n_pad
+    const bool row_ok = row < a.n;
+    const float ca = row_ok ? a.coef_a[row] : 0.0f;
+    const float lb = row_ok ? a.lse[row] * kLog2e : 0.0f;
+    float* Sr = S + tid;
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+        if (wc == half) stage_half(S, acc, wr, lane);
+        __syncthreads();
+        const int64_t col0 = n0 + half * 128;   // chunk-local column
+        const int64_t rem = a.width - col0;
+        const int ncol = rem <= 0 ? 0 : (rem >= 128 ? 128 : (int)rem);
+        for (int c = 0; c < 128; ++c) {
+            const float x = Sr[c * kEpiStride];
+            Sr[c * kEpiStride] = (c < ncol && ca != 0.0f) ? ca * exp2_fast(__builtin_fmaf(x, kLog2e, -lb)) : 0.0f;
+        }
+        if (row_ok) {
+            const int32_t* idr = a.ids + row * a.k;
+            const float* cr = a.coef_c + row * a.k;
+            for (int kk = 0; kk < a.k; ++kk) {
+                const int64_t j = (int64_t)idr[kk] - a.v0 - col0;
+                if (j >= 0 && j < ncol) Sr[j * kEpiStride] += cr[kk];
+            }
+        }
+        if (a.G != nullptr) {
+            bf16_bits* g = a.G + row * a.w_pad + col0;
+            for (int c8 = 0; c8 < 16; ++c8) {
+                uint4 v;
+                uint32_t w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t lo = to_bf16(Sr[(c8 * 8 + 2 * i) * kEpiStride]);
+                    const uint32_t hi = to_bf16(Sr[(c8 * 8 + 2 * i + 1) * kEpiStride]);
+                    w[i] = lo | (hi << 16);
+                }
+                v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
+                *reinterpret_cast<uint4*>(g + c8 * 8) = v;
+            }
+        }
+        if (a.Gt != nullptr) {
+            bf16_bits* gt = a.Gt + col0 * a.n_pad + row;
+            for (int c = 0; c < 128; ++c) gt[(int64_t)c * a.n_pad] = to_bf16(Sr[c * kEpiStride]);
+        }
+        __syncthreads();
+    }
+}
+
+// dW rows of one chunk: dW[v0 + i, h] = sum_n G^T[i, n] H^T[h, n], a single
+// K-loop over every row n in ascending order; bf16 store of the fp32 sum.
+__global__ __launch_bounds__(kThreads, 1) void bwd_dw_kernel(DwArgs a) {
+    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+    int64_t tm, tn;
+    map_tile(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    const int64_t m0 = tm * kTile, n0 = tn * kTile;
+    floatx16 acc[4][4];
+    gemm_mainloop(Operand{a.Gt, a.n_pad, a.w_pad}, m0, Operand{a.Ht, a.n_pad, a.hidden}, n0, a.n_pad,
+                  smem, acc);
+    float* S = reinterpret_cast<float*>(smem);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+    const int64_t v = m0 + tid;   // chunk-local vocabulary row
+    const float* Sr = S + tid;
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+        if (wc == half) stage_half(S, acc, wr, lane);
+        __syncthreads();
+        const int64_t h0 = n0 + half * 128;
+        if (v < a.width) {
+            bf16_bits* out = a.dW + (a.v0 + v) * a.hidden + h0;
+            for (int c8 = 0; c8 < 16; ++c8) {
+                if (h0 + c8 * 8 >= a.hidden) break;
+                uint32_t w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    w[i] = (uint32_t)to_bf16(Sr[(c8 * 8 + 2 * i) * kEpiStride]) |
+                           ((uint32_t)to_bf16(Sr[(c8 * 8 + 2 * i + 1) * kEpiStride]) << 16);
+                *reinterpret_cast<uint4*>(out + c8 * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// dH contribution of one chunk: acc = sum_j G[n, j] W_c^T[h, j] over the
+// chunk's columns; the fp32 running sum over chunks (chunk order) lives in
+// dh_acc and the last chunk writes the bf16 result.
+__global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(DhArgs a) {
+    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+    int64_t tm, tn;
+    map_tile(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    const int64_t m0 = tm * kTile, n0 = tn * kTile;
+    floatx16 acc[4][4];
+    gemm_mainloop(Operand{a.G, a.w_pad, a.n_pad}, m0, Operand{a.Wt, a.w_pad, a.hidden}, n0, a.w_pad,
+                  smem, acc);
+    float* S = reinterpret_cast<float*>(smem);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+    const int64_t r = m0 + tid;
+    const float* Sr = S + tid;
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+        if (wc == half) stage_half(S, acc, wr, lane);
+        __syncthreads();
+        const int64_t h0 = n0 + half * 128;
+        if (r < a.n) {
+            const int64_t o = r * a.hidden + h0;
+            for (int c4 = 0; c4 < 32; ++c4) {
+                if (h0 + c4 * 4 >= a.hidden) break;
+                float4 v = make_float4(Sr[(c4 * 4 + 0) * kEpiStride], Sr[(c4 * 4 + 1) * kEpiStride],
+                                       Sr[(c4 * 4 + 2) * kEpiStride], Sr[(c4 * 4 + 3) * kEpiStride]);
+                if (!a.first) {
+                    const float4 p = *reinterpret_cast<const float4*>(a.dh_acc + o + c4 * 4);
+                    v.x = p.x + v.x;
+                    v.y = p.y + v.y;
+                    v.z = p.z + v.z;
+                    v.w = p.w + v.w;
+                }
+                if (a.last) {
+                    const uint32_t lo = (uint32_t)to_bf16(v.x) | ((uint32_t)to_bf16(v.y) << 16);
+                    const uint32_t hi = (uint32_t)to_bf16(v.z) | ((uint32_t)to_bf16(v.w) << 16);
+                    *reinterpret_cast<uint2*>(a.dH + o + c4 * 4) = make_uint2(lo, hi);
+                } else {
+                    *reinterpret_cast<float4*>(a.dh_acc + o + c4 * 4) = v;
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// out[c, r] = in[r, c] for r < rows, 0 for rows <= r < rows_pad; columns are a
+// multiple of 64, rows_pad a multiple of 64. 64 x 64 tiles through LDS.
+__global__ void transpose_kernel(const bf16_bits* in, int64_t ld_in, int64_t rows, int64_t cols,
+                                 bf16_bits* out, int64_t rows_pad) {
+    __shared__ bf16_bits tile[64][64 + 8];
+    const int tid = threadIdx.x;
+    const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
+    {
+        const int r = tid >> 2, seg = (tid & 3) * 16;
+        uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
+        if (r0 + r < rows) {
+            const uint4* src = reinterpret_cast<const uint4*>(in + (r0 + r) * ld_in + c0 + seg);
+            v0 = src[0];
+            v1 = src[1];
+        }
+        const bf16_bits* p0 = reinterpret_cast<const bf16_bits*>(&v0);
+        const bf16_bits* p1 = reinterpret_cast<const bf16_bits*>(&v1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            tile[r][seg + i] = p0[i];
+            tile[r][seg + 8 + i] = p1[i];
+        }
+    }
+    __syncthreads();
+    {
+        const int c = tid >> 2, seg = (tid & 3) * 16;
+        bf16_bits vals[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) vals[i] = tile[seg + i][c];
+        uint4* dst = reinterpret_cast<uint4*>(out + (c0 + c) * rows_pad + r0 + seg);
+        dst[0] = *reinterpret_cast<const uint4*>(&vals[0]);
+        dst[1] = *reinterpret_cast<const uint4*>(&vals[8]);
+    }
+}
+
+}  // namespace lmhead

@@ -1,0 +1,221 @@
+/*
+ * lmhead.h — C ABI of the deterministic chunked LM-head + loss library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library projects bf16 hidden states H[n, hidden] through the bf16
+ * vocabulary matrix W[vocab, hidden] without ever holding the n x vocab
+ * logits: each 256-wide vocabulary tile is reduced to a per-row (max, sum of
+ * exponentials) pair and the logits at the requested ids, and the pairs are
+ * merged in a fixed order into logsumexp. The backward pass recomputes the
+ * logits one vocabulary chunk at a time, forms dL/dz in registers and feeds
+ * the two contractions dH = dZ W and dW = dZ^T H.
+ *
+ * Passages that define the operations (cited below by short name):
+ *   [PR8059]  FlashInfer pull request #8059, "feat(cake_lm_head_det_loss):
+ *             det names for the chunked LM-head + loss backend" — the PR
+ *             description (deterministic forward and backward for fixed
+ *             inputs, hardware, chunk plan and initial accumulation buffers;
+ *             BF16 only; CE and policy losses, the log-probability entry and
+ *             the support-set log-probability and KL entries) and the
+ *             CodeRabbit summary (candidate-restricted log-probabilities and
+ *             forward KL; valid-row controls; workspace reporting).
+ *   [PR8059-review]  the same PR's CodeRabbit review comment on cache-miss
+ *             bindings (FP32 dx / dw accumulators plus BF16 outputs).
+ *   [PR14-op] miles-ext-kernels pull request #14, "[Cake 13/13] mok", the
+ *             commit declaring the lm_head op (every negative label marks an
+ *             ignored row; a label >= V must not give a plausible value; dW
+ *             is BF16, the cast of an FP32 [V, H] accumulator).
+ *   [PR14-tests] the same PR's commit adding tests/cake/lm_head/ (empty
+ *             calls, frozen inputs, given counts, zero-gradient rows,
+ *             negative labels, geometry and device errors).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device pointers are device memory on the current
+ *     HIP device; `p` and `code`/`row` out-parameters are host memory.
+ *   - The caller owns and allocates every buffer, including the workspace;
+ *     the library never allocates device memory and never synchronises
+ *     (except lmhead_read_device_error). All work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the null stream).
+ *   - Host-checkable errors (NULL required pointers, bad sizes, misaligned
+ *     pointers, a small workspace, a device that is not gfx950) return a
+ *     status before anything is enqueued.
+ *   - Data errors found on the device (a label >= vocab, a candidate id
+ *     outside [0, vocab)) never trap: the row's outputs become NaN (forward)
+ *     or the row gets zero gradient (backward), and the workspace's error
+ *     word records the lowest offending row (lmhead_read_device_error).
+ *   - Results are a function of (inputs, problem incl. chunk, library build,
+ *     device model): no floating-point atomics, every reduction runs in a
+ *     fixed order, and the work decomposition does not depend on the number
+ *     of compute units. Two calls with the same arguments give the same bits.
+ *   - A workspace may not be shared by two calls in flight. Its contents are
+ *     undefined between calls; the state the backward needs (lse, and lp
+ *     for the support KL) is passed explicitly.
+ */
+#ifndef LMHEAD_H
+#define LMHEAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+enum lmhead_status {
+    LMHEAD_OK = 0,
+    LMHEAD_ERR_ARG = 1,        /* NULL required pointer, unknown entry, nonzero flags */
+    LMHEAD_ERR_SHAPE = 2,      /* sizes outside the supported ranges */
+    LMHEAD_ERR_ALIGN = 3,      /* a device pointer not 16-byte aligned (workspace: 256) */
+    LMHEAD_ERR_WORKSPACE = 4,  /* workspace_bytes < lmhead_workspace_size(...) */
+    LMHEAD_ERR_DEVICE = 5,     /* current device is not gfx950 or no device */
+    LMHEAD_ERR_HIP = 6         /* a HIP launch or runtime call failed */
+};
+
+/* Loss entries ([PR8059]: CE loss, log-probability entry, support-set entries). */
+enum lmhead_entry {
+    LMHEAD_ENTRY_CE_MEAN = 0,  /* mean cross-entropy over valid rows */
+    LMHEAD_ENTRY_CE_SUM = 1,   /* summed cross-entropy over valid rows */
+    LMHEAD_ENTRY_LOGPROB = 2,  /* per-token log-probability of the label */
+    LMHEAD_ENTRY_SUPPORT = 3   /* log-probabilities of K candidates + KL */
+};
+
+/* Device error codes recorded in the workspace's error word. */
+enum lmhead_device_error {
+    LMHEAD_DEVERR_NONE = 0,
+    LMHEAD_DEVERR_LABEL = 1,     /* a label >= vocab ([PR14-op]) */
+    LMHEAD_DEVERR_CANDIDATE = 2  /* a candidate id outside [0, vocab) */
+};
+
+/*
+ * Problem description (host memory).
+ *   n          rows (tokens), 0 <= n <= 2^30. n = 0 is a valid, empty call.
+ *   hidden     hidden size, a multiple of 64, 64 <= hidden <= 65536.
+ *   vocab      vocabulary size, 1 <= vocab <= 2^30. Any value: the last
+ *              256-wide tile is masked, so results equal the definition over
+ *              exactly `vocab` columns (no padding of W).
+ *   chunk      vocabulary chunk of the backward pass: a multiple of 256,
+ *              >= 256. The backward materialises dL/dz for one chunk
+ *              ([n x chunk] bf16) at a time; the forward's result does not
+ *              depend on it.
+ *   num_valid  -1: count valid rows (0 <= label < vocab) on the device,
+ *              with no host synchronisation; >= 0: use this value verbatim as
+ *              the CE mean's denominator ("given counts", [PR14-tests]).
+ *   k          candidates per row for LMHEAD_ENTRY_SUPPORT (1..1024);
+ *              ignored by the other entries.
+ *   flags      reserved, must be 0.
+ */
+typedef struct lmhead_problem {
+    int64_t n;
+    int64_t hidden;
+    int64_t vocab;
+    int64_t chunk;
+    int64_t num_valid;
+    int32_t k;
+    int32_t flags;
+} lmhead_problem;
+
+/*
+ * Bytes of device workspace an entry needs ("workspace reporting",
+ * [PR8059]). Pure host function: no device is touched. `with_backward`
+ * != 0 sizes the workspace for lmhead_loss_bwd (which needs more: one
+ * chunk of dL/dz in two layouts, transposed operands and the fp32 dH
+ * accumulator). Returns 0 for an invalid problem or entry.
+ */
+size_t lmhead_workspace_size(const lmhead_problem* p, int entry, int with_backward);
+
+/*
+ * Cross-entropy forward ([PR8059]; ignore rule [PR14-op]).
+ *   entry      LMHEAD_ENTRY_CE_MEAN or LMHEAD_ENTRY_CE_SUM.
+ *   H          device, bf16 [n, hidden], row-major, 16-byte aligned.
+ *   W          device, bf16 [vocab, hidden], row-major, 16-byte aligned.
+ *   targets    device, int32 [n]. Every negative value marks an ignored row
+ *              (loss 0, not counted); a value >= vocab is a data error.
+ *   loss       device, fp32 [1]: sum over valid rows of (lse - z[t]) divided
+ *              by the valid count (MEAN; 0 when the count is 0) or not (SUM).
+ *   lse        device, fp32 [n] or NULL: per-row logsumexp of the logits,
+ *              the state the backward needs.
+ *   workspace  device, >= lmhead_workspace_size(p, entry, 0) bytes,
+ *              256-byte aligned.
+ */
+int lmhead_loss_fwd(const lmhead_problem* p, int entry,
+                    const void* H, const void* W, const int32_t* targets,
+                    float* loss, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Per-token log-probability ([PR8059] "the log-probability entry"; the RL
+ * policy-loss input).
+ *   logp       device, fp32 [n]: z[n, t_n] - lse[n]; 0 on ignored rows.
+ *   lse        device, fp32 [n] or NULL.
+ * Other arguments as lmhead_loss_fwd.
+ */
+int lmhead_logprob(const lmhead_problem* p,
+                   const void* H, const void* W, const int32_t* targets,
+                   float* logp, float* lse,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Support-set log-probabilities and KL ([PR8059] "support-set
+ * log-probability and KL entries", "candidate-restricted
+ * log-probabilities", "forward-KL").
+ *   ids        device, int32 [n, k]: candidate vocabulary ids per row
+ *              (duplicates allowed, each counts separately); an id outside
+ *              [0, vocab) is a data error.
+ *   ref_logq   device, fp32 [n, k] or NULL: reference log-probabilities
+ *              over the k candidates. NULL: no KL.
+ *   lp         device, fp32 [n, k]: full-vocabulary log-probability
+ *              z[n, id] - lse[n] of each candidate.
+ *   kl         device, fp32 [n] or NULL (must be NULL when ref_logq is):
+ *              KL(q || p_hat) = sum_k q_k (ref_logq_k - log p_hat_k), q =
+ *              exp(ref_logq), p_hat = the model's softmax renormalised over
+ *              the k listed candidates; terms with q = 0 contribute 0.
+ *   lse        device, fp32 [n] or NULL.
+ */
+int lmhead_support_logprob_kl(const lmhead_problem* p,
+                              const void* H, const void* W, const int32_t* ids,
+                              const float* ref_logq, float* lp, float* kl, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of any entry: recompute each vocabulary chunk's logits, form
+ * dL/dz = a_n softmax(z)_n + sum_k c_nk onehot(id_nk) in registers, round it
+ * to bf16 and contract: dH = dZ W, dW = dZ^T H ([PR8059]; FP32 accumulators
+ * with BF16 outputs, [PR8059-review], [PR14-op]).
+ *   entry           the forward's entry.
+ *   targets_or_ids  device, int32 [n] (CE, LOGPROB) or [n, k] (SUPPORT).
+ *   ref_logq        device, fp32 [n, k] (SUPPORT with a KL gradient) or NULL.
+ *   lse             device, fp32 [n]: the forward's lse output.
+ *   saved_lp        device, fp32 [n, k]: the forward's lp output (SUPPORT
+ *                   with grad_kl only; else NULL).
+ *   grad            device, fp32: CE: [1] dL/dloss; LOGPROB: [n] dL/dlogp;
+ *                   SUPPORT: [n, k] dL/dlp or NULL (= 0).
+ *   grad_kl         device, fp32 [n] dL/dKL (SUPPORT) or NULL (= 0).
+ *   dH              device, bf16 [n, hidden] or NULL (frozen H: skipped).
+ *   dW              device, bf16 [vocab, hidden] or NULL (frozen W: skipped).
+ *   workspace       >= lmhead_workspace_size(p, entry, 1) bytes.
+ * Ignored rows, rows with zero upstream gradient and rows with a data error
+ * get exactly zero gradient. n = 0 writes zeros to dW.
+ */
+int lmhead_loss_bwd(const lmhead_problem* p, int entry,
+                    const void* H, const void* W, const int32_t* targets_or_ids,
+                    const float* ref_logq, const float* lse, const float* saved_lp,
+                    const float* grad, const float* grad_kl,
+                    void* dH, void* dW,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable text for a status code. */
+const char* lmhead_status_string(int status);
+
+/*
+ * Reads the device error word the last call on `workspace` left behind.
+ * Synchronises `stream` (tests and debugging only). code: an
+ * lmhead_device_error bit set; row: the lowest offending row, or -1.
+ */
+int lmhead_read_device_error(const void* workspace, void* stream, int32_t* code, int64_t* row);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMHEAD_H */

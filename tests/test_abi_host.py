@@ -1,0 +1,125 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library loads and exports every function include/lmhead.h declares;
+lmhead_workspace_size is a pure host function; every host-checkable error is
+returned before anything touches a device. Calls here use fake addresses
+and always fail validation first, so nothing is ever launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import chunked_lm_head_amd as lm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lmhead.h")
+
+FAKE = 1 << 20          # a 256-aligned fake address; never dereferenced
+BIG = 1 << 40
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lmhead_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert names == sorted([
+        "lmhead_loss_bwd", "lmhead_loss_fwd", "lmhead_logprob", "lmhead_read_device_error",
+        "lmhead_status_string", "lmhead_support_logprob_kl", "lmhead_workspace_size"])
+    L = ctypes.CDLL(lm.LIB_PATH)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    for st in range(7):
+        assert lm.lmhead_status_string(st)
+    assert lm.lmhead_status_string(99) == "unknown status"
+
+
+def _p(**kw):
+    d = dict(n=64, hidden=256, vocab=1024, chunk=256, num_valid=-1, k=1, flags=0)
+    d.update(kw)
+    return lm.problem(**d)
+
+
+def test_workspace_size_rules():
+    ws = lm.lmhead_workspace_size
+    assert ws(_p(), lm.ENTRY_CE_MEAN, 0) > 0
+    assert ws(_p(), lm.ENTRY_CE_MEAN, 1) >= ws(_p(), lm.ENTRY_CE_MEAN, 0)
+    # invalid problems report 0
+    for bad in (dict(hidden=100), dict(hidden=0), dict(vocab=0), dict(chunk=100), dict(chunk=0),
+                dict(n=-1), dict(num_valid=-2), dict(flags=1), dict(n=1 << 31)):
+        assert ws(_p(**bad), lm.ENTRY_CE_MEAN, 0) == 0, bad
+    assert ws(_p(), 7, 0) == 0
+    assert ws(_p(k=0), lm.ENTRY_SUPPORT, 0) == 0
+    assert ws(_p(k=1025), lm.ENTRY_SUPPORT, 0) == 0
+    # grows with n, vocab and k; the forward does not depend on the chunk
+    assert ws(_p(n=128), 0, 0) > ws(_p(n=64), 0, 0)
+    assert ws(_p(vocab=4096), 0, 0) > ws(_p(vocab=1024), 0, 0)
+    assert ws(_p(k=64), lm.ENTRY_SUPPORT, 0) > ws(_p(k=8), lm.ENTRY_SUPPORT, 0)
+    assert ws(_p(chunk=512), 0, 0) == ws(_p(chunk=256), 0, 0)
+    assert ws(_p(chunk=512), 0, 1) > ws(_p(chunk=256), 0, 1)
+    # headline: 64-bit arithmetic (the dL/dz chunk alone is 2 x 134 MB)
+    head = lm.problem(8192, 4096, 151936, 8192, -1, 1, 0)
+    b = ws(head, 0, 1)
+    assert b > 2 * 2 * 8192 * 8192 and b < 1 << 31
+    big = lm.problem(1 << 20, 8192, 1 << 20, 1 << 20, -1, 1, 0)
+    assert ws(big, 0, 1) > 1 << 40    # no 32-bit wrap
+    assert ws(_p(n=0), 0, 0) > 0 and ws(_p(n=0), 0, 1) > 0
+
+
+def test_host_errors_precede_device_use():
+    p = _p()
+    WSZ = lm.lmhead_workspace_size(p, 0, 1)
+    f = lm.lmhead_loss_fwd
+    assert f(p, 0, None, FAKE, FAKE, FAKE, FAKE, FAKE, WSZ, 0) == lm.LMHEAD_ERR_ARG
+    assert f(p, 0, FAKE, FAKE, FAKE, None, FAKE, FAKE, WSZ, 0) == lm.LMHEAD_ERR_ARG
+    assert f(p, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, WSZ, 0) == lm.LMHEAD_ERR_ARG
+    assert f(p, lm.ENTRY_LOGPROB, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, WSZ, 0) == lm.LMHEAD_ERR_ARG
+    assert f(_p(hidden=96), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, WSZ, 0) == lm.LMHEAD_ERR_SHAPE
+    assert f(p, 0, FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, WSZ, 0) == lm.LMHEAD_ERR_ALIGN
+    assert f(p, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16, WSZ, 0) == lm.LMHEAD_ERR_ALIGN
+    assert f(p, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1024, 0) == lm.LMHEAD_ERR_WORKSPACE
+    g = lm.lmhead_logprob
+    assert g(p, FAKE, FAKE, FAKE, None, FAKE, FAKE, WSZ, 0) == lm.LMHEAD_ERR_ARG
+    s = lm.lmhead_support_logprob_kl
+    ps = _p(k=4)
+    # kl requested without ref_logq
+    assert s(ps, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, BIG, 0) == lm.LMHEAD_ERR_ARG
+    assert s(_p(k=0), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, BIG, 0) == lm.LMHEAD_ERR_SHAPE
+    b = lm.lmhead_loss_bwd
+    assert b(p, 0, FAKE, FAKE, FAKE, None, None, None, FAKE, None, FAKE, FAKE, FAKE, BIG, 0) \
+        == lm.LMHEAD_ERR_ARG          # lse missing
+    assert b(p, 0, FAKE, FAKE, FAKE, None, FAKE, None, None, None, FAKE, FAKE, FAKE, BIG, 0) \
+        == lm.LMHEAD_ERR_ARG          # CE grad missing
+    assert b(ps, 3, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, BIG, 0) \
+        == lm.LMHEAD_ERR_ARG          # KL grad without ref_logq / saved lp
+    assert b(p, 0, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE + 8, FAKE, FAKE, BIG, 0) \
+        == lm.LMHEAD_ERR_ALIGN
+    assert b(p, 0, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, 4096, 0) \
+        == lm.LMHEAD_ERR_WORKSPACE
+    assert b(p, 9, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, BIG, 0) \
+        == lm.LMHEAD_ERR_ARG
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_no_device_status():
+    p = _p()
+    WSZ = lm.lmhead_workspace_size(p, 0, 1)
+    st = lm.lmhead_loss_fwd(p, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, WSZ, 0)
+    assert st == lm.LMHEAD_ERR_DEVICE
+
+
+def test_python_layer_rejects_cpu_tensors():
+    H = torch.zeros(4, 64, dtype=torch.bfloat16)
+    W = torch.zeros(8, 64, dtype=torch.bfloat16)
+    t = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        lm.ce_loss(H, W, t, chunk=256)
