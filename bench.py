@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunked LM-head + loss path on one MI355X.
+
+One step = the whole hot path over one batch: forward (label scan, logits
+tiles with the online max / sum-exp epilogue, per-row logsumexp merge, loss
+reduction) and backward (row coefficients, per-chunk logits recompute with
+the dL/dz epilogue, dW and dH contractions). Inputs are resident in HBM
+before the timed region; outputs and workspace are allocated once.
+
+Prints ONE JSON line on stdout (progress goes to stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6     # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBS = 8000.0
+METRIC = "fused LM-head+CE fwd+bwd tokens/s and TFLOP/s (% bf16 MFMA peak) at V=151936"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="headline",
+                    choices=["headline", "mid", "logprob", "support", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall time of the oracle sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import chunked_lm_head_amd as lm
+    import workloads
+
+    wl = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    inp = workloads.make_inputs(wl)
+    log(f"inputs for {wl.name} drawn in {time.time() - t0:.1f}s")
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    H, W = bf16(inp.H), bf16(inp.W)
+    entry = wl.entry
+    k = wl.k if entry == workloads.ENTRY_SUPPORT else 1
+    idx = torch.from_numpy(inp.targets if inp.targets is not None else inp.ids).to(dev)
+    grad = torch.from_numpy(inp.grad).to(dev)
+    ref_logq = torch.from_numpy(inp.ref_logq).to(dev) if inp.ref_logq is not None else None
+    grad_kl = torch.from_numpy(inp.grad_kl).to(dev) if inp.grad_kl is not None else None
+
+    p = lm.problem(wl.n, wl.hidden, wl.vocab, wl.chunk, -1, k)
+    ws_bytes = lm.lmhead_workspace_size(p, entry, 1)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(wl.n, dtype=torch.float32, device=dev)
+    row_out = torch.empty((wl.n, k) if k > 1 else (wl.n,), dtype=torch.float32, device=dev)
+    kl = torch.empty(wl.n, dtype=torch.float32, device=dev)
+    dH = torch.empty_like(H)
+    dW = torch.empty_like(W)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    log(f"workspace {ws_bytes / 2**20:.1f} MiB; dtype bf16; chunk {wl.chunk}")
+
+    def fwd():
+        if entry in (workloads.ENTRY_CE_MEAN, workloads.ENTRY_CE_SUM):
+            st = lm.lmhead_loss_fwd(p, entry, H, W, idx, loss, lse, ws, ws_bytes, sp)
+        elif entry == workloads.ENTRY_LOGPROB:
+            st = lm.lmhead_logprob(p, H, W, idx, row_out, lse, ws, ws_bytes, sp)
+        else:
+            st = lm.lmhead_support_logprob_kl(p, H, W, idx, ref_logq, row_out, kl, lse, ws,
+                                              ws_bytes, sp)
+        if st:
+            raise lm.LMHeadError(st, "forward")
+
+    def bwd():
+        saved = row_out if entry == workloads.ENTRY_SUPPORT else None
+        st = lm.lmhead_loss_bwd(p, entry, H, W, idx, ref_logq, lse, saved, grad, grad_kl, dH, dW,
+                                ws, ws_bytes, sp)
+        if st:
+            raise lm.LMHeadError(st, "backward")
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    log(f"{args.warmup} warmup steps done")
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        fwd()
+        ev[i][1].record(stream)
+        bwd()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    fwd_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    bwd_ms = [b.elapsed_time(c) for _, b, c in ev]
+    step_ms = [a.elapsed_time(c) for a, _, c in ev]
+    ms_per_step = wall * 1e3 / K
+    log(f"timed {K} steps: wall {ms_per_step:.3f} ms/step; events fwd {np.mean(fwd_ms):.3f} "
+        f"bwd {np.mean(bwd_ms):.3f} step {np.mean(step_ms):.3f} ms")
+
+    # determinism: the last timed step's outputs against one more step
+    def digest():
+        torch.cuda.synchronize()
+        h = hashlib.sha256()
+        for t in (loss, lse, row_out, dH, dW):
+            h.update(t.view(torch.uint8).cpu().numpy().tobytes())
+        return h.hexdigest()
+
+    d1 = digest()
+    fwd()
+    bwd()
+    d2 = digest()
+    deterministic = d1 == d2
+    log(f"bitwise repeat: {deterministic} ({d1[:16]})")
+
+    flops = wl.flops_fwd_bwd
+    tokens_per_s = wl.n * K / wall
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    fwd_flops = 2.0 * wl.n * wl.vocab * wl.hidden
+    fwd_avg_ms = float(np.mean(fwd_ms))
+    achieved = fwd_flops / (fwd_avg_ms * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normals, no checkpoint or dataset)",
+        "config": {
+            "workload": f"{wl.name}: N={wl.n} tokens, Hd={wl.hidden}, V={wl.vocab}, "
+                        f"chunk {wl.chunk}, entry {['ce_mean', 'ce_sum', 'logprob', 'support'][entry]}"
+                        + (f", K={wl.k}" if k > 1 else "") + ", forward + backward (dH, dW)",
+            "n": wl.n, "hidden": wl.hidden, "vocab": wl.vocab, "chunk": wl.chunk,
+            "seed": wl.seed,
+        },
+        "tflops_8nvh": round(tflops, 2),
+        "tflops_6nvh_model": round(tflops * 6 / 8, 2),
+        "pct_bf16_peak": round(100 * tflops / BF16_PEAK_TFLOPS, 2),
+        "fwd_ms": round(fwd_avg_ms, 4),
+        "bwd_ms": round(float(np.mean(bwd_ms)), 4),
+        "deterministic_repeat": deterministic,
+        "roofline": {
+            "kernel": "fwd_tiles_kernel (logits GEMM + online max/sum-exp epilogue, one launch over all of V)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "timing": "HIP events around lmhead_loss_fwd on its stream (label scan, row merge "
+                      "and loss reduction add <1% next to the tiles kernel)",
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, inp, target_s):
+    """The fp64 oracle, as it stands, on a bounded sample of rows of the same
+    workload: for each sampled row the full forward (logits over the whole
+    vocabulary, lse, loss) and backward (dL/dz, its dH row and its share of
+    every dW row). Throughput is scaled to tokens/s."""
+    import oracle
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
+    rng = np.random.default_rng(wl.seed + 77)
+
+    def one(rows):
+        rows = np.sort(rows)
+        t0 = time.perf_counter()
+        z = oracle.logits(inp.H, inp.W, rows, threads=threads)
+        if wl.entry in (0, 1):
+            t = inp.targets[rows]
+            f = oracle.ce_forward(z, t, -1, "mean")
+            dz = oracle.ce_dz(z, t, 1.0, max(f["count"], 1), "mean")
+        elif wl.entry == 2:
+            t = inp.targets[rows]
+            oracle.logprob_forward(z, t)
+            dz = oracle.logprob_dz(z, t, inp.grad[rows])
+        else:
+            oracle.support_forward(z, inp.ids[rows], inp.ref_logq[rows])
+            dz = oracle.support_dz(z, inp.ids[rows], inp.ref_logq[rows], inp.grad[rows],
+                                   inp.grad_kl[rows])
+        oracle.grad_hidden(dz, inp.W, threads=threads)
+        for v0 in range(0, wl.vocab, 8192):   # dW in vocabulary blocks (bounded memory)
+            oracle.grad_weight(dz[:, v0:v0 + 8192], inp.H, rows, threads=threads)
+        return time.perf_counter() - t0
+
+    probe_rows = rng.choice(wl.n, size=4, replace=False)
+    t_probe = one(probe_rows)
+    per_row = t_probe / 4
+    n_rows = int(max(4, min(256, target_s / max(per_row, 1e-6))))
+    n_rows = (n_rows // 4) * 4
+    rows = rng.choice(wl.n, size=n_rows, replace=False)
+    log(f"cpu baseline: probe {t_probe:.2f}s for 4 rows; timing {n_rows} rows on {threads} threads")
+    dt = one(rows)
+    return {
+        "value": round(n_rows / dt, 4),
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{n_rows} rows of the {wl.name} workload (fp64 C oracle: logits over all "
+                  f"{wl.vocab} ids, lse, loss, dL/dz, the rows' dH and their dW contribution over "
+                  f"all vocabulary rows), {dt:.1f}s wall",
+        "seconds": round(dt, 2),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -167,7 +167,7 @@ int forward(const lmhead_problem* p, int entry, const void* H, const void* W, co
     fin.lse = lse_out != nullptr ? lse_out : (float*)(w + L.lse);
     fin.row_out = ce ? (float*)(w + L.rows) : row_out;
     fin.kl = kl;
-    finalize_rows_kernel<<<grid_1d(L.n, kThreads, INT_MAX), kThreads, 0, s>>>(fin);
+    finalize_rows_kernel<<<grid_1d(L.n * 8, kThreads, INT_MAX), kThreads, 0, s>>>(fin);   // 8 lanes per row
     if (ce)
         ce_reduce_kernel<<<1, kThreads, 0, s>>>(fin.row_out, L.n, hdr, p->num_valid,
                                                 entry == LMHEAD_ENTRY_CE_MEAN ? 1 : 0, loss);

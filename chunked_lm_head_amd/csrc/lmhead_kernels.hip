@@ -130,20 +130,46 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTilesArgs a) 
     if (row_ok) a.part[tn * a.n + row] = make_float2(run_m, run_s);
 }
 
-// Per row: merge the tiles' (max, sum) pairs in ascending tile order into
-// lse = M + log(sum_t s_t exp(m_t - M)), then the entry's per-row outputs.
+// Per row: merge the tiles' (max, sum) pairs into lse = M + log(sum_t s_t
+// exp(m_t - M)). Eight lanes share a row: lane `sub` takes tiles t = sub,
+// sub + 8, ... in ascending order, and the eight partial results are combined
+// by xor-shuffles with a fixed pairing (1, 2, 4), so the association order is
+// a function of the tile count only. Lane 0 of each group then writes the
+// entry's per-row outputs.
+constexpr int kFinLanes = 8;
+
+__device__ __forceinline__ float group_max8(float v) {
+    v = fmaxf(v, __shfl_xor(v, 1));
+    v = fmaxf(v, __shfl_xor(v, 2));
+    v = fmaxf(v, __shfl_xor(v, 4));
+    return v;
+}
+__device__ __forceinline__ float group_sum8(float v) {
+    v = v + __shfl_xor(v, 1);
+    v = v + __shfl_xor(v, 2);
+    v = v + __shfl_xor(v, 4);
+    return v;
+}
+
 __global__ void finalize_rows_kernel(FinalizeArgs a) {
-    const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (row >= a.n) return;
-    const float2* p = a.part + row;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t row = gid / kFinLanes;
+    const int sub = (int)(gid % kFinLanes);
+    const bool live = row < a.n;                 // whole groups share `live`
+    const float2* p = a.part + (live ? row : 0);
     float M = neg_inf();
-    for (int64_t t = 0; t < a.tiles_n; ++t) M = fmaxf(M, p[t * a.n].x);
-    float S = 0.0f;
+    if (live)
+        for (int64_t t = sub; t < a.tiles_n; t += kFinLanes) M = fmaxf(M, p[t * a.n].x);
+    M = group_max8(M);
     const float Mb = M * kLog2e;
-    for (int64_t t = 0; t < a.tiles_n; ++t) {
-        const float2 v = p[t * a.n];
-        S += v.y * exp2_fast(__builtin_fmaf(v.x, kLog2e, -Mb));
-    }
+    float S = 0.0f;
+    if (live)
+        for (int64_t t = sub; t < a.tiles_n; t += kFinLanes) {
+            const float2 v = p[t * a.n];
+            S += v.y * exp2_fast(__builtin_fmaf(v.x, kLog2e, -Mb));
+        }
+    S = group_sum8(S);
+    if (!live || sub != 0) return;
     const float lse = M + logf(S);
     a.lse[row] = lse;
     if (a.entry == kEntryCeMean || a.entry == kEntryCeSum || a.entry == kEntryLogprob) {
