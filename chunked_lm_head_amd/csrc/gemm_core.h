@@ -213,12 +213,14 @@ __device__ __forceinline__ void stage_half(float* S, const floatx16 (&acc)[4][4]
             }
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ bf16_bits to_bf16(float x) {
-    const uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_bits)((u >> 16) | 0x40u);
-    const uint32_t rounding = 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_bits)((u + rounding) >> 16);
+// fp32 -> bf16, round to nearest even: the conversion lowers to gfx950's
+// v_cvt_pk_bf16_f32, two values per instruction, packed low | high << 16.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2_t v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 }  // namespace lmhead

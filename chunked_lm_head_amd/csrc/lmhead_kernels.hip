@@ -356,24 +356,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
                 if (j >= 0 && j < ncol) Sr[j * kEpiStride] += cr[kk];
             }
         }
+        __syncthreads();
         if (a.G != nullptr) {
+            // row-major copy: thread = row, 16-byte stores of 8 columns
             bf16_bits* g = a.G + row * a.w_pad + col0;
             for (int c8 = 0; c8 < 16; ++c8) {
-                uint4 v;
                 uint32_t w[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t lo = to_bf16(Sr[(c8 * 8 + 2 * i) * kEpiStride]);
-                    const uint32_t hi = to_bf16(Sr[(c8 * 8 + 2 * i + 1) * kEpiStride]);
-                    w[i] = lo | (hi << 16);
-                }
-                v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
-                *reinterpret_cast<uint4*>(g + c8 * 8) = v;
+                for (int i = 0; i < 4; ++i)
+                    w[i] = pack_bf16x2(Sr[(c8 * 8 + 2 * i) * kEpiStride], Sr[(c8 * 8 + 2 * i + 1) * kEpiStride]);
+                *reinterpret_cast<uint4*>(g + c8 * 8) = make_uint4(w[0], w[1], w[2], w[3]);
             }
         }
         if (a.Gt != nullptr) {
-            bf16_bits* gt = a.Gt + col0 * a.n_pad + row;
-            for (int c = 0; c < 128; ++c) gt[(int64_t)c * a.n_pad] = to_bf16(Sr[c * kEpiStride]);
+            // transposed copy: 32 lanes cover one column's 256 rows (8 rows, 16 bytes each)
+            const int rg = tid & 31;
+            for (int it = 0; it < 16; ++it) {
+                const int c = it * 8 + (tid >> 5);
+                const float4 lo = *reinterpret_cast<const float4*>(S + c * kEpiStride + rg * 8);
+                const float4 hi = *reinterpret_cast<const float4*>(S + c * kEpiStride + rg * 8 + 4);
+                const uint4 v = make_uint4(pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w),
+                                           pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w));
+                *reinterpret_cast<uint4*>(a.Gt + (col0 + c) * a.n_pad + m0 + rg * 8) = v;
+            }
         }
         __syncthreads();
     }
@@ -406,8 +411,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dw_kernel(DwArgs a) {
                 uint32_t w[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    w[i] = (uint32_t)to_bf16(Sr[(c8 * 8 + 2 * i) * kEpiStride]) |
-                           ((uint32_t)to_bf16(Sr[(c8 * 8 + 2 * i + 1) * kEpiStride]) << 16);
+                    w[i] = pack_bf16x2(Sr[(c8 * 8 + 2 * i) * kEpiStride], Sr[(c8 * 8 + 2 * i + 1) * kEpiStride]);
                 *reinterpret_cast<uint4*>(out + c8 * 8) = make_uint4(w[0], w[1], w[2], w[3]);
             }
         }
@@ -450,8 +454,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(DhArgs a) {
                     v.w = p.w + v.w;
                 }
                 if (a.last) {
-                    const uint32_t lo = (uint32_t)to_bf16(v.x) | ((uint32_t)to_bf16(v.y) << 16);
-                    const uint32_t hi = (uint32_t)to_bf16(v.z) | ((uint32_t)to_bf16(v.w) << 16);
+                    const uint32_t lo = pack_bf16x2(v.x, v.y);
+                    const uint32_t hi = pack_bf16x2(v.z, v.w);
                     *reinterpret_cast<uint2*>(a.dH + o + c4 * 4) = make_uint2(lo, hi);
                 } else {
                     *reinterpret_cast<float4*>(a.dh_acc + o + c4 * 4) = v;
