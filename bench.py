@@ -42,7 +42,36 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run one device-to-device copy of BYTES (counter calibration)")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = ["chunked_lm_head_amd/csrc/gemm_core.h", "chunked_lm_head_amd/csrc/lmhead_kernels.hip",
+                  "chunked_lm_head_amd/csrc/lmhead_kernels.h", "chunked_lm_head_amd/build.py"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_tiles_headline_traffic.json")
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch of the forward tiles kernel, from the committed
+    FETCH_SIZE / WRITE_SIZE counter runs, if they were taken on the current
+    kernel sources (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_digest() or rec.get("workload") != workload:
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def main():
@@ -56,6 +85,17 @@ def main():
 
     import chunked_lm_head_amd as lm
     import workloads
+
+    if args.copy_probe:
+        # a plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE readings
+        # calibrate the counters to bytes
+        src = torch.ones(args.copy_probe // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": src.numel() * 4}), flush=True)
+        return
 
     wl = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -187,7 +227,7 @@ def main():
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(wl.name),
             "timing": "HIP events around lmhead_loss_fwd on its stream (label scan, row merge "
                       "and loss reduction add <1% next to the tiles kernel)",
         },
