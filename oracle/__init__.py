@@ -278,11 +278,29 @@ def support_dz(z: np.ndarray, ids: np.ndarray, ref_logq: Optional[np.ndarray],
 
 # ------------------------------------------------------------- whole-problem API
 
+def temperature_scale(n: int, temperature: float = 0.0, row_temperature=None) -> np.ndarray:
+    """Per-row temperature tau_n = t * r_n, with t = 1 when temperature is 0 (off) and
+    r_n = 1 without a per-row array (miles-ext-kernels PR #14, tests/cake/lm_head/ commit:
+    routes with the temperature off, scalar, per-row and 1.0). The method then works on
+    the logits z / tau_n."""
+    t = 1.0 if temperature == 0.0 else float(temperature)
+    tau = np.full(n, t, dtype=np.float64)
+    if row_temperature is not None:
+        tau = tau * np.asarray(row_temperature, dtype=np.float64)
+    if np.any(~(tau > 0)) or not np.all(np.isfinite(tau)):
+        raise ValueError("temperature must be positive and finite")
+    return tau
+
+
 def run(entry: int, H: np.ndarray, W: np.ndarray, *, targets=None, ids=None, ref_logq=None,
         grad=None, grad_kl=None, num_valid: int = -1, backward: bool = True,
-        threads: int = 0) -> dict:
-    """Full forward (+ backward) of one entry over every row. For small problems."""
-    z = logits(H, W, threads=threads)
+        temperature: float = 0.0, row_temperature=None, threads: int = 0) -> dict:
+    """Full forward (+ backward) of one entry over every row. For small problems.
+
+    With a temperature, every definition applies to z / tau_n, and the backward
+    multiplies dL/d(z / tau) by 1 / tau_n (chain rule) before the contractions."""
+    tau = temperature_scale(H.shape[0], temperature, row_temperature)
+    z = logits(H, W, threads=threads) / tau[:, None]
     out: dict = {}
     if entry in (ENTRY_CE_MEAN, ENTRY_CE_SUM):
         red = "mean" if entry == ENTRY_CE_MEAN else "sum"
@@ -306,6 +324,7 @@ def run(entry: int, H: np.ndarray, W: np.ndarray, *, targets=None, ids=None, ref
     else:
         raise ValueError(f"unknown entry {entry}")
     if backward:
+        dz = dz / tau[:, None]
         out["dz"] = dz
         out["dH"] = grad_hidden(dz, W, threads=threads)
         out["dW"] = grad_weight(dz, H, np.arange(H.shape[0]), threads=threads)
@@ -314,14 +333,16 @@ def run(entry: int, H: np.ndarray, W: np.ndarray, *, targets=None, ids=None, ref
 
 def rows_forward_backward(entry: int, H: np.ndarray, W: np.ndarray, rows, *, targets=None,
                           ids=None, ref_logq=None, grad=None, grad_kl=None,
-                          count: Optional[int] = None, threads: int = 0) -> dict:
+                          count: Optional[int] = None, temperature: float = 0.0,
+                          row_temperature=None, threads: int = 0) -> dict:
     """Forward values and dH for a sample of rows, each computed over the whole vocabulary.
 
     Rows are independent except through the CE mean's denominator, which the
     caller passes as ``count`` (the number of valid rows of the full problem).
     """
     rows = np.ascontiguousarray(rows, dtype=np.int64)
-    z = logits(H, W, rows, threads=threads)
+    tau = temperature_scale(H.shape[0], temperature, row_temperature)[rows]
+    z = logits(H, W, rows, threads=threads) / tau[:, None]
     out: dict = {"rows": rows}
     if entry in (ENTRY_CE_MEAN, ENTRY_CE_SUM):
         t = np.asarray(targets)[rows]
@@ -347,6 +368,7 @@ def rows_forward_backward(entry: int, H: np.ndarray, W: np.ndarray, rows, *, tar
         dz = support_dz(z, np.asarray(ids)[rows], None if ref_logq is None else ref_logq[rows],
                         None if grad is None else np.asarray(grad)[rows],
                         None if grad_kl is None else np.asarray(grad_kl)[rows])
+    dz = dz / tau[:, None]
     out["dz"] = dz
     out["dH"] = grad_hidden(dz, W, threads=threads)
     return out

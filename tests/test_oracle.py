@@ -420,3 +420,71 @@ def test_mutations_are_caught(monkeypatch):
     f = oracle.ce_forward(z, inp.targets)
     assert abs(f["loss_rows"].sum() / 64 - ref) > 1e-3
     assert abs(f["loss"] - ref) < 1e-12
+
+
+# ----------------------------------------------------------------- temperature
+
+def test_temperature_routes():
+    """tau = 1.0 equals no temperature exactly; a scalar tau equals logits / tau in
+    torch fp64 cross_entropy and autograd; a per-row tau scales each row."""
+    wl, inp = _tiny_inputs(n=24, hidden=64, vocab=300, ignore_frac=0.1, seed=17)
+    off = oracle.run(oracle.ENTRY_CE_MEAN, inp.H, inp.W, targets=inp.targets)
+    one = oracle.run(oracle.ENTRY_CE_MEAN, inp.H, inp.W, targets=inp.targets, temperature=1.0)
+    assert off["loss"] == one["loss"]
+    np.testing.assert_array_equal(off["dW"], one["dW"])
+    tau = np.linspace(0.5, 2.0, 24)
+    for temp, rowt in ((0.7, None), (0.0, tau), (1.3, tau)):
+        got = oracle.run(oracle.ENTRY_CE_MEAN, inp.H, inp.W, targets=inp.targets,
+                         temperature=temp, row_temperature=rowt)
+        H, W = _torch_problem(inp)
+        t_eff = torch.tensor((temp if temp else 1.0) * (rowt if rowt is not None else np.ones(24)))
+        z = (H @ W.T) / t_eff[:, None]
+        loss = F.cross_entropy(z, torch.tensor(inp.targets, dtype=torch.long), ignore_index=IGNORE_INDEX)
+        loss.backward()
+        assert abs(got["loss"] - loss.item()) < 1e-12
+        np.testing.assert_allclose(got["dH"], H.grad.numpy(), rtol=1e-10, atol=1e-14)
+        np.testing.assert_allclose(got["dW"], W.grad.numpy(), rtol=1e-10, atol=1e-14)
+
+
+@pytest.mark.parametrize("entry", [0, 2, 3])
+def test_temperature_finite_differences(entry):
+    rng = np.random.default_rng(300 + entry)
+    N, Hd, V, K = 3, 6, 12, 3
+    H = rng.standard_normal((N, Hd))
+    W = rng.standard_normal((V, Hd)) * 0.5
+    t = np.array([2, -100, 11])
+    ids = np.stack([rng.choice(V, K, replace=False) for _ in range(N)])
+    q = rng.random((N, K)) + 0.1
+    rq = np.log(q / q.sum(1, keepdims=True))
+    rowt = np.array([0.6, 1.7, 1.1])
+    g = np.array([0.9]) if entry == 0 else rng.standard_normal(N if entry == 2 else (N, K))
+    gkl = rng.standard_normal(N) if entry == 3 else None
+    kw = dict(targets=t if entry < 3 else None, ids=ids if entry == 3 else None,
+              ref_logq=rq if entry == 3 else None, grad=g, grad_kl=gkl,
+              temperature=0.8, row_temperature=rowt)
+    out = oracle.run(entry, H, W, **kw)
+
+    def obj(Hx, Wx):
+        f = oracle.run(entry, Hx, Wx, backward=False, **kw)
+        if entry == 0:
+            return float(g[0] * f["loss"])
+        if entry == 2:
+            return float((f["logp"] * g).sum())
+        return float((f["lp"] * g).sum() + (f["kl"] * gkl).sum())
+
+    h = 1e-6
+    for name, X, G in (("H", H, out["dH"]), ("W", W, out["dW"])):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(X.shape):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[idx] += h
+            Xm[idx] -= h
+            num[idx] = ((obj(Xp, W) - obj(Xm, W)) if name == "H" else (obj(H, Xp) - obj(H, Xm))) / (2 * h)
+        np.testing.assert_allclose(G, num, rtol=1e-6, atol=1e-8, err_msg=f"d{name} entry {entry}")
+
+
+def test_temperature_rejects_nonpositive():
+    with pytest.raises(ValueError):
+        oracle.temperature_scale(3, -1.0)
+    with pytest.raises(ValueError):
+        oracle.temperature_scale(3, 0.0, np.array([1.0, 0.0, 2.0]))
