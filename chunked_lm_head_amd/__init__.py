@@ -44,6 +44,7 @@ ENTRY_SUPPORT = 3
 
 DEVERR_LABEL = 1
 DEVERR_CANDIDATE = 2
+DEVERR_TEMPERATURE = 4
 
 IGNORE_INDEX = -100
 
@@ -57,12 +58,17 @@ class lmhead_problem(ctypes.Structure):
         ("num_valid", ctypes.c_int64),
         ("k", ctypes.c_int32),
         ("flags", ctypes.c_int32),
+        ("temperature", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
+        ("row_temperature", ctypes.c_void_p),
     ]
 
 
 def problem(n: int, hidden: int, vocab: int, chunk: int, num_valid: int = -1, k: int = 1,
-            flags: int = 0) -> lmhead_problem:
-    return lmhead_problem(n, hidden, vocab, chunk, num_valid, k, flags)
+            flags: int = 0, temperature: float = 0.0, row_temperature=None) -> lmhead_problem:
+    """row_temperature: a device fp32 [n] tensor (kept alive by the caller) or an address."""
+    return lmhead_problem(n, hidden, vocab, chunk, num_valid, k, flags, float(temperature), 0,
+                          _p(row_temperature))
 
 
 class LMHeadError(RuntimeError):
@@ -178,6 +184,15 @@ def _check_inputs(H: torch.Tensor, W: torch.Tensor, idx: torch.Tensor):
         raise ValueError("expected H [n, hidden] and W [vocab, hidden]")
 
 
+def _check_row_temperature(rt, n: int):
+    if rt is None:
+        return
+    if not isinstance(rt, torch.Tensor) or rt.device.type != "cuda":
+        raise ValueError("row_temperature must be a tensor on a GPU device")
+    if rt.dtype != torch.float32 or not rt.is_contiguous() or tuple(rt.shape) != (n,):
+        raise ValueError("row_temperature must be a contiguous float32 tensor of shape [n]")
+
+
 def workspace(p: lmhead_problem, entry: int, with_backward: bool, device) -> torch.Tensor:
     nbytes = lmhead_workspace_size(p, entry, int(with_backward))
     if nbytes == 0:
@@ -191,11 +206,15 @@ def _ok(status: int, where: str):
 
 
 def ce_loss_forward(H, W, targets, chunk: int, reduction: str = "mean", num_valid: int = -1,
-                    ws: Optional[torch.Tensor] = None):
-    """Returns (loss fp32 [], lse fp32 [n], workspace)."""
+                    ws: Optional[torch.Tensor] = None, temperature: float = 0.0,
+                    row_temperature=None):
+    """Returns (loss fp32 [], lse fp32 [n], workspace). temperature 0 = off;
+    row_temperature: optional fp32 [n] factors (tau_n = t * r_n)."""
     _check_inputs(H, W, targets)
+    _check_row_temperature(row_temperature, H.shape[0])
     entry = ENTRY_CE_MEAN if reduction == "mean" else ENTRY_CE_SUM
-    p = problem(H.shape[0], H.shape[1], W.shape[0], chunk, num_valid)
+    p = problem(H.shape[0], H.shape[1], W.shape[0], chunk, num_valid,
+                temperature=temperature, row_temperature=row_temperature)
     if ws is None:
         ws = workspace(p, entry, False, H.device)
     loss = torch.empty(1, dtype=torch.float32, device=H.device)
@@ -204,10 +223,13 @@ def ce_loss_forward(H, W, targets, chunk: int, reduction: str = "mean", num_vali
     return loss[0], lse, ws
 
 
-def logprob_forward(H, W, targets, chunk: int, ws: Optional[torch.Tensor] = None):
-    """Returns (logp fp32 [n], lse fp32 [n], workspace)."""
+def logprob_forward(H, W, targets, chunk: int, ws: Optional[torch.Tensor] = None,
+                    temperature: float = 0.0, row_temperature=None):
+    """Returns (logp fp32 [n], lse fp32 [n], workspace); lse is of the tempered logits."""
     _check_inputs(H, W, targets)
-    p = problem(H.shape[0], H.shape[1], W.shape[0], chunk)
+    _check_row_temperature(row_temperature, H.shape[0])
+    p = problem(H.shape[0], H.shape[1], W.shape[0], chunk, temperature=temperature,
+                row_temperature=row_temperature)
     if ws is None:
         ws = workspace(p, ENTRY_LOGPROB, False, H.device)
     logp = torch.empty(H.shape[0], dtype=torch.float32, device=H.device)
@@ -216,11 +238,14 @@ def logprob_forward(H, W, targets, chunk: int, ws: Optional[torch.Tensor] = None
     return logp, lse, ws
 
 
-def support_forward(H, W, ids, ref_logq, chunk: int, ws: Optional[torch.Tensor] = None):
+def support_forward(H, W, ids, ref_logq, chunk: int, ws: Optional[torch.Tensor] = None,
+                    temperature: float = 0.0, row_temperature=None):
     """Returns (lp fp32 [n, k], kl fp32 [n] or None, lse fp32 [n], workspace)."""
     _check_inputs(H, W, ids)
     n, k = ids.shape
-    p = problem(n, H.shape[1], W.shape[0], chunk, -1, k)
+    _check_row_temperature(row_temperature, n)
+    p = problem(n, H.shape[1], W.shape[0], chunk, -1, k, temperature=temperature,
+                row_temperature=row_temperature)
     if ws is None:
         ws = workspace(p, ENTRY_SUPPORT, False, H.device)
     lp = torch.empty(n, k, dtype=torch.float32, device=H.device)
@@ -233,11 +258,15 @@ def support_forward(H, W, ids, ref_logq, chunk: int, ws: Optional[torch.Tensor] 
 
 def backward(entry: int, H, W, idx, lse, grad, chunk: int, *, ref_logq=None, saved_lp=None,
              grad_kl=None, num_valid: int = -1, need_dH: bool = True, need_dW: bool = True,
-             ws: Optional[torch.Tensor] = None, dH=None, dW=None):
-    """Returns (dH bf16 [n, hidden] or None, dW bf16 [vocab, hidden] or None)."""
+             ws: Optional[torch.Tensor] = None, dH=None, dW=None, temperature: float = 0.0,
+             row_temperature=None):
+    """Returns (dH bf16 [n, hidden] or None, dW bf16 [vocab, hidden] or None).
+    temperature / row_temperature must be those of the forward that produced lse."""
     _check_inputs(H, W, idx)
+    _check_row_temperature(row_temperature, H.shape[0])
     k = idx.shape[1] if entry == ENTRY_SUPPORT else 1
-    p = problem(H.shape[0], H.shape[1], W.shape[0], chunk, num_valid, k)
+    p = problem(H.shape[0], H.shape[1], W.shape[0], chunk, num_valid, k,
+                temperature=temperature, row_temperature=row_temperature)
     if ws is None:
         ws = workspace(p, entry, True, H.device)
     if need_dH and dH is None:
@@ -256,50 +285,57 @@ class ChunkedLMHeadCE(torch.autograd.Function):
     """Cross-entropy of softmax(H W^T) against targets, mean or sum over valid rows."""
 
     @staticmethod
-    def forward(ctx, H, W, targets, chunk, reduction="mean", num_valid=-1):
-        loss, lse, _ = ce_loss_forward(H, W, targets, chunk, reduction, num_valid)
-        ctx.save_for_backward(H, W, targets, lse)
-        ctx.cfg = (chunk, reduction, num_valid)
+    def forward(ctx, H, W, targets, chunk, reduction="mean", num_valid=-1, temperature=0.0,
+                row_temperature=None):
+        loss, lse, _ = ce_loss_forward(H, W, targets, chunk, reduction, num_valid,
+                                       temperature=temperature, row_temperature=row_temperature)
+        ctx.save_for_backward(H, W, targets, lse, row_temperature)
+        ctx.cfg = (chunk, reduction, num_valid, temperature)
         return loss
 
     @staticmethod
     def backward(ctx, g):
-        H, W, targets, lse = ctx.saved_tensors
-        chunk, reduction, num_valid = ctx.cfg
+        H, W, targets, lse, rt = ctx.saved_tensors
+        chunk, reduction, num_valid, temperature = ctx.cfg
         entry = ENTRY_CE_MEAN if reduction == "mean" else ENTRY_CE_SUM
         grad = g.reshape(1).to(torch.float32).contiguous()
         dH, dW = backward(entry, H, W, targets, lse, grad, chunk, num_valid=num_valid,
-                          need_dH=ctx.needs_input_grad[0], need_dW=ctx.needs_input_grad[1])
-        return dH, dW, None, None, None, None
+                          need_dH=ctx.needs_input_grad[0], need_dW=ctx.needs_input_grad[1],
+                          temperature=temperature, row_temperature=rt)
+        return dH, dW, None, None, None, None, None, None
 
 
 class ChunkedLMHeadLogprob(torch.autograd.Function):
     """Per-token log-probability of the target under softmax(H W^T)."""
 
     @staticmethod
-    def forward(ctx, H, W, targets, chunk):
-        logp, lse, _ = logprob_forward(H, W, targets, chunk)
-        ctx.save_for_backward(H, W, targets, lse)
-        ctx.chunk = chunk
+    def forward(ctx, H, W, targets, chunk, temperature=0.0, row_temperature=None):
+        logp, lse, _ = logprob_forward(H, W, targets, chunk, temperature=temperature,
+                                       row_temperature=row_temperature)
+        ctx.save_for_backward(H, W, targets, lse, row_temperature)
+        ctx.cfg = (chunk, temperature)
         return logp
 
     @staticmethod
     def backward(ctx, g):
-        H, W, targets, lse = ctx.saved_tensors
+        H, W, targets, lse, rt = ctx.saved_tensors
+        chunk, temperature = ctx.cfg
         dH, dW = backward(ENTRY_LOGPROB, H, W, targets, lse, g.to(torch.float32).contiguous(),
-                          ctx.chunk, need_dH=ctx.needs_input_grad[0],
-                          need_dW=ctx.needs_input_grad[1])
-        return dH, dW, None, None
+                          chunk, need_dH=ctx.needs_input_grad[0],
+                          need_dW=ctx.needs_input_grad[1], temperature=temperature,
+                          row_temperature=rt)
+        return dH, dW, None, None, None, None
 
 
 class ChunkedLMHeadSupport(torch.autograd.Function):
     """Full-vocabulary log-probabilities of K candidates per row and KL(q || p_hat)."""
 
     @staticmethod
-    def forward(ctx, H, W, ids, ref_logq, chunk):
-        lp, kl, lse, _ = support_forward(H, W, ids, ref_logq, chunk)
-        ctx.save_for_backward(H, W, ids, ref_logq, lse, lp)
-        ctx.chunk = chunk
+    def forward(ctx, H, W, ids, ref_logq, chunk, temperature=0.0, row_temperature=None):
+        lp, kl, lse, _ = support_forward(H, W, ids, ref_logq, chunk, temperature=temperature,
+                                         row_temperature=row_temperature)
+        ctx.save_for_backward(H, W, ids, ref_logq, lse, lp, row_temperature)
+        ctx.cfg = (chunk, temperature)
         ctx.has_kl = kl is not None
         if kl is None:
             kl = torch.zeros(H.shape[0], dtype=torch.float32, device=H.device)
@@ -307,23 +343,28 @@ class ChunkedLMHeadSupport(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, g_lp, g_kl):
-        H, W, ids, ref_logq, lse, lp = ctx.saved_tensors
+        H, W, ids, ref_logq, lse, lp, rt = ctx.saved_tensors
+        chunk, temperature = ctx.cfg
         gl = g_lp.to(torch.float32).contiguous() if g_lp is not None else None
         gk = g_kl.to(torch.float32).contiguous() if (g_kl is not None and ctx.has_kl) else None
-        dH, dW = backward(ENTRY_SUPPORT, H, W, ids, lse, gl, ctx.chunk,
+        dH, dW = backward(ENTRY_SUPPORT, H, W, ids, lse, gl, chunk,
                           ref_logq=ref_logq if ctx.has_kl else None,
                           saved_lp=lp if ctx.has_kl else None, grad_kl=gk,
-                          need_dH=ctx.needs_input_grad[0], need_dW=ctx.needs_input_grad[1])
-        return dH, dW, None, None, None
+                          need_dH=ctx.needs_input_grad[0], need_dW=ctx.needs_input_grad[1],
+                          temperature=temperature, row_temperature=rt)
+        return dH, dW, None, None, None, None, None
 
 
-def ce_loss(H, W, targets, chunk: int = 8192, reduction: str = "mean", num_valid: int = -1):
-    return ChunkedLMHeadCE.apply(H, W, targets, chunk, reduction, num_valid)
+def ce_loss(H, W, targets, chunk: int = 8192, reduction: str = "mean", num_valid: int = -1,
+            temperature: float = 0.0, row_temperature=None):
+    return ChunkedLMHeadCE.apply(H, W, targets, chunk, reduction, num_valid, temperature,
+                                 row_temperature)
 
 
-def logprob(H, W, targets, chunk: int = 8192):
-    return ChunkedLMHeadLogprob.apply(H, W, targets, chunk)
+def logprob(H, W, targets, chunk: int = 8192, temperature: float = 0.0, row_temperature=None):
+    return ChunkedLMHeadLogprob.apply(H, W, targets, chunk, temperature, row_temperature)
 
 
-def support_logprob_kl(H, W, ids, ref_logq, chunk: int = 8192):
-    return ChunkedLMHeadSupport.apply(H, W, ids, ref_logq, chunk)
+def support_logprob_kl(H, W, ids, ref_logq, chunk: int = 8192, temperature: float = 0.0,
+                       row_temperature=None):
+    return ChunkedLMHeadSupport.apply(H, W, ids, ref_logq, chunk, temperature, row_temperature)

@@ -35,7 +35,9 @@ struct Layout {
 int validate_problem(const lmhead_problem* p, int entry) {
     if (p == nullptr) return LMHEAD_ERR_ARG;
     if (entry < LMHEAD_ENTRY_CE_MEAN || entry > LMHEAD_ENTRY_SUPPORT) return LMHEAD_ERR_ARG;
-    if (p->flags != 0) return LMHEAD_ERR_ARG;
+    if (p->flags != 0 || p->reserved != 0) return LMHEAD_ERR_ARG;
+    // scalar temperature: 0 (off) or positive and finite
+    if (!(p->temperature >= 0.0f && p->temperature <= 3.402823466e38f)) return LMHEAD_ERR_ARG;
     if (p->n < 0 || p->n > kMaxRows) return LMHEAD_ERR_SHAPE;
     if (p->hidden < 64 || p->hidden > kMaxHidden || p->hidden % 64 != 0) return LMHEAD_ERR_SHAPE;
     if (p->vocab < 1 || p->vocab > kMaxVocab) return LMHEAD_ERR_SHAPE;
@@ -84,6 +86,13 @@ Layout plan(const lmhead_problem& p, int entry) {
 
 bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
 
+Temperature temperature_of(const lmhead_problem& p) {
+    Temperature T;
+    T.t = p.temperature == 0.0f ? 1.0f : p.temperature;
+    T.row = p.row_temperature;
+    return T;
+}
+
 int check_device() {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return LMHEAD_ERR_DEVICE;
@@ -123,9 +132,11 @@ int forward(const lmhead_problem* p, int entry, const void* H, const void* W, co
         if (!ce && row_out == nullptr) return LMHEAD_ERR_ARG;
     }
     if (kl != nullptr && ref_logq == nullptr) return LMHEAD_ERR_ARG;
-    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(ws, 256)) return LMHEAD_ERR_ALIGN;
+    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(ws, 256) || !aligned(p->row_temperature, 4))
+        return LMHEAD_ERR_ALIGN;
     const Layout L = plan(*p, entry);
     if (ws_bytes < L.fwd_total) return LMHEAD_ERR_WORKSPACE;
+    const Temperature T = temperature_of(*p);
     st = check_device();
     if (st != LMHEAD_OK) return st;
 
@@ -139,8 +150,9 @@ int forward(const lmhead_problem* p, int entry, const void* H, const void* W, co
     }
     const bool support = entry == LMHEAD_ENTRY_SUPPORT;
     scan_labels_kernel<<<grid_1d(L.n, kThreads, 1024), kThreads, 0, s>>>(ids, L.n, (int)L.k, L.vocab,
-                                                                          support ? 1 : 0, hdr);
+                                                                          support ? 1 : 0, T, hdr);
     FwdTilesArgs fa;
+    fa.T = T;
     fa.H = (const bf16_bits*)H;
     fa.W = (const bf16_bits*)W;
     fa.n = L.n;
@@ -155,6 +167,7 @@ int forward(const lmhead_problem* p, int entry, const void* H, const void* W, co
     fwd_tiles_kernel<<<(unsigned)(fa.tiles_m * fa.tiles_n), kThreads, 0, s>>>(fa);
 
     FinalizeArgs fin;
+    fin.T = T;
     fin.part = fa.part;
     fin.n = L.n;
     fin.tiles_n = L.tiles_v;
@@ -220,10 +233,11 @@ int lmhead_loss_bwd(const lmhead_problem* p, int entry, const void* H, const voi
             return LMHEAD_ERR_ARG;
     }
     if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16) ||
-        !aligned(workspace, 256))
+        !aligned(workspace, 256) || !aligned(p->row_temperature, 4))
         return LMHEAD_ERR_ALIGN;
     const Layout L = plan(*p, entry);
     if (workspace_bytes < L.bwd_total) return LMHEAD_ERR_WORKSPACE;
+    const Temperature T = temperature_of(*p);
     st = check_device();
     if (st != LMHEAD_OK) return st;
     if (dH == nullptr && dW == nullptr) return LMHEAD_OK;
@@ -237,8 +251,9 @@ int lmhead_loss_bwd(const lmhead_problem* p, int entry, const void* H, const voi
         return launched();
     }
     scan_labels_kernel<<<grid_1d(L.n, kThreads, 1024), kThreads, 0, s>>>(ids, L.n, (int)L.k, L.vocab,
-                                                                          support ? 1 : 0, hdr);
+                                                                          support ? 1 : 0, T, hdr);
     CoeffArgs ca;
+    ca.T = T;
     ca.entry = entry;
     ca.n = L.n;
     ca.n_pad = L.n_pad;
@@ -274,6 +289,7 @@ int lmhead_loss_bwd(const lmhead_problem* p, int entry, const void* H, const voi
         const bf16_bits* Wc = (const bf16_bits*)W + v0 * L.hidden;
 
         LogitGradArgs ga;
+        ga.T = T;
         ga.H = (const bf16_bits*)H;
         ga.Wc = Wc;
         ga.n = L.n;

@@ -21,6 +21,20 @@ constexpr int kHdrErrRow = 1;
 constexpr int kHdrCount = 2;
 constexpr int kDevErrLabel = 1;
 constexpr int kDevErrCandidate = 2;
+constexpr int kDevErrTemperature = 4;
+
+// Temperature: tau_n = t * r_n (r_n = 1 without a per-row array). Kernels use
+// 1 / tau_n; tau_n = 1 gives exactly 1, so that route is bit-identical to no
+// temperature.
+struct Temperature {
+    float t;            // scalar, already resolved (1 when off)
+    const float* row;   // [n] or null
+};
+
+__device__ __forceinline__ float row_tau(const Temperature& T, int64_t row) {
+    return T.row != nullptr ? T.t * T.row[row] : T.t;
+}
+__device__ __forceinline__ bool tau_ok(float tau) { return tau > 0.0f && tau <= 3.402823466e38f; }
 
 struct FwdTilesArgs {
     const bf16_bits* H;
@@ -31,6 +45,7 @@ struct FwdTilesArgs {
     int k;
     float2* part;         // [tiles_n, n] (max, sum) per (tile, row)
     float* zg;            // [n, k] logits at the ids
+    Temperature T;
 };
 
 struct FinalizeArgs {
@@ -44,6 +59,7 @@ struct FinalizeArgs {
     float* lse;             // [n]
     float* row_out;         // CE: loss rows; logprob: logp [n]; support: lp [n, k]
     float* kl;              // support: [n] or null
+    Temperature T;
 };
 
 struct CoeffArgs {
@@ -59,6 +75,7 @@ struct CoeffArgs {
     int64_t num_valid;
     float* coef_a;   // [n_pad]
     float* coef_c;   // [n, k]
+    Temperature T;
 };
 
 struct LogitGradArgs {
@@ -74,6 +91,7 @@ struct LogitGradArgs {
     const float* lse;
     bf16_bits* G;          // [n_pad, w_pad] or null
     bf16_bits* Gt;         // [w_pad, n_pad] or null
+    Temperature T;
 };
 
 struct DwArgs {
@@ -96,7 +114,7 @@ struct DhArgs {
 
 __global__ void init_header_kernel(int32_t* hdr);
 __global__ void scan_labels_kernel(const int32_t* ids, int64_t n, int k, int64_t vocab, int support,
-                                   int32_t* hdr);
+                                   Temperature T, int32_t* hdr);
 __global__ void fill_u32_kernel(uint32_t* p, int64_t count, uint32_t value);
 __global__ void fwd_tiles_kernel(FwdTilesArgs a);
 __global__ void finalize_rows_kernel(FinalizeArgs a);

@@ -38,13 +38,17 @@ __global__ void init_header_kernel(int32_t* hdr) {
 // value is an ignored row, t >= V is an error (miles-ext-kernels PR #14, the
 // commit declaring the lm_head op). Candidate ids must lie in [0, V).
 __global__ void scan_labels_kernel(const int32_t* ids, int64_t n, int k, int64_t vocab,
-                                   int support, int32_t* hdr) {
+                                   int support, Temperature T, int32_t* hdr) {
     __shared__ int32_t s_count, s_row, s_code;
     if (threadIdx.x == 0) { s_count = 0; s_row = INT_MAX; s_code = 0; }
     __syncthreads();
     int32_t count = 0, row_min = INT_MAX, code = 0;
     for (int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; row < n;
          row += (int64_t)gridDim.x * blockDim.x) {
+        if (T.row != nullptr && !tau_ok(row_tau(T, row))) {
+            code |= kDevErrTemperature;
+            row_min = row_min < row ? row_min : (int32_t)row;
+        }
         if (!support) {
             const int64_t t = ids[row];
             if (t >= vocab) { code |= kDevErrLabel; row_min = row_min < row ? row_min : (int32_t)row; }
@@ -96,7 +100,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTilesArgs a) 
     const int wr = wave >> 1, wc = wave & 1;
     const int64_t row = m0 + tid;
     const bool row_ok = row < a.n;
-    const float* Sr = S + tid;
+    // logits / tau_n (the scale is exactly 1 without a temperature)
+    const float inv_tau = row_ok ? 1.0f / row_tau(a.T, row) : 1.0f;
+    float* Sr = S + tid;
     float run_m = neg_inf(), run_s = 0.0f;
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
@@ -105,6 +111,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTilesArgs a) 
         const int64_t col0 = n0 + half * 128;
         const int64_t rem = a.vocab - col0;
         const int ncol = rem <= 0 ? 0 : (rem >= 128 ? 128 : (int)rem);
+        if (inv_tau != 1.0f)
+            for (int c = 0; c < ncol; ++c) Sr[c * kEpiStride] *= inv_tau;
         float m = neg_inf();
         for (int c = 0; c < ncol; ++c) m = fmaxf(m, Sr[c * kEpiStride]);
         const float mb = m * kLog2e;
@@ -172,9 +180,10 @@ __global__ void finalize_rows_kernel(FinalizeArgs a) {
     if (!live || sub != 0) return;
     const float lse = M + logf(S);
     a.lse[row] = lse;
+    const bool bad_tau = a.T.row != nullptr && !tau_ok(row_tau(a.T, row));
     if (a.entry == kEntryCeMean || a.entry == kEntryCeSum || a.entry == kEntryLogprob) {
         const int64_t t = a.ids[row];
-        const bool bad = t >= a.vocab;
+        const bool bad = t >= a.vocab || bad_tau;
         const bool valid = t >= 0 && !bad;
         const float zt = valid ? a.zg[row] : 0.0f;
         float out;
@@ -187,7 +196,7 @@ __global__ void finalize_rows_kernel(FinalizeArgs a) {
     const int k = a.k;
     const int32_t* idr = a.ids + row * k;
     const float* zc = a.zg + row * k;
-    bool bad = false;
+    bool bad = bad_tau;
     for (int kk = 0; kk < k; ++kk) {
         const int64_t id = idr[kk];
         bad = bad || id < 0 || id >= a.vocab;
@@ -256,9 +265,13 @@ __global__ void coeffs_kernel(CoeffArgs a) {
         return;
     }
     const int k = a.k;
+    // chain rule through z / tau_n: every coefficient carries 1 / tau_n
+    const float tau = row_tau(a.T, row);
+    const bool good_tau = a.T.row == nullptr || tau_ok(tau);
+    const float inv_tau = good_tau ? 1.0f / tau : 0.0f;
     if (a.entry != kEntrySupport) {
         const int64_t t = a.ids[row];
-        const bool valid = t >= 0 && t < a.vocab;
+        const bool valid = t >= 0 && t < a.vocab && good_tau;
         float ca = 0.0f, cc = 0.0f;
         if (a.entry == kEntryCeMean) {
             const int64_t cnt = a.num_valid >= 0 ? a.num_valid : (int64_t)a.hdr[kHdrCount];
@@ -272,12 +285,12 @@ __global__ void coeffs_kernel(CoeffArgs a) {
             ca = -g;
             cc = g;
         }
-        a.coef_a[row] = ca;
-        a.coef_c[row] = cc;
+        a.coef_a[row] = ca * inv_tau;
+        a.coef_c[row] = cc * inv_tau;
         return;
     }
     const int32_t* idr = a.ids + row * k;
-    bool bad = false;
+    bool bad = !good_tau;
     for (int kk = 0; kk < k; ++kk) {
         const int64_t id = idr[kk];
         bad = bad || id < 0 || id >= a.vocab;
@@ -295,7 +308,7 @@ __global__ void coeffs_kernel(CoeffArgs a) {
         gsum += gk;
         c[kk] = gk;
     }
-    a.coef_a[row] = -gsum;
+    a.coef_a[row] = -gsum * inv_tau;
     if (a.grad_kl != nullptr) {
         const float beta = a.grad_kl[row];
         const float* lp = a.saved_lp + row * k;
@@ -313,6 +326,7 @@ __global__ void coeffs_kernel(CoeffArgs a) {
             c[kk] += beta * (Q * phat - expf(r[kk]));
         }
     }
+    for (int kk = 0; kk < k; ++kk) c[kk] *= inv_tau;
 }
 
 // Recompute one chunk's logits tile and write dL/dz in bf16: G[n, j] = a_n
@@ -336,6 +350,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
     const bool row_ok = row < a.n;
     const float ca = row_ok ? a.coef_a[row] : 0.0f;
     const float lb = row_ok ? a.lse[row] * kLog2e : 0.0f;
+    const float xs = row_ok ? kLog2e / row_tau(a.T, row) : kLog2e;   // log2(e) / tau_n
     float* Sr = S + tid;
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
@@ -346,7 +361,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
         const int ncol = rem <= 0 ? 0 : (rem >= 128 ? 128 : (int)rem);
         for (int c = 0; c < 128; ++c) {
             const float x = Sr[c * kEpiStride];
-            Sr[c * kEpiStride] = (c < ncol && ca != 0.0f) ? ca * exp2_fast(__builtin_fmaf(x, kLog2e, -lb)) : 0.0f;
+            Sr[c * kEpiStride] = (c < ncol && ca != 0.0f) ? ca * exp2_fast(__builtin_fmaf(x, xs, -lb)) : 0.0f;
         }
         if (row_ok) {
             const int32_t* idr = a.ids + row * a.k;

@@ -40,9 +40,10 @@
  *     pointers, a small workspace, a device that is not gfx950) return a
  *     status before anything is enqueued.
  *   - Data errors found on the device (a label >= vocab, a candidate id
- *     outside [0, vocab)) never trap: the row's outputs become NaN (forward)
- *     or the row gets zero gradient (backward), and the workspace's error
- *     word records the lowest offending row (lmhead_read_device_error).
+ *     outside [0, vocab), a per-row temperature that is not positive and
+ *     finite) never trap: the row's outputs become NaN (forward) or the row
+ *     gets zero gradient (backward), and the workspace's error word records
+ *     the lowest offending row (lmhead_read_device_error).
  *   - Results are a function of (inputs, problem incl. chunk, library build,
  *     device model): no floating-point atomics, every reduction runs in a
  *     fixed order, and the work decomposition does not depend on the number
@@ -84,7 +85,8 @@ enum lmhead_entry {
 enum lmhead_device_error {
     LMHEAD_DEVERR_NONE = 0,
     LMHEAD_DEVERR_LABEL = 1,     /* a label >= vocab ([PR14-op]) */
-    LMHEAD_DEVERR_CANDIDATE = 2  /* a candidate id outside [0, vocab) */
+    LMHEAD_DEVERR_CANDIDATE = 2, /* a candidate id outside [0, vocab) */
+    LMHEAD_DEVERR_TEMPERATURE = 4 /* a per-row temperature that is not positive and finite */
 };
 
 /*
@@ -104,6 +106,15 @@ enum lmhead_device_error {
  *   k          candidates per row for LMHEAD_ENTRY_SUPPORT (1..1024);
  *              ignored by the other entries.
  *   flags      reserved, must be 0.
+ *   temperature     scalar temperature t applied to every row; 0 = off
+ *                   (t = 1). Must be finite and >= 0.
+ *   reserved        must be 0.
+ *   row_temperature device fp32 [n] per-row temperatures r_n, or NULL.
+ *              Every entry then works on the logits z / tau_n with
+ *              tau_n = t * r_n (temperature routes off, scalar, per-row and
+ *              1.0: [PR14-tests]); tau_n = 1 gives bit-identical results to
+ *              no temperature. A tau_n that is not positive and finite is a
+ *              data error (LMHEAD_DEVERR_TEMPERATURE) handled like a bad label.
  */
 typedef struct lmhead_problem {
     int64_t n;
@@ -113,6 +124,9 @@ typedef struct lmhead_problem {
     int64_t num_valid;
     int32_t k;
     int32_t flags;
+    float temperature;
+    int32_t reserved;
+    const float* row_temperature;
 } lmhead_problem;
 
 /*

@@ -84,29 +84,30 @@ class Dev:
 
 
 def run_entry(d: Dev, entry: int, chunk: int, *, num_valid=-1, need_dH=True, need_dW=True,
-              with_kl=True, stream=None):
+              with_kl=True, stream=None, temperature=0.0, row_temperature=None):
     """Forward + backward of one entry through the C ABI. Returns torch outputs."""
     out = {}
+    tk = dict(temperature=temperature, row_temperature=row_temperature)
     if entry in (lm.ENTRY_CE_MEAN, lm.ENTRY_CE_SUM):
         red = "mean" if entry == lm.ENTRY_CE_MEAN else "sum"
-        loss, lse, _ = lm.ce_loss_forward(d.H, d.W, d.t, chunk, red, num_valid)
+        loss, lse, _ = lm.ce_loss_forward(d.H, d.W, d.t, chunk, red, num_valid, **tk)
         out.update(loss=loss, lse=lse)
         grad = d.grad
         idx, saved_lp, ref, gkl = d.t, None, None, None
     elif entry == lm.ENTRY_LOGPROB:
-        logp, lse, _ = lm.logprob_forward(d.H, d.W, d.t, chunk)
+        logp, lse, _ = lm.logprob_forward(d.H, d.W, d.t, chunk, **tk)
         out.update(logp=logp, lse=lse)
         grad = d.grad
         idx, saved_lp, ref, gkl = d.t, None, None, None
     else:
         ref = d.ref_logq if with_kl else None
-        lp, kl, lse, _ = lm.support_forward(d.H, d.W, d.ids, ref, chunk)
+        lp, kl, lse, _ = lm.support_forward(d.H, d.W, d.ids, ref, chunk, **tk)
         out.update(lp=lp, kl=kl, lse=lse)
         grad = d.grad
         idx, saved_lp, gkl = d.ids, (lp if with_kl else None), (d.grad_kl if with_kl else None)
     if need_dH or need_dW:
         dH, dW = lm.backward(entry, d.H, d.W, idx, out["lse"], grad, chunk, ref_logq=ref,
                              saved_lp=saved_lp, grad_kl=gkl, num_valid=num_valid,
-                             need_dH=need_dH, need_dW=need_dW)
+                             need_dH=need_dH, need_dW=need_dW, **tk)
         out.update(dH=dH, dW=dW)
     return out

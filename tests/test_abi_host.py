@@ -55,7 +55,9 @@ def test_workspace_size_rules():
     assert ws(_p(), lm.ENTRY_CE_MEAN, 1) >= ws(_p(), lm.ENTRY_CE_MEAN, 0)
     # invalid problems report 0
     for bad in (dict(hidden=100), dict(hidden=0), dict(vocab=0), dict(chunk=100), dict(chunk=0),
-                dict(n=-1), dict(num_valid=-2), dict(flags=1), dict(n=1 << 31)):
+                dict(n=-1), dict(num_valid=-2), dict(flags=1), dict(n=1 << 31),
+                dict(temperature=-1.0), dict(temperature=float("inf")),
+                dict(temperature=float("nan"))):
         assert ws(_p(**bad), lm.ENTRY_CE_MEAN, 0) == 0, bad
     assert ws(_p(), 7, 0) == 0
     assert ws(_p(k=0), lm.ENTRY_SUPPORT, 0) == 0
@@ -107,6 +109,28 @@ def test_host_errors_precede_device_use():
         == lm.LMHEAD_ERR_WORKSPACE
     assert b(p, 9, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, BIG, 0) \
         == lm.LMHEAD_ERR_ARG
+
+
+def test_temperature_host_checks():
+    """The scalar temperature is 0 (off) or positive and finite; the reserved
+    word is 0; a per-row temperature array is 4-byte aligned."""
+    ws = lm.lmhead_workspace_size
+    assert ws(_p(temperature=0.7), 0, 1) == ws(_p(), 0, 1)
+    assert ws(_p(temperature=0.7, row_temperature=FAKE), 0, 1) == ws(_p(), 0, 1)
+    f = lm.lmhead_loss_fwd
+    W = ws(_p(), 0, 1)
+    for t in (-0.5, float("inf"), float("nan")):
+        assert f(_p(temperature=t), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, W, 0) == lm.LMHEAD_ERR_ARG
+    q = _p()
+    q.reserved = 1
+    assert f(q, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, W, 0) == lm.LMHEAD_ERR_ARG
+    assert f(_p(row_temperature=FAKE + 2), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, W, 0) \
+        == lm.LMHEAD_ERR_ALIGN
+    b = lm.lmhead_loss_bwd
+    assert b(_p(row_temperature=FAKE + 1), 0, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE,
+             FAKE, FAKE, BIG, 0) == lm.LMHEAD_ERR_ALIGN
+    assert b(_p(temperature=-2.0), 0, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE,
+             FAKE, FAKE, BIG, 0) == lm.LMHEAD_ERR_ARG
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
