@@ -10,7 +10,8 @@ Two layers:
 
 * ``lmhead_workspace_size``, ``lmhead_loss_fwd``, ``lmhead_logprob``,
   ``lmhead_support_logprob_kl``, ``lmhead_loss_bwd``,
-  ``lmhead_status_string``, ``lmhead_read_device_error``: the C entry points
+  ``lmhead_loss_bwd_accumulate``, ``lmhead_status_string``,
+  ``lmhead_read_device_error``: the C entry points
   under the same names. Pointer arguments accept a torch tensor, an integer
   address or None; the return value is the C status code.
 * ``ce_loss``, ``logprob``, ``support_logprob_kl`` (and their autograd
@@ -97,12 +98,14 @@ def lib() -> ctypes.CDLL:
         L.lmhead_logprob.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
         L.lmhead_support_logprob_kl.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.lmhead_loss_bwd.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.lmhead_loss_bwd_accumulate.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                 vp, vp, sz, vp]
         L.lmhead_status_string.argtypes = [i32]
         L.lmhead_status_string.restype = ctypes.c_char_p
         L.lmhead_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32),
                                                ctypes.POINTER(ctypes.c_int64)]
         for f in (L.lmhead_loss_fwd, L.lmhead_logprob, L.lmhead_support_logprob_kl,
-                  L.lmhead_loss_bwd, L.lmhead_read_device_error):
+                  L.lmhead_loss_bwd, L.lmhead_loss_bwd_accumulate, L.lmhead_read_device_error):
             f.restype = i32
         _lib = L
     return _lib
@@ -152,6 +155,15 @@ def lmhead_loss_bwd(p, entry, H, W, targets_or_ids, ref_logq, lse, saved_lp, gra
     return lib().lmhead_loss_bwd(ctypes.byref(p), entry, _p(H), _p(W), _p(targets_or_ids),
                                  _p(ref_logq), _p(lse), _p(saved_lp), _p(grad), _p(grad_kl), _p(dH),
                                  _p(dW), _p(workspace), workspace_bytes, _stream(stream))
+
+
+def lmhead_loss_bwd_accumulate(p, entry, H, W, targets_or_ids, ref_logq, lse, saved_lp, grad,
+                               grad_kl, dH_acc, dW_acc, dH, dW, workspace, workspace_bytes,
+                               stream=None) -> int:
+    return lib().lmhead_loss_bwd_accumulate(ctypes.byref(p), entry, _p(H), _p(W), _p(targets_or_ids),
+                                            _p(ref_logq), _p(lse), _p(saved_lp), _p(grad),
+                                            _p(grad_kl), _p(dH_acc), _p(dW_acc), _p(dH), _p(dW),
+                                            _p(workspace), workspace_bytes, _stream(stream))
 
 
 def lmhead_status_string(status: int) -> str:
@@ -277,6 +289,39 @@ def backward(entry: int, H, W, idx, lse, grad, chunk: int, *, ref_logq=None, sav
                         dH if need_dH else None, dW if need_dW else None, ws, ws.numel()),
         "lmhead_loss_bwd")
     return (dH if need_dH else None), (dW if need_dW else None)
+
+
+def _check_acc(name, t, shape, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or t.device != device:
+        raise ValueError(f"{name} must be a tensor on the inputs' device")
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)}")
+
+
+def backward_accumulate(entry: int, H, W, idx, lse, grad, chunk: int, *, dH_acc=None, dW_acc=None,
+                        ref_logq=None, saved_lp=None, grad_kl=None, num_valid: int = -1,
+                        out_bf16: bool = False, ws: Optional[torch.Tensor] = None,
+                        temperature: float = 0.0, row_temperature=None):
+    """dH_acc += dL/dH and dW_acc += dL/dW in fp32 (either may be None).
+    Returns (dH, dW): the bf16 casts of the updated accumulators when out_bf16,
+    else (None, None)."""
+    _check_inputs(H, W, idx)
+    _check_row_temperature(row_temperature, H.shape[0])
+    _check_acc("dH_acc", dH_acc, H.shape, H.device)
+    _check_acc("dW_acc", dW_acc, W.shape, H.device)
+    k = idx.shape[1] if entry == ENTRY_SUPPORT else 1
+    p = problem(H.shape[0], H.shape[1], W.shape[0], chunk, num_valid, k,
+                temperature=temperature, row_temperature=row_temperature)
+    if ws is None:
+        ws = workspace(p, entry, True, H.device)
+    dH = torch.empty_like(H) if (out_bf16 and dH_acc is not None) else None
+    dW = torch.empty_like(W) if (out_bf16 and dW_acc is not None) else None
+    _ok(lmhead_loss_bwd_accumulate(p, entry, H, W, idx, ref_logq, lse, saved_lp, grad, grad_kl,
+                                   dH_acc, dW_acc, dH, dW, ws, ws.numel()),
+        "lmhead_loss_bwd_accumulate")
+    return dH, dW
 
 
 # --------------------------------------------------------------- autograd

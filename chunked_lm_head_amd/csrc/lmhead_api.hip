@@ -187,6 +187,145 @@ int forward(const lmhead_problem* p, int entry, const void* H, const void* W, co
     return launched();
 }
 
+// The backward of both entry points. dH_acc / dW_acc: the caller's fp32
+// accumulators (null for the plain backward, where dH / dW are the results).
+int backward(const lmhead_problem* p, int entry, const void* H, const void* W, const int32_t* ids,
+             const float* ref_logq, const float* lse, const float* saved_lp, const float* grad,
+             const float* grad_kl, void* dH, void* dW, float* dH_acc, float* dW_acc, void* workspace,
+             size_t workspace_bytes, void* stream) {
+    int st = validate_problem(p, entry);
+    if (st != LMHEAD_OK) return st;
+    const bool support = entry == LMHEAD_ENTRY_SUPPORT;
+    if (workspace == nullptr) return LMHEAD_ERR_ARG;
+    if (p->n > 0) {
+        if (H == nullptr || W == nullptr || ids == nullptr || lse == nullptr) return LMHEAD_ERR_ARG;
+        if (!support && grad == nullptr) return LMHEAD_ERR_ARG;
+        if (support && grad_kl != nullptr && (ref_logq == nullptr || saved_lp == nullptr))
+            return LMHEAD_ERR_ARG;
+    }
+    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16) ||
+        !aligned(dH_acc, 16) || !aligned(dW_acc, 16) || !aligned(workspace, 256) ||
+        !aligned(p->row_temperature, 4))
+        return LMHEAD_ERR_ALIGN;
+    const Layout L = plan(*p, entry);
+    if (workspace_bytes < L.bwd_total) return LMHEAD_ERR_WORKSPACE;
+    const Temperature T = temperature_of(*p);
+    st = check_device();
+    if (st != LMHEAD_OK) return st;
+    const bool want_dh = dH != nullptr || dH_acc != nullptr;
+    const bool want_dw = dW != nullptr || dW_acc != nullptr;
+    if (!want_dh && !want_dw) return LMHEAD_OK;
+
+    hipStream_t s = (hipStream_t)stream;
+    char* w = (char*)workspace;
+    int32_t* hdr = (int32_t*)(w + L.hdr);
+    init_header_kernel<<<1, 64, 0, s>>>(hdr);
+    if (L.n == 0) {
+        // dL/dW = 0: the plain result is zero, an accumulator is unchanged
+        if (dW != nullptr && dW_acc == nullptr) fill_u32(dW, L.vocab * L.hidden / 2, 0u, s);
+        if (dW != nullptr && dW_acc != nullptr)
+            f32_to_bf16_kernel<<<grid_1d(L.vocab * L.hidden / 2, kThreads, 4096), kThreads, 0, s>>>(
+                dW_acc, L.vocab * L.hidden, (bf16_bits*)dW);
+        return launched();
+    }
+    scan_labels_kernel<<<grid_1d(L.n, kThreads, 1024), kThreads, 0, s>>>(ids, L.n, (int)L.k, L.vocab,
+                                                                          support ? 1 : 0, T, hdr);
+    CoeffArgs ca;
+    ca.T = T;
+    ca.entry = entry;
+    ca.n = L.n;
+    ca.n_pad = L.n_pad;
+    ca.vocab = L.vocab;
+    ca.k = (int)L.k;
+    ca.ids = ids;
+    ca.ref_logq = ref_logq;
+    ca.saved_lp = saved_lp;
+    ca.grad = grad;
+    ca.grad_kl = (support && ref_logq != nullptr && saved_lp != nullptr) ? grad_kl : nullptr;
+    ca.hdr = hdr;
+    ca.num_valid = p->num_valid;
+    ca.coef_a = (float*)(w + L.coef_a);
+    ca.coef_c = (float*)(w + L.coef_c);
+    coeffs_kernel<<<grid_1d(L.n_pad, kThreads, INT_MAX), kThreads, 0, s>>>(ca);
+
+    bf16_bits* Ht = (bf16_bits*)(w + L.Ht);
+    bf16_bits* G = (bf16_bits*)(w + L.G);
+    bf16_bits* Gt = (bf16_bits*)(w + L.Gt);
+    bf16_bits* Wt = (bf16_bits*)(w + L.Wt);
+    if (want_dw) {
+        dim3 grid((unsigned)(L.hidden / 64), (unsigned)(L.n_pad / 64));
+        transpose_kernel<<<grid, kThreads, 0, s>>>((const bf16_bits*)H, L.hidden, L.n, L.hidden, Ht,
+                                                   L.n_pad);
+    }
+    const int64_t nchunks = cdiv(L.vocab, L.chunk);
+    const int64_t tiles_rows = L.n_pad / kTile;
+    const int64_t tiles_hidden = cdiv(L.hidden, kTile);
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const int64_t v0 = c * L.chunk;
+        const int64_t width = (L.vocab - v0) < L.chunk ? (L.vocab - v0) : L.chunk;
+        const int64_t w_pad = round_up(width, kTile);
+        const bf16_bits* Wc = (const bf16_bits*)W + v0 * L.hidden;
+
+        LogitGradArgs ga;
+        ga.T = T;
+        ga.H = (const bf16_bits*)H;
+        ga.Wc = Wc;
+        ga.n = L.n;
+        ga.n_pad = L.n_pad;
+        ga.hidden = L.hidden;
+        ga.v0 = v0;
+        ga.width = width;
+        ga.w_pad = w_pad;
+        ga.tiles_m = tiles_rows;
+        ga.tiles_n = w_pad / kTile;
+        ga.coef_a = ca.coef_a;
+        ga.coef_c = ca.coef_c;
+        ga.ids = ids;
+        ga.k = (int)L.k;
+        ga.lse = lse;
+        ga.G = want_dh ? G : nullptr;
+        ga.Gt = want_dw ? Gt : nullptr;
+        bwd_logit_grad_kernel<<<(unsigned)(ga.tiles_m * ga.tiles_n), kThreads, 0, s>>>(ga);
+
+        if (want_dw) {
+            DwArgs da;
+            da.Gt = Gt;
+            da.Ht = Ht;
+            da.n_pad = L.n_pad;
+            da.hidden = L.hidden;
+            da.v0 = v0;
+            da.width = width;
+            da.w_pad = w_pad;
+            da.tiles_m = w_pad / kTile;
+            da.tiles_n = tiles_hidden;
+            da.dW = (bf16_bits*)dW;
+            da.dw_acc = dW_acc;
+            bwd_dw_kernel<<<(unsigned)(da.tiles_m * da.tiles_n), kThreads, 0, s>>>(da);
+        }
+        if (want_dh) {
+            dim3 grid((unsigned)(L.hidden / 64), (unsigned)(w_pad / 64));
+            transpose_kernel<<<grid, kThreads, 0, s>>>(Wc, L.hidden, width, L.hidden, Wt, w_pad);
+            DhArgs ha;
+            ha.G = G;
+            ha.Wt = Wt;
+            ha.n = L.n;
+            ha.n_pad = L.n_pad;
+            ha.hidden = L.hidden;
+            ha.w_pad = w_pad;
+            ha.tiles_m = tiles_rows;
+            ha.tiles_n = tiles_hidden;
+            ha.first = c == 0 && dH_acc == nullptr;
+            ha.last = c == nchunks - 1;
+            ha.keep_acc = dH_acc != nullptr;
+            ha.dh_acc = dH_acc != nullptr ? dH_acc : (float*)(w + L.dh_acc);
+            ha.dH = (bf16_bits*)dH;
+            bwd_dh_kernel<<<(unsigned)(ha.tiles_m * ha.tiles_n), kThreads, 0, s>>>(ha);
+        }
+    }
+    return launched();
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -218,131 +357,25 @@ int lmhead_support_logprob_kl(const lmhead_problem* p, const void* H, const void
                    workspace_bytes, stream);
 }
 
+
 int lmhead_loss_bwd(const lmhead_problem* p, int entry, const void* H, const void* W,
                     const int32_t* ids, const float* ref_logq, const float* lse,
                     const float* saved_lp, const float* grad, const float* grad_kl, void* dH,
                     void* dW, void* workspace, size_t workspace_bytes, void* stream) {
-    int st = validate_problem(p, entry);
-    if (st != LMHEAD_OK) return st;
-    const bool support = entry == LMHEAD_ENTRY_SUPPORT;
-    if (workspace == nullptr) return LMHEAD_ERR_ARG;
-    if (p->n > 0) {
-        if (H == nullptr || W == nullptr || ids == nullptr || lse == nullptr) return LMHEAD_ERR_ARG;
-        if (!support && grad == nullptr) return LMHEAD_ERR_ARG;
-        if (support && grad_kl != nullptr && (ref_logq == nullptr || saved_lp == nullptr))
-            return LMHEAD_ERR_ARG;
-    }
-    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16) ||
-        !aligned(workspace, 256) || !aligned(p->row_temperature, 4))
-        return LMHEAD_ERR_ALIGN;
-    const Layout L = plan(*p, entry);
-    if (workspace_bytes < L.bwd_total) return LMHEAD_ERR_WORKSPACE;
-    const Temperature T = temperature_of(*p);
-    st = check_device();
-    if (st != LMHEAD_OK) return st;
-    if (dH == nullptr && dW == nullptr) return LMHEAD_OK;
+    return backward(p, entry, H, W, ids, ref_logq, lse, saved_lp, grad, grad_kl, dH, dW, nullptr,
+                    nullptr, workspace, workspace_bytes, stream);
+}
 
-    hipStream_t s = (hipStream_t)stream;
-    char* w = (char*)workspace;
-    int32_t* hdr = (int32_t*)(w + L.hdr);
-    init_header_kernel<<<1, 64, 0, s>>>(hdr);
-    if (L.n == 0) {
-        if (dW != nullptr) fill_u32(dW, L.vocab * L.hidden / 2, 0u, s);
-        return launched();
-    }
-    scan_labels_kernel<<<grid_1d(L.n, kThreads, 1024), kThreads, 0, s>>>(ids, L.n, (int)L.k, L.vocab,
-                                                                          support ? 1 : 0, T, hdr);
-    CoeffArgs ca;
-    ca.T = T;
-    ca.entry = entry;
-    ca.n = L.n;
-    ca.n_pad = L.n_pad;
-    ca.vocab = L.vocab;
-    ca.k = (int)L.k;
-    ca.ids = ids;
-    ca.ref_logq = ref_logq;
-    ca.saved_lp = saved_lp;
-    ca.grad = grad;
-    ca.grad_kl = (support && ref_logq != nullptr && saved_lp != nullptr) ? grad_kl : nullptr;
-    ca.hdr = hdr;
-    ca.num_valid = p->num_valid;
-    ca.coef_a = (float*)(w + L.coef_a);
-    ca.coef_c = (float*)(w + L.coef_c);
-    coeffs_kernel<<<grid_1d(L.n_pad, kThreads, INT_MAX), kThreads, 0, s>>>(ca);
-
-    bf16_bits* Ht = (bf16_bits*)(w + L.Ht);
-    bf16_bits* G = (bf16_bits*)(w + L.G);
-    bf16_bits* Gt = (bf16_bits*)(w + L.Gt);
-    bf16_bits* Wt = (bf16_bits*)(w + L.Wt);
-    if (dW != nullptr) {
-        dim3 grid((unsigned)(L.hidden / 64), (unsigned)(L.n_pad / 64));
-        transpose_kernel<<<grid, kThreads, 0, s>>>((const bf16_bits*)H, L.hidden, L.n, L.hidden, Ht,
-                                                   L.n_pad);
-    }
-    const int64_t nchunks = cdiv(L.vocab, L.chunk);
-    const int64_t tiles_rows = L.n_pad / kTile;
-    const int64_t tiles_hidden = cdiv(L.hidden, kTile);
-    for (int64_t c = 0; c < nchunks; ++c) {
-        const int64_t v0 = c * L.chunk;
-        const int64_t width = (L.vocab - v0) < L.chunk ? (L.vocab - v0) : L.chunk;
-        const int64_t w_pad = round_up(width, kTile);
-        const bf16_bits* Wc = (const bf16_bits*)W + v0 * L.hidden;
-
-        LogitGradArgs ga;
-        ga.T = T;
-        ga.H = (const bf16_bits*)H;
-        ga.Wc = Wc;
-        ga.n = L.n;
-        ga.n_pad = L.n_pad;
-        ga.hidden = L.hidden;
-        ga.v0 = v0;
-        ga.width = width;
-        ga.w_pad = w_pad;
-        ga.tiles_m = tiles_rows;
-        ga.tiles_n = w_pad / kTile;
-        ga.coef_a = ca.coef_a;
-        ga.coef_c = ca.coef_c;
-        ga.ids = ids;
-        ga.k = (int)L.k;
-        ga.lse = lse;
-        ga.G = dH != nullptr ? G : nullptr;
-        ga.Gt = dW != nullptr ? Gt : nullptr;
-        bwd_logit_grad_kernel<<<(unsigned)(ga.tiles_m * ga.tiles_n), kThreads, 0, s>>>(ga);
-
-        if (dW != nullptr) {
-            DwArgs da;
-            da.Gt = Gt;
-            da.Ht = Ht;
-            da.n_pad = L.n_pad;
-            da.hidden = L.hidden;
-            da.v0 = v0;
-            da.width = width;
-            da.w_pad = w_pad;
-            da.tiles_m = w_pad / kTile;
-            da.tiles_n = tiles_hidden;
-            da.dW = (bf16_bits*)dW;
-            bwd_dw_kernel<<<(unsigned)(da.tiles_m * da.tiles_n), kThreads, 0, s>>>(da);
-        }
-        if (dH != nullptr) {
-            dim3 grid((unsigned)(L.hidden / 64), (unsigned)(w_pad / 64));
-            transpose_kernel<<<grid, kThreads, 0, s>>>(Wc, L.hidden, width, L.hidden, Wt, w_pad);
-            DhArgs ha;
-            ha.G = G;
-            ha.Wt = Wt;
-            ha.n = L.n;
-            ha.n_pad = L.n_pad;
-            ha.hidden = L.hidden;
-            ha.w_pad = w_pad;
-            ha.tiles_m = tiles_rows;
-            ha.tiles_n = tiles_hidden;
-            ha.first = c == 0;
-            ha.last = c == nchunks - 1;
-            ha.dh_acc = (float*)(w + L.dh_acc);
-            ha.dH = (bf16_bits*)dH;
-            bwd_dh_kernel<<<(unsigned)(ha.tiles_m * ha.tiles_n), kThreads, 0, s>>>(ha);
-        }
-    }
-    return launched();
+int lmhead_loss_bwd_accumulate(const lmhead_problem* p, int entry, const void* H, const void* W,
+                               const int32_t* ids, const float* ref_logq, const float* lse,
+                               const float* saved_lp, const float* grad, const float* grad_kl,
+                               float* dH_acc, float* dW_acc, void* dH, void* dW, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    // a bf16 output is the cast of its accumulator, so it needs one
+    if ((dH != nullptr && dH_acc == nullptr) || (dW != nullptr && dW_acc == nullptr))
+        return LMHEAD_ERR_ARG;
+    return backward(p, entry, H, W, ids, ref_logq, lse, saved_lp, grad, grad_kl, dH, dW, dH_acc,
+                    dW_acc, workspace, workspace_bytes, stream);
 }
 
 const char* lmhead_status_string(int status) {

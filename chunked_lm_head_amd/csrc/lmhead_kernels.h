@@ -99,7 +99,8 @@ struct DwArgs {
     const bf16_bits* Ht;   // [hidden, n_pad]
     int64_t n_pad, hidden, v0, width, w_pad;
     int64_t tiles_m, tiles_n;
-    bf16_bits* dW;         // [vocab, hidden]
+    bf16_bits* dW;         // [vocab, hidden] or null
+    float* dw_acc;         // caller's fp32 [vocab, hidden] (+=) or null
 };
 
 struct DhArgs {
@@ -107,9 +108,11 @@ struct DhArgs {
     const bf16_bits* Wt;   // [hidden, w_pad]
     int64_t n, n_pad, hidden, w_pad;
     int64_t tiles_m, tiles_n;
-    int first, last;
+    int first;             // chunk 0 of a fresh sum: dh_acc is written, not read
+    int last;              // last chunk: the bf16 dH is written (if dH is set)
+    int keep_acc;          // the last chunk also stores the fp32 sum (caller's accumulator)
     float* dh_acc;         // [n, hidden]
-    bf16_bits* dH;         // [n, hidden]
+    bf16_bits* dH;         // [n, hidden] or null
 };
 
 __global__ void init_header_kernel(int32_t* hdr);
@@ -124,6 +127,7 @@ __global__ void coeffs_kernel(CoeffArgs a);
 __global__ void bwd_logit_grad_kernel(LogitGradArgs a);
 __global__ void bwd_dw_kernel(DwArgs a);
 __global__ void bwd_dh_kernel(DhArgs a);
+__global__ void f32_to_bf16_kernel(const float* in, int64_t count, bf16_bits* out);
 __global__ void transpose_kernel(const bf16_bits* in, int64_t ld_in, int64_t rows, int64_t cols,
                                  bf16_bits* out, int64_t rows_pad);
 

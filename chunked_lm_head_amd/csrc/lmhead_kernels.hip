@@ -401,6 +401,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
 
 // dW rows of one chunk: dW[v0 + i, h] = sum_n G^T[i, n] H^T[h, n], a single
 // K-loop over every row n in ascending order; bf16 store of the fp32 sum.
+// With a caller accumulator the fp32 sum is first added to it (dw_acc +=),
+// and the bf16 output, if any, is the cast of the updated accumulator.
 __global__ __launch_bounds__(kThreads, 1) void bwd_dw_kernel(DwArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
     int64_t tm, tn;
@@ -419,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dw_kernel(DwArgs a) {
         if (wc == half) stage_half(S, acc, wr, lane);
         __syncthreads();
         const int64_t h0 = n0 + half * 128;
-        if (v < a.width) {
+        if (v < a.width && a.dw_acc == nullptr) {
             bf16_bits* out = a.dW + (a.v0 + v) * a.hidden + h0;
             for (int c8 = 0; c8 < 16; ++c8) {
                 if (h0 + c8 * 8 >= a.hidden) break;
@@ -429,6 +431,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dw_kernel(DwArgs a) {
                     w[i] = pack_bf16x2(Sr[(c8 * 8 + 2 * i) * kEpiStride], Sr[(c8 * 8 + 2 * i + 1) * kEpiStride]);
                 *reinterpret_cast<uint4*>(out + c8 * 8) = make_uint4(w[0], w[1], w[2], w[3]);
             }
+        } else if (v < a.width) {
+            const int64_t o = (a.v0 + v) * a.hidden + h0;
+            for (int c4 = 0; c4 < 32; ++c4) {
+                if (h0 + c4 * 4 >= a.hidden) break;
+                const float4 p = *reinterpret_cast<const float4*>(a.dw_acc + o + c4 * 4);
+                float4 x;
+                x.x = p.x + Sr[(c4 * 4 + 0) * kEpiStride];
+                x.y = p.y + Sr[(c4 * 4 + 1) * kEpiStride];
+                x.z = p.z + Sr[(c4 * 4 + 2) * kEpiStride];
+                x.w = p.w + Sr[(c4 * 4 + 3) * kEpiStride];
+                *reinterpret_cast<float4*>(a.dw_acc + o + c4 * 4) = x;
+                if (a.dW != nullptr)
+                    *reinterpret_cast<uint2*>(a.dW + o + c4 * 4) =
+                        make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
+            }
         }
         __syncthreads();
     }
@@ -436,7 +453,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dw_kernel(DwArgs a) {
 
 // dH contribution of one chunk: acc = sum_j G[n, j] W_c^T[h, j] over the
 // chunk's columns; the fp32 running sum over chunks (chunk order) lives in
-// dh_acc and the last chunk writes the bf16 result.
+// dh_acc and the last chunk writes the bf16 result. A caller accumulator is
+// dh_acc itself: read from chunk 0 on and stored after the last chunk too.
 __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(DhArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
     int64_t tm, tn;
@@ -468,16 +486,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(DhArgs a) {
                     v.z = p.z + v.z;
                     v.w = p.w + v.w;
                 }
-                if (a.last) {
+                if (a.last && a.dH != nullptr) {
                     const uint32_t lo = pack_bf16x2(v.x, v.y);
                     const uint32_t hi = pack_bf16x2(v.z, v.w);
                     *reinterpret_cast<uint2*>(a.dH + o + c4 * 4) = make_uint2(lo, hi);
-                } else {
-                    *reinterpret_cast<float4*>(a.dh_acc + o + c4 * 4) = v;
                 }
+                if (!a.last || a.keep_acc) *reinterpret_cast<float4*>(a.dh_acc + o + c4 * 4) = v;
             }
         }
         __syncthreads();
+    }
+}
+
+// out[i] = bf16 (round to nearest even) of in[i]; count is a multiple of 2.
+__global__ void f32_to_bf16_kernel(const float* in, int64_t count, bf16_bits* out) {
+    for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 2; i < count;
+         i += (int64_t)gridDim.x * blockDim.x * 2) {
+        const float2 v = *reinterpret_cast<const float2*>(in + i);
+        *reinterpret_cast<uint32_t*>(out + i) = pack_bf16x2(v.x, v.y);
     }
 }
 

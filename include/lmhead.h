@@ -218,6 +218,35 @@ int lmhead_loss_bwd(const lmhead_problem* p, int entry,
                     void* dH, void* dW,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Backward into caller-owned FP32 accumulators: the same computation as
+ * lmhead_loss_bwd, but dL/dH and dL/dW (before any bf16 rounding) are added
+ * to dH_acc and dW_acc, so that gradients of several calls (micro-batches,
+ * or several losses of one batch) are summed in FP32 ("initial accumulation
+ * buffers" are part of the determinism contract, [PR8059]; FP32 dx / dw
+ * accumulators plus BF16 outputs, [PR8059-review]; dW as the BF16 cast of
+ * the FP32 accumulator, [PR14-tests]). For a CE mean over several
+ * micro-batches, pass the global valid-row count as p->num_valid.
+ *   dH_acc   device, fp32 [n, hidden] or NULL: dH_acc += dL/dH. Within a
+ *            call the chunks are added in ascending order, starting from the
+ *            caller's values.
+ *   dW_acc   device, fp32 [vocab, hidden] or NULL: dW_acc += dL/dW (each
+ *            element gets one fp32 sum over the rows, then one addition).
+ *   dH, dW   device, bf16, or NULL: the RNE bf16 cast of the updated
+ *            accumulator. Each needs its accumulator (else LMHEAD_ERR_ARG).
+ *   The other arguments are those of lmhead_loss_bwd. NULL accumulators
+ *   (frozen H / W) skip that side; with n = 0 the accumulators are unchanged
+ *   and dH / dW receive their casts. Bits depend on the accumulators'
+ *   initial values as well as on the inputs. With zero-initialised
+ *   accumulators, dH and dW equal lmhead_loss_bwd's outputs bit for bit.
+ */
+int lmhead_loss_bwd_accumulate(const lmhead_problem* p, int entry,
+                               const void* H, const void* W, const int32_t* targets_or_ids,
+                               const float* ref_logq, const float* lse, const float* saved_lp,
+                               const float* grad, const float* grad_kl,
+                               float* dH_acc, float* dW_acc, void* dH, void* dW,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable text for a status code. */
 const char* lmhead_status_string(int status);
 

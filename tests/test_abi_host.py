@@ -30,7 +30,8 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
     assert names == sorted([
-        "lmhead_loss_bwd", "lmhead_loss_fwd", "lmhead_logprob", "lmhead_read_device_error",
+        "lmhead_loss_bwd", "lmhead_loss_bwd_accumulate", "lmhead_loss_fwd", "lmhead_logprob",
+        "lmhead_read_device_error",
         "lmhead_status_string", "lmhead_support_logprob_kl", "lmhead_workspace_size"])
     L = ctypes.CDLL(lm.LIB_PATH)
     for name in names:
@@ -109,6 +110,22 @@ def test_host_errors_precede_device_use():
         == lm.LMHEAD_ERR_WORKSPACE
     assert b(p, 9, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, BIG, 0) \
         == lm.LMHEAD_ERR_ARG
+
+
+def test_accumulate_host_checks():
+    p = _p()
+    a = lm.lmhead_loss_bwd_accumulate
+    # a bf16 output needs its accumulator
+    assert a(p, 0, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, None, None, FAKE, FAKE, None, FAKE, BIG, 0) \
+        == lm.LMHEAD_ERR_ARG
+    assert a(p, 0, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None, None, FAKE, FAKE, BIG, 0) \
+        == lm.LMHEAD_ERR_ARG
+    assert a(p, 0, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE + 8, FAKE, None, None, FAKE,
+             BIG, 0) == lm.LMHEAD_ERR_ALIGN
+    assert a(p, 0, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, None, None, FAKE,
+             4096, 0) == lm.LMHEAD_ERR_WORKSPACE
+    assert a(p, 0, FAKE, FAKE, FAKE, None, None, None, FAKE, None, FAKE, FAKE, None, None, FAKE,
+             BIG, 0) == lm.LMHEAD_ERR_ARG   # lse missing
 
 
 def test_temperature_host_checks():
