@@ -10,7 +10,8 @@ Two layers:
 
 * ``lmhead_workspace_size``, ``lmhead_loss_fwd``, ``lmhead_logprob``,
   ``lmhead_support_logprob_kl``, ``lmhead_loss_bwd``,
-  ``lmhead_loss_bwd_accumulate``, ``lmhead_status_string``,
+  ``lmhead_loss_bwd_accumulate``, ``lmhead_memory_report``,
+  ``lmhead_plan_chunk``, ``lmhead_status_string``,
   ``lmhead_read_device_error``: the C entry points
   under the same names. Pointer arguments accept a torch tensor, an integer
   address or None; the return value is the C status code.
@@ -72,6 +73,20 @@ def problem(n: int, hidden: int, vocab: int, chunk: int, num_valid: int = -1, k:
                           _p(row_temperature))
 
 
+class lmhead_memory_figures(ctypes.Structure):
+    _fields_ = [
+        ("chunk", ctypes.c_int64),
+        ("chunks", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("forward_bytes", ctypes.c_size_t),
+        ("partials_bytes", ctypes.c_size_t),
+        ("dz_chunk_bytes", ctypes.c_size_t),
+        ("operand_copy_bytes", ctypes.c_size_t),
+        ("dh_acc_bytes", ctypes.c_size_t),
+        ("caller_output_bytes", ctypes.c_size_t),
+    ]
+
+
 class LMHeadError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -100,12 +115,15 @@ def lib() -> ctypes.CDLL:
         L.lmhead_loss_bwd.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.lmhead_loss_bwd_accumulate.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                  vp, vp, sz, vp]
+        L.lmhead_memory_report.argtypes = [P, i32, i32, ctypes.POINTER(lmhead_memory_figures)]
+        L.lmhead_plan_chunk.argtypes = [P, i32, sz, ctypes.POINTER(ctypes.c_int64)]
         L.lmhead_status_string.argtypes = [i32]
         L.lmhead_status_string.restype = ctypes.c_char_p
         L.lmhead_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32),
                                                ctypes.POINTER(ctypes.c_int64)]
         for f in (L.lmhead_loss_fwd, L.lmhead_logprob, L.lmhead_support_logprob_kl,
-                  L.lmhead_loss_bwd, L.lmhead_loss_bwd_accumulate, L.lmhead_read_device_error):
+                  L.lmhead_loss_bwd, L.lmhead_loss_bwd_accumulate, L.lmhead_read_device_error,
+                  L.lmhead_memory_report, L.lmhead_plan_chunk):
             f.restype = i32
         _lib = L
     return _lib
@@ -131,6 +149,34 @@ def _stream(stream) -> Optional[int]:
 
 def lmhead_workspace_size(p: lmhead_problem, entry: int, with_backward: int) -> int:
     return int(lib().lmhead_workspace_size(ctypes.byref(p), entry, int(with_backward)))
+
+
+def lmhead_memory_report(p: lmhead_problem, entry: int, with_backward: int, out) -> int:
+    return lib().lmhead_memory_report(ctypes.byref(p), entry, int(with_backward), ctypes.byref(out))
+
+
+def lmhead_plan_chunk(p: lmhead_problem, entry: int, budget_bytes: int, chunk) -> int:
+    return lib().lmhead_plan_chunk(ctypes.byref(p), entry, int(budget_bytes), ctypes.byref(chunk))
+
+
+def memory_report(n: int, hidden: int, vocab: int, chunk: int, entry: int = ENTRY_CE_MEAN,
+                  with_backward: bool = True, k: int = 1) -> dict:
+    """Byte counts of one call: workspace and its parts, and the outputs the
+    caller allocates (lmhead_memory_report)."""
+    r = lmhead_memory_figures()
+    _ok(lmhead_memory_report(problem(n, hidden, vocab, chunk, -1, k), entry, with_backward, r),
+        "lmhead_memory_report")
+    return {name: int(getattr(r, name)) for name, _ in r._fields_}
+
+
+def plan_chunk(n: int, hidden: int, vocab: int, budget_bytes: int, entry: int = ENTRY_CE_MEAN,
+               k: int = 1) -> int:
+    """The backward chunk whose workspace fits the byte budget with the fewest
+    vocabulary passes (lmhead_plan_chunk)."""
+    c = ctypes.c_int64(0)
+    _ok(lmhead_plan_chunk(problem(n, hidden, vocab, 256, -1, k), entry, budget_bytes, c),
+        "lmhead_plan_chunk")
+    return int(c.value)
 
 
 def lmhead_loss_fwd(p, entry, H, W, targets, loss, lse, workspace, workspace_bytes, stream=None) -> int:
@@ -400,16 +446,27 @@ class ChunkedLMHeadSupport(torch.autograd.Function):
         return dH, dW, None, None, None, None, None
 
 
+def _chunk(chunk, memory_budget, H, W, entry, k=1):
+    """The given chunk, or the planned one when a workspace byte budget is given."""
+    if memory_budget is None:
+        return chunk
+    return plan_chunk(H.shape[0], H.shape[1], W.shape[0], memory_budget, entry, k)
+
+
 def ce_loss(H, W, targets, chunk: int = 8192, reduction: str = "mean", num_valid: int = -1,
-            temperature: float = 0.0, row_temperature=None):
+            temperature: float = 0.0, row_temperature=None, memory_budget: Optional[int] = None):
+    chunk = _chunk(chunk, memory_budget, H, W, ENTRY_CE_MEAN)
     return ChunkedLMHeadCE.apply(H, W, targets, chunk, reduction, num_valid, temperature,
                                  row_temperature)
 
 
-def logprob(H, W, targets, chunk: int = 8192, temperature: float = 0.0, row_temperature=None):
+def logprob(H, W, targets, chunk: int = 8192, temperature: float = 0.0, row_temperature=None,
+            memory_budget: Optional[int] = None):
+    chunk = _chunk(chunk, memory_budget, H, W, ENTRY_LOGPROB)
     return ChunkedLMHeadLogprob.apply(H, W, targets, chunk, temperature, row_temperature)
 
 
 def support_logprob_kl(H, W, ids, ref_logq, chunk: int = 8192, temperature: float = 0.0,
-                       row_temperature=None):
+                       row_temperature=None, memory_budget: Optional[int] = None):
+    chunk = _chunk(chunk, memory_budget, H, W, ENTRY_SUPPORT, ids.shape[1])
     return ChunkedLMHeadSupport.apply(H, W, ids, ref_logq, chunk, temperature, row_temperature)

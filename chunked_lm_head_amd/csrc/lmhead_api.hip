@@ -336,6 +336,57 @@ size_t lmhead_workspace_size(const lmhead_problem* p, int entry, int with_backwa
     return with_backward ? L.bwd_total : L.fwd_total;
 }
 
+int lmhead_memory_report(const lmhead_problem* p, int entry, int with_backward,
+                         lmhead_memory_figures* out) {
+    if (out == nullptr) return LMHEAD_ERR_ARG;
+    const int st = validate_problem(p, entry);
+    if (st != LMHEAD_OK) return st;
+    const Layout L = plan(*p, entry);
+    lmhead_memory_figures r{};
+    r.chunk = L.chunk;
+    r.chunks = cdiv(L.vocab, L.chunk);
+    r.workspace_bytes = with_backward ? L.bwd_total : L.fwd_total;
+    r.forward_bytes = L.fwd_total;
+    r.partials_bytes = (size_t)(8 * L.tiles_v * L.n);
+    if (with_backward) {
+        r.dz_chunk_bytes = (size_t)(4 * L.n_pad * L.w_pad);
+        r.operand_copy_bytes = (size_t)(2 * L.hidden * L.n_pad + 2 * L.hidden * L.w_pad);
+        r.dh_acc_bytes = (size_t)(4 * L.n * L.hidden);
+    }
+    // fp32 outputs: lse [n] plus loss [1] / logp [n] / lp [n, k] and kl [n]
+    size_t outs = (size_t)(4 * L.n);
+    if (entry == LMHEAD_ENTRY_CE_MEAN || entry == LMHEAD_ENTRY_CE_SUM) outs += 4;
+    else if (entry == LMHEAD_ENTRY_LOGPROB) outs += (size_t)(4 * L.n);
+    else outs += (size_t)(4 * L.n * L.k + 4 * L.n);
+    if (with_backward) outs += (size_t)(2 * L.n * L.hidden + 2 * L.vocab * L.hidden);
+    r.caller_output_bytes = outs;
+    *out = r;
+    return LMHEAD_OK;
+}
+
+int lmhead_plan_chunk(const lmhead_problem* p, int entry, size_t budget_bytes, int64_t* chunk) {
+    if (p == nullptr || chunk == nullptr) return LMHEAD_ERR_ARG;
+    lmhead_problem q = *p;
+    q.chunk = 256;
+    const int st = validate_problem(&q, entry);
+    if (st != LMHEAD_OK) return st;
+    auto fits = [&](int64_t c) {
+        q.chunk = c;
+        return plan(q, entry).bwd_total <= budget_bytes;
+    };
+    if (!fits(256)) return LMHEAD_ERR_WORKSPACE;
+    // largest fitting chunk (the workspace grows with the chunk), by bisection over multiples of 256
+    int64_t lo = 1, hi = cdiv(q.vocab, 256);
+    while (lo < hi) {
+        const int64_t mid = lo + (hi - lo + 1) / 2;
+        if (fits(mid * 256)) lo = mid;
+        else hi = mid - 1;
+    }
+    const int64_t passes = cdiv(q.vocab, lo * 256);
+    *chunk = round_up(cdiv(q.vocab, passes), 256);
+    return LMHEAD_OK;
+}
+
 int lmhead_loss_fwd(const lmhead_problem* p, int entry, const void* H, const void* W,
                     const int32_t* targets, float* loss, float* lse, void* workspace,
                     size_t workspace_bytes, void* stream) {

@@ -139,6 +139,40 @@ typedef struct lmhead_problem {
 size_t lmhead_workspace_size(const lmhead_problem* p, int entry, int with_backward);
 
 /*
+ * Memory report ("workspace reporting", "memory-budgeted backend options",
+ * [PR8059]; the memory of a multi-chunk plan, [PR8059-review]). Pure host
+ * function. Every figure is in bytes for the problem as given (its chunk).
+ */
+typedef struct lmhead_memory_figures {
+    int64_t chunk;               /* vocabulary chunk of the backward */
+    int64_t chunks;              /* number of chunks, ceil(vocab / chunk) */
+    size_t workspace_bytes;      /* = lmhead_workspace_size(p, entry, with_backward) */
+    size_t forward_bytes;        /* workspace the forward uses */
+    size_t partials_bytes;       /* forward: (max, sum-exp) per 256-column tile and row */
+    size_t dz_chunk_bytes;       /* backward: one chunk of dL/dz, bf16, row- and column-major */
+    size_t operand_copy_bytes;   /* backward: H^T and one chunk of W^T, bf16 */
+    size_t dh_acc_bytes;         /* backward: fp32 running sum of dH over the chunks */
+    size_t caller_output_bytes;  /* buffers the caller allocates: the entry's fp32 outputs
+                                    (loss / logp / lp, kl, lse), plus bf16 dH and dW
+                                    with the backward */
+} lmhead_memory_figures;
+
+/* Fills *out. Returns LMHEAD_ERR_ARG / LMHEAD_ERR_SHAPE for an invalid
+ * problem or entry (then *out is untouched). */
+int lmhead_memory_report(const lmhead_problem* p, int entry, int with_backward,
+                         lmhead_memory_figures* out);
+
+/*
+ * Memory-budgeted chunk planner ([PR8059]). Pure host function; p->chunk is
+ * ignored. Chooses the chunk for lmhead_loss_bwd whose workspace fits in
+ * `budget_bytes` with the fewest vocabulary chunks (the fewest passes) and,
+ * among those, the smallest chunk (a multiple of 256), which spreads the
+ * vocabulary evenly over the passes. Writes it to *chunk. Returns
+ * LMHEAD_ERR_WORKSPACE if even a 256-wide chunk does not fit.
+ */
+int lmhead_plan_chunk(const lmhead_problem* p, int entry, size_t budget_bytes, int64_t* chunk);
+
+/*
  * Cross-entropy forward ([PR8059]; ignore rule [PR14-op]).
  *   entry      LMHEAD_ENTRY_CE_MEAN or LMHEAD_ENTRY_CE_SUM.
  *   H          device, bf16 [n, hidden], row-major, 16-byte aligned.

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     names = _declared_functions()
     assert names == sorted([
         "lmhead_loss_bwd", "lmhead_loss_bwd_accumulate", "lmhead_loss_fwd", "lmhead_logprob",
-        "lmhead_read_device_error",
+        "lmhead_memory_report", "lmhead_plan_chunk", "lmhead_read_device_error",
         "lmhead_status_string", "lmhead_support_logprob_kl", "lmhead_workspace_size"])
     L = ctypes.CDLL(lm.LIB_PATH)
     for name in names:

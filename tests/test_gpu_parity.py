@@ -237,3 +237,23 @@ def test_mutation_gate_catches_two_percent():
         grad_check("dW x1.02", dW * 1.02, ref["dW"])
     with pytest.raises(AssertionError):
         rel_check("loss x1.02", [got["loss"].item() * 1.02], [ref["loss"]])
+
+
+def test_planned_chunk_against_oracle():
+    """A workspace budget that forces several small chunks: the planned chunk
+    runs, fits, and matches the oracle (the result does not depend on the plan
+    beyond rounding of the bf16 dL/dz operand)."""
+    inp = _ragged(0)
+    d = Dev(inp)
+    p = lm.problem(inp.wl.n, inp.wl.hidden, inp.wl.vocab, 256)
+    budget = lm.lmhead_workspace_size(p, 0, 1) + 1000   # fits 256, not 512
+    chunk = lm.plan_chunk(inp.wl.n, inp.wl.hidden, inp.wl.vocab, budget)
+    assert chunk == 256
+    H = d.H.clone().requires_grad_(True)
+    W = d.W.clone().requires_grad_(True)
+    loss = lm.ce_loss(H, W, d.t, memory_budget=budget)
+    loss.backward()
+    ref = _oracle(0, inp)
+    rel_check("loss", [loss.item()], [ref["loss"]])
+    grad_check("dH", bf16_to_np(H.grad), ref["dH"])
+    grad_check("dW", bf16_to_np(W.grad), ref["dW"])
