@@ -14,7 +14,8 @@ bf16 bytes the GPU receives (bf16 widens to fp64 exactly):
 * per-token log-probability ``z[n, t_n] - lse``;
 * support-set log-probabilities ``z[n, id_nk] - lse`` and
   ``KL(q_ref || p_hat)`` with ``p_hat`` the model renormalised over the K
-  listed candidates;
+  listed candidates, also as a KL-only entry and over padded candidate lists
+  (a negative id is a padding slot that takes no part);
 * backward: ``dZ = dL/dz`` from the textbook derivative of each entry, then
   ``dH = dZ W`` and ``dW = dZ^T H`` (C loops).
 
@@ -51,6 +52,7 @@ ENTRY_CE_MEAN = 0
 ENTRY_CE_SUM = 1
 ENTRY_LOGPROB = 2
 ENTRY_SUPPORT = 3
+ENTRY_SUPPORT_KL = 4
 
 _lib = None
 
@@ -151,11 +153,15 @@ def check_targets(t: np.ndarray, vocab: int) -> np.ndarray:
     return t >= 0
 
 
-def check_ids(ids: np.ndarray, vocab: int) -> None:
-    bad = np.argwhere((ids < 0) | (ids >= vocab))
+def check_ids(ids: np.ndarray, vocab: int, padded: bool = False) -> np.ndarray:
+    """Validates candidate ids; returns the mask of real (non-padding) slots.
+    With padded lists a negative id is a padding slot; otherwise every id must
+    lie in [0, vocab)."""
+    bad = np.argwhere((ids >= vocab) | ((ids < 0) & (not padded)))
     if bad.size:
         r, k = bad[0]
         raise ValueError(f"candidate id {int(ids[r, k])} outside [0, {vocab}) at row {int(r)}")
+    return ids >= 0
 
 
 def _gather(z: np.ndarray, t: np.ndarray, valid: np.ndarray) -> np.ndarray:
@@ -190,28 +196,47 @@ def logprob_forward(z: np.ndarray, t: np.ndarray):
     return dict(logp=np.where(valid, zt - lse, 0.0), lse=lse, valid=valid)
 
 
-def support_forward(z: np.ndarray, ids: np.ndarray, ref_logq: Optional[np.ndarray]):
+def support_forward(z: np.ndarray, ids: np.ndarray, ref_logq: Optional[np.ndarray],
+                    padded: bool = False):
     """Support-set log-probabilities and KL(q_ref || p_hat) over the K candidates.
 
     lp[n, k]      = z[n, id_nk] - lse[n]                  (full-vocabulary log-prob)
     log p_hat     = z[n, id_nk] - log sum_j exp z[n, id_nj] (renormalised over the K ids)
     KL[n]         = sum_k q_nk (ref_logq_nk - log p_hat_nk), q = exp(ref_logq), 0 where q = 0
+
+    Padded lists (negative id = padding slot): a padding slot has lp = 0 and
+    log p_hat = 0, and takes no part in the renormalisation or the KL sum; a
+    row with no real candidate has KL = 0.
     """
     vocab = z.shape[1]
     ids = np.asarray(ids, dtype=np.int64)
-    check_ids(ids, vocab)
+    real = check_ids(ids, vocab, padded)
     lse = logsumexp_rows(z)
-    zc = np.take_along_axis(z, ids, axis=1)
-    lp = zc - lse[:, None]
+    zc = np.take_along_axis(z, np.where(real, ids, 0), axis=1)
+    lp = np.where(real, zc - lse[:, None], 0.0)
     out = dict(lp=lp, lse=lse)
     if ref_logq is not None:
         r = np.asarray(ref_logq, dtype=np.float64)
-        log_phat = zc - logsumexp_rows(zc)[:, None]
+        log_phat = np.zeros_like(zc)
+        for n in range(zc.shape[0]):
+            sel = real[n]
+            if sel.any():
+                v = zc[n, sel]
+                m = v.max()
+                log_phat[n, sel] = v - (m + np.log(np.exp(v - m).sum()))
         q = np.exp(r)
-        terms = np.where(q > 0.0, q * (r - log_phat), 0.0)
+        terms = np.where(real & (q > 0.0), q * (r - log_phat), 0.0)
         out["kl"] = terms.sum(axis=1)
         out["log_phat"] = log_phat
     return out
+
+
+def support_kl_forward(z: np.ndarray, ids: np.ndarray, ref_logq: np.ndarray,
+                       padded: bool = False):
+    """KL-only support entry: KL(q_ref || p_hat) and log p_hat; neither depends
+    on logits outside the listed candidates."""
+    f = support_forward(z, ids, ref_logq, padded)
+    return dict(kl=f["kl"], log_phat=f["log_phat"])
 
 
 # ----------------------------------------------------------------- derivatives
@@ -249,30 +274,34 @@ def logprob_dz(z: np.ndarray, t: np.ndarray, grad: np.ndarray) -> np.ndarray:
 
 
 def support_dz(z: np.ndarray, ids: np.ndarray, ref_logq: Optional[np.ndarray],
-               grad: Optional[np.ndarray], grad_kl: Optional[np.ndarray]) -> np.ndarray:
+               grad: Optional[np.ndarray], grad_kl: Optional[np.ndarray],
+               padded: bool = False) -> np.ndarray:
     """d(sum grad * lp + sum grad_kl * KL)/dz.
 
     lp part:  sum_k g_nk ([v = id_nk] - p_nv)
     KL part:  b_n sum_k [v = id_nk] (Q_n p_hat_nk - q_nk),  Q_n = sum_k q_nk
+    Padding slots (padded lists) contribute nothing and are not in Q_n.
     """
     n, vocab = z.shape
     ids = np.asarray(ids, dtype=np.int64)
-    f = support_forward(z, ids, ref_logq)
+    f = support_forward(z, ids, ref_logq, padded)
+    real = ids >= 0
+    safe = np.where(real, ids, 0)
     dz = np.zeros_like(z)
     rows = np.arange(n)
     if grad is not None:
-        g = np.asarray(grad, dtype=np.float64)
+        g = np.where(real, np.asarray(grad, dtype=np.float64), 0.0)
         dz -= g.sum(axis=1)[:, None] * softmax_rows(z, f["lse"])
         for k in range(ids.shape[1]):
-            np.add.at(dz, (rows, ids[:, k]), g[:, k])
+            np.add.at(dz, (rows, safe[:, k]), g[:, k])
     if grad_kl is not None and ref_logq is not None:
         b = np.asarray(grad_kl, dtype=np.float64)
-        q = np.exp(np.asarray(ref_logq, dtype=np.float64))
+        q = np.where(real, np.exp(np.asarray(ref_logq, dtype=np.float64)), 0.0)
         Q = q.sum(axis=1)
-        phat = np.exp(f["log_phat"])
+        phat = np.where(real, np.exp(f["log_phat"]), 0.0)
         coef = b[:, None] * (Q[:, None] * phat - q)
         for k in range(ids.shape[1]):
-            np.add.at(dz, (rows, ids[:, k]), coef[:, k])
+            np.add.at(dz, (rows, safe[:, k]), coef[:, k])
     return dz
 
 
@@ -294,7 +323,8 @@ def temperature_scale(n: int, temperature: float = 0.0, row_temperature=None) ->
 
 def run(entry: int, H: np.ndarray, W: np.ndarray, *, targets=None, ids=None, ref_logq=None,
         grad=None, grad_kl=None, num_valid: int = -1, backward: bool = True,
-        temperature: float = 0.0, row_temperature=None, threads: int = 0) -> dict:
+        temperature: float = 0.0, row_temperature=None, padded: bool = False,
+        threads: int = 0) -> dict:
     """Full forward (+ backward) of one entry over every row. For small problems.
 
     With a temperature, every definition applies to z / tau_n, and the backward
@@ -315,12 +345,18 @@ def run(entry: int, H: np.ndarray, W: np.ndarray, *, targets=None, ids=None, ref
         if backward:
             dz = logprob_dz(z, targets, grad)
     elif entry == ENTRY_SUPPORT:
-        f = support_forward(z, ids, ref_logq)
+        f = support_forward(z, ids, ref_logq, padded)
         out.update(lp=f["lp"], lse=f["lse"])
         if "kl" in f:
             out["kl"] = f["kl"]
+            out["log_phat"] = f["log_phat"]
         if backward:
-            dz = support_dz(z, ids, ref_logq, grad, grad_kl)
+            dz = support_dz(z, ids, ref_logq, grad, grad_kl, padded)
+    elif entry == ENTRY_SUPPORT_KL:
+        f = support_kl_forward(z, ids, ref_logq, padded)
+        out.update(kl=f["kl"], log_phat=f["log_phat"])
+        if backward:
+            dz = support_dz(z, ids, ref_logq, None, grad_kl, padded)
     else:
         raise ValueError(f"unknown entry {entry}")
     if backward:
@@ -334,7 +370,7 @@ def run(entry: int, H: np.ndarray, W: np.ndarray, *, targets=None, ids=None, ref
 def rows_forward_backward(entry: int, H: np.ndarray, W: np.ndarray, rows, *, targets=None,
                           ids=None, ref_logq=None, grad=None, grad_kl=None,
                           count: Optional[int] = None, temperature: float = 0.0,
-                          row_temperature=None, threads: int = 0) -> dict:
+                          row_temperature=None, padded: bool = False, threads: int = 0) -> dict:
     """Forward values and dH for a sample of rows, each computed over the whole vocabulary.
 
     Rows are independent except through the CE mean's denominator, which the
@@ -361,13 +397,17 @@ def rows_forward_backward(entry: int, H: np.ndarray, W: np.ndarray, rows, *, tar
         out.update(lse=f["lse"], logp=f["logp"])
         dz = logprob_dz(z, t, np.asarray(grad)[rows])
     else:
-        f = support_forward(z, np.asarray(ids)[rows], None if ref_logq is None else ref_logq[rows])
-        out.update(lse=f["lse"], lp=f["lp"])
+        kl_only = entry == ENTRY_SUPPORT_KL
+        ids_r = np.asarray(ids)[rows]
+        ref_r = None if ref_logq is None else ref_logq[rows]
+        f = support_forward(z, ids_r, ref_r, padded)
+        if not kl_only:
+            out.update(lse=f["lse"], lp=f["lp"])
         if "kl" in f:
-            out["kl"] = f["kl"]
-        dz = support_dz(z, np.asarray(ids)[rows], None if ref_logq is None else ref_logq[rows],
-                        None if grad is None else np.asarray(grad)[rows],
-                        None if grad_kl is None else np.asarray(grad_kl)[rows])
+            out.update(kl=f["kl"], log_phat=f["log_phat"])
+        dz = support_dz(z, ids_r, ref_r,
+                        None if (kl_only or grad is None) else np.asarray(grad)[rows],
+                        None if grad_kl is None else np.asarray(grad_kl)[rows], padded)
     dz = dz / tau[:, None]
     out["dz"] = dz
     out["dH"] = grad_hidden(dz, W, threads=threads)

@@ -488,3 +488,114 @@ def test_temperature_rejects_nonpositive():
         oracle.temperature_scale(3, -1.0)
     with pytest.raises(ValueError):
         oracle.temperature_scale(3, 0.0, np.array([1.0, 0.0, 2.0]))
+
+
+# ------------------------------------------- padded lists and the KL-only entry
+
+def _padded_case(seed=61):
+    wl = wlmod.custom(n=12, hidden=64, vocab=300, entry=wlmod.ENTRY_SUPPORT, k=8, seed=seed,
+                      pad_frac=0.3)
+    inp = wlmod.make_inputs(wl)
+    inp.ids[3, :] = -1            # a row with no real candidate
+    inp.ids[5, 2] = -7            # any negative id is padding, also mid-list
+    return inp
+
+
+def test_padded_support_vs_torch_on_compacted_lists():
+    """A padded list equals the list with its padding slots removed: torch fp64
+    log_softmax / kl_div / autograd on each row's real candidates only."""
+    inp = _padded_case()
+    out = oracle.run(oracle.ENTRY_SUPPORT, inp.H, inp.W, ids=inp.ids, ref_logq=inp.ref_logq,
+                     grad=inp.grad, grad_kl=inp.grad_kl, padded=True)
+    H, W = _torch_problem(inp)
+    z = H @ W.T
+    lsm = F.log_softmax(z, 1)
+    obj = torch.zeros((), dtype=torch.float64)
+    for n in range(inp.ids.shape[0]):
+        real = np.nonzero(inp.ids[n] >= 0)[0]
+        pad = np.nonzero(inp.ids[n] < 0)[0]
+        assert np.all(out["lp"][n, pad] == 0.0)
+        if real.size == 0:
+            assert out["kl"][n] == 0.0
+            continue
+        idx = torch.tensor(inp.ids[n, real], dtype=torch.long)
+        lp = lsm[n, idx]
+        r = torch.tensor(inp.ref_logq[n, real], dtype=torch.float64)
+        kl = F.kl_div(F.log_softmax(z[n, idx], 0), r, log_target=True, reduction="sum")
+        np.testing.assert_allclose(out["lp"][n, real], lp.detach().numpy(), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(out["kl"][n], kl.item(), rtol=1e-10, atol=1e-14)
+        g = torch.tensor(inp.grad[n, real], dtype=torch.float64)
+        obj = obj + (lp * g).sum() + kl * float(inp.grad_kl[n])
+    obj.backward()
+    np.testing.assert_allclose(out["dH"], H.grad.numpy(), rtol=1e-9, atol=1e-13)
+    np.testing.assert_allclose(out["dW"], W.grad.numpy(), rtol=1e-9, atol=1e-13)
+
+
+def test_kl_only_entry_vs_torch():
+    """KL-only entry: KL(q || softmax over the candidates) and its gradient,
+    torch fp64 autograd; log p_hat is torch's log_softmax over the candidates."""
+    wl = wlmod.custom(n=10, hidden=64, vocab=350, entry=wlmod.ENTRY_SUPPORT, k=12, seed=62)
+    inp = wlmod.make_inputs(wl)
+    out = oracle.run(oracle.ENTRY_SUPPORT_KL, inp.H, inp.W, ids=inp.ids, ref_logq=inp.ref_logq,
+                     grad_kl=inp.grad_kl)
+    assert "lp" not in out and "lse" not in out
+    H, W = _torch_problem(inp)
+    zc = (H @ W.T).gather(1, torch.tensor(inp.ids, dtype=torch.long))
+    log_phat = F.log_softmax(zc, 1)
+    r = torch.tensor(inp.ref_logq, dtype=torch.float64)
+    kl = F.kl_div(log_phat, r, log_target=True, reduction="none").sum(1)
+    np.testing.assert_allclose(out["kl"], kl.detach().numpy(), rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(out["log_phat"], log_phat.detach().numpy(), rtol=1e-12, atol=1e-13)
+    (kl * torch.tensor(inp.grad_kl, dtype=torch.float64)).sum().backward()
+    np.testing.assert_allclose(out["dH"], H.grad.numpy(), rtol=1e-9, atol=1e-13)
+    np.testing.assert_allclose(out["dW"], W.grad.numpy(), rtol=1e-9, atol=1e-13)
+
+
+@pytest.mark.parametrize("entry", [3, 4])
+def test_padded_finite_differences(entry):
+    """Central differences on every element of H and W with padded lists (and
+    a duplicate id) for the support and KL-only entries."""
+    rng = np.random.default_rng(120 + entry)
+    N, Hd, V, K = 4, 6, 12, 5
+    H = rng.standard_normal((N, Hd))
+    W = rng.standard_normal((V, Hd)) * 0.5
+    ids = np.stack([rng.choice(V, K, replace=False) for _ in range(N)])
+    ids[0, 3:] = -1
+    ids[2, 1] = -1
+    ids[3, 4] = ids[3, 0]
+    q = rng.random((N, K)) + 0.1
+    rq = np.log(q / q.sum(1, keepdims=True))
+    g = rng.standard_normal((N, K)) if entry == 3 else None
+    gkl = rng.standard_normal(N)
+    out = oracle.run(entry, H, W, ids=ids, ref_logq=rq, grad=g, grad_kl=gkl, padded=True)
+
+    def obj(Hx, Wx):
+        z = oracle.logits(Hx, Wx)
+        f = oracle.support_forward(z, ids, rq, padded=True)
+        v = float((f["kl"] * gkl).sum())
+        if entry == 3:
+            v += float((f["lp"] * g).sum())
+        return v
+
+    h = 1e-6
+    for name, X, G in (("H", H, out["dH"]), ("W", W, out["dW"])):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(X.shape):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[idx] += h
+            Xm[idx] -= h
+            num[idx] = ((obj(Xp, W) - obj(Xm, W)) if name == "H" else (obj(H, Xp) - obj(H, Xm))) / (2 * h)
+        np.testing.assert_allclose(G, num, rtol=1e-6, atol=1e-8, err_msg=f"d{name} entry {entry}")
+
+
+def test_padding_rules():
+    z = np.zeros((2, 10))
+    ids = np.array([[1, -1], [3, 4]])
+    with pytest.raises(ValueError):
+        oracle.support_forward(z, ids, None)               # negative id without padding
+    with pytest.raises(ValueError):
+        oracle.support_forward(z, np.array([[1, 10], [0, 2]]), None, padded=True)   # >= V
+    f = oracle.support_forward(z, ids, np.log(np.full((2, 2), 0.5)), padded=True)
+    # row 0 has one real candidate: p_hat = 1 there, KL = q (log q - 0) with q = 0.5
+    assert f["log_phat"][0, 0] == 0.0 and abs(f["kl"][0] - 0.5 * math.log(0.5)) < 1e-15
+    assert f["lp"][0, 1] == 0.0

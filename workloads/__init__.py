@@ -44,6 +44,7 @@ ENTRY_CE_MEAN = 0
 ENTRY_CE_SUM = 1
 ENTRY_LOGPROB = 2
 ENTRY_SUPPORT = 3
+ENTRY_SUPPORT_KL = 4
 
 
 @dataclasses.dataclass(frozen=True)
@@ -60,6 +61,7 @@ class Workload:
     ignore_frac: float = 0.0
     k: int = 1                        # candidates per row (support entry)
     w_std: float = 0.02
+    pad_frac: float = 0.0             # padded candidate lists: mean fraction of padding slots
 
     @property
     def flops_fwd_bwd(self) -> float:
@@ -164,6 +166,12 @@ def make_inputs(wl: Workload, *, with_W: bool = True) -> Inputs:
         ref_logq = (g - np.log(np.exp(g).sum(axis=1, keepdims=True))).astype(np.float32)
         grad = rng.standard_normal((wl.n, wl.k), dtype=np.float32)
         grad_kl = rng.standard_normal(wl.n, dtype=np.float32)
+        if wl.pad_frac > 0.0:
+            # right-padded lists: row i keeps its first k - p_i ids, p_i ~ Binomial(k, pad_frac)
+            pads = rng.binomial(wl.k, wl.pad_frac, size=wl.n)
+            for i in range(wl.n):
+                if pads[i]:
+                    ids[i, wl.k - pads[i]:] = -1
     return Inputs(wl, H, W, targets, ids, ref_logq, grad, grad_kl)
 
 
