@@ -9,7 +9,8 @@ every entry raises.
 Two layers:
 
 * ``lmhead_workspace_size``, ``lmhead_loss_fwd``, ``lmhead_logprob``,
-  ``lmhead_support_logprob_kl``, ``lmhead_loss_bwd``,
+  ``lmhead_support_logprob_kl``, ``lmhead_support_logprob``,
+  ``lmhead_support_kl``, ``lmhead_loss_bwd``,
   ``lmhead_loss_bwd_accumulate``, ``lmhead_memory_report``,
   ``lmhead_plan_chunk``, ``lmhead_status_string``,
   ``lmhead_read_device_error``: the C entry points
@@ -43,6 +44,9 @@ ENTRY_CE_MEAN = 0
 ENTRY_CE_SUM = 1
 ENTRY_LOGPROB = 2
 ENTRY_SUPPORT = 3
+ENTRY_SUPPORT_KL = 4
+
+FLAG_PADDED_IDS = 1
 
 DEVERR_LABEL = 1
 DEVERR_CANDIDATE = 2
@@ -112,6 +116,8 @@ def lib() -> ctypes.CDLL:
         L.lmhead_loss_fwd.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.lmhead_logprob.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
         L.lmhead_support_logprob_kl.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.lmhead_support_logprob.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.lmhead_support_kl.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.lmhead_loss_bwd.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.lmhead_loss_bwd_accumulate.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                  vp, vp, sz, vp]
@@ -122,6 +128,7 @@ def lib() -> ctypes.CDLL:
         L.lmhead_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32),
                                                ctypes.POINTER(ctypes.c_int64)]
         for f in (L.lmhead_loss_fwd, L.lmhead_logprob, L.lmhead_support_logprob_kl,
+                  L.lmhead_support_logprob, L.lmhead_support_kl,
                   L.lmhead_loss_bwd, L.lmhead_loss_bwd_accumulate, L.lmhead_read_device_error,
                   L.lmhead_memory_report, L.lmhead_plan_chunk):
             f.restype = i32
@@ -194,6 +201,17 @@ def lmhead_support_logprob_kl(p, H, W, ids, ref_logq, lp, kl, lse, workspace, wo
     return lib().lmhead_support_logprob_kl(ctypes.byref(p), _p(H), _p(W), _p(ids), _p(ref_logq),
                                            _p(lp), _p(kl), _p(lse), _p(workspace), workspace_bytes,
                                            _stream(stream))
+
+
+def lmhead_support_logprob(p, H, W, ids, lp, lse, workspace, workspace_bytes, stream=None) -> int:
+    return lib().lmhead_support_logprob(ctypes.byref(p), _p(H), _p(W), _p(ids), _p(lp), _p(lse),
+                                        _p(workspace), workspace_bytes, _stream(stream))
+
+
+def lmhead_support_kl(p, H, W, ids, ref_logq, kl, logp_hat, workspace, workspace_bytes,
+                      stream=None) -> int:
+    return lib().lmhead_support_kl(ctypes.byref(p), _p(H), _p(W), _p(ids), _p(ref_logq), _p(kl),
+                                   _p(logp_hat), _p(workspace), workspace_bytes, _stream(stream))
 
 
 def lmhead_loss_bwd(p, entry, H, W, targets_or_ids, ref_logq, lse, saved_lp, grad, grad_kl, dH, dW,
@@ -297,13 +315,14 @@ def logprob_forward(H, W, targets, chunk: int, ws: Optional[torch.Tensor] = None
 
 
 def support_forward(H, W, ids, ref_logq, chunk: int, ws: Optional[torch.Tensor] = None,
-                    temperature: float = 0.0, row_temperature=None):
-    """Returns (lp fp32 [n, k], kl fp32 [n] or None, lse fp32 [n], workspace)."""
+                    temperature: float = 0.0, row_temperature=None, padded: bool = False):
+    """Returns (lp fp32 [n, k], kl fp32 [n] or None, lse fp32 [n], workspace).
+    padded: a negative id is a padding slot (LMHEAD_FLAG_PADDED_IDS)."""
     _check_inputs(H, W, ids)
     n, k = ids.shape
     _check_row_temperature(row_temperature, n)
-    p = problem(n, H.shape[1], W.shape[0], chunk, -1, k, temperature=temperature,
-                row_temperature=row_temperature)
+    p = problem(n, H.shape[1], W.shape[0], chunk, -1, k, FLAG_PADDED_IDS if padded else 0,
+                temperature=temperature, row_temperature=row_temperature)
     if ws is None:
         ws = workspace(p, ENTRY_SUPPORT, False, H.device)
     lp = torch.empty(n, k, dtype=torch.float32, device=H.device)
@@ -314,17 +333,52 @@ def support_forward(H, W, ids, ref_logq, chunk: int, ws: Optional[torch.Tensor] 
     return lp, kl, lse, ws
 
 
+def support_logprob_forward(H, W, ids, chunk: int, ws: Optional[torch.Tensor] = None,
+                            temperature: float = 0.0, row_temperature=None, padded: bool = False):
+    """Support-set log-probabilities only. Returns (lp fp32 [n, k], lse fp32 [n], workspace)."""
+    _check_inputs(H, W, ids)
+    n, k = ids.shape
+    _check_row_temperature(row_temperature, n)
+    p = problem(n, H.shape[1], W.shape[0], chunk, -1, k, FLAG_PADDED_IDS if padded else 0,
+                temperature=temperature, row_temperature=row_temperature)
+    if ws is None:
+        ws = workspace(p, ENTRY_SUPPORT, False, H.device)
+    lp = torch.empty(n, k, dtype=torch.float32, device=H.device)
+    lse = torch.empty(n, dtype=torch.float32, device=H.device)
+    _ok(lmhead_support_logprob(p, H, W, ids, lp, lse, ws, ws.numel()), "lmhead_support_logprob")
+    return lp, lse, ws
+
+
+def support_kl_forward(H, W, ids, ref_logq, ws: Optional[torch.Tensor] = None,
+                       temperature: float = 0.0, row_temperature=None, padded: bool = False):
+    """KL-only support entry (no vocabulary-wide pass). Returns (kl fp32 [n],
+    log p_hat fp32 [n, k], workspace)."""
+    _check_inputs(H, W, ids)
+    n, k = ids.shape
+    _check_row_temperature(row_temperature, n)
+    p = problem(n, H.shape[1], W.shape[0], 256, -1, k, FLAG_PADDED_IDS if padded else 0,
+                temperature=temperature, row_temperature=row_temperature)
+    if ws is None:
+        ws = workspace(p, ENTRY_SUPPORT_KL, False, H.device)
+    kl = torch.empty(n, dtype=torch.float32, device=H.device)
+    logp_hat = torch.empty(n, k, dtype=torch.float32, device=H.device)
+    _ok(lmhead_support_kl(p, H, W, ids, ref_logq, kl, logp_hat, ws, ws.numel()), "lmhead_support_kl")
+    return kl, logp_hat, ws
+
+
 def backward(entry: int, H, W, idx, lse, grad, chunk: int, *, ref_logq=None, saved_lp=None,
              grad_kl=None, num_valid: int = -1, need_dH: bool = True, need_dW: bool = True,
              ws: Optional[torch.Tensor] = None, dH=None, dW=None, temperature: float = 0.0,
-             row_temperature=None):
+             row_temperature=None, padded: bool = False):
     """Returns (dH bf16 [n, hidden] or None, dW bf16 [vocab, hidden] or None).
-    temperature / row_temperature must be those of the forward that produced lse."""
+    temperature / row_temperature must be those of the forward that produced lse.
+    ENTRY_SUPPORT_KL: saved_lp is the forward's log p_hat; lse and grad are unused."""
     _check_inputs(H, W, idx)
     _check_row_temperature(row_temperature, H.shape[0])
-    k = idx.shape[1] if entry == ENTRY_SUPPORT else 1
+    k = idx.shape[1] if entry in (ENTRY_SUPPORT, ENTRY_SUPPORT_KL) else 1
     p = problem(H.shape[0], H.shape[1], W.shape[0], chunk, num_valid, k,
-                temperature=temperature, row_temperature=row_temperature)
+                FLAG_PADDED_IDS if padded else 0, temperature=temperature,
+                row_temperature=row_temperature)
     if ws is None:
         ws = workspace(p, entry, True, H.device)
     if need_dH and dH is None:
@@ -349,7 +403,7 @@ def _check_acc(name, t, shape, device):
 def backward_accumulate(entry: int, H, W, idx, lse, grad, chunk: int, *, dH_acc=None, dW_acc=None,
                         ref_logq=None, saved_lp=None, grad_kl=None, num_valid: int = -1,
                         out_bf16: bool = False, ws: Optional[torch.Tensor] = None,
-                        temperature: float = 0.0, row_temperature=None):
+                        temperature: float = 0.0, row_temperature=None, padded: bool = False):
     """dH_acc += dL/dH and dW_acc += dL/dW in fp32 (either may be None).
     Returns (dH, dW): the bf16 casts of the updated accumulators when out_bf16,
     else (None, None)."""
@@ -357,9 +411,10 @@ def backward_accumulate(entry: int, H, W, idx, lse, grad, chunk: int, *, dH_acc=
     _check_row_temperature(row_temperature, H.shape[0])
     _check_acc("dH_acc", dH_acc, H.shape, H.device)
     _check_acc("dW_acc", dW_acc, W.shape, H.device)
-    k = idx.shape[1] if entry == ENTRY_SUPPORT else 1
+    k = idx.shape[1] if entry in (ENTRY_SUPPORT, ENTRY_SUPPORT_KL) else 1
     p = problem(H.shape[0], H.shape[1], W.shape[0], chunk, num_valid, k,
-                temperature=temperature, row_temperature=row_temperature)
+                FLAG_PADDED_IDS if padded else 0, temperature=temperature,
+                row_temperature=row_temperature)
     if ws is None:
         ws = workspace(p, entry, True, H.device)
     dH = torch.empty_like(H) if (out_bf16 and dH_acc is not None) else None
@@ -422,11 +477,12 @@ class ChunkedLMHeadSupport(torch.autograd.Function):
     """Full-vocabulary log-probabilities of K candidates per row and KL(q || p_hat)."""
 
     @staticmethod
-    def forward(ctx, H, W, ids, ref_logq, chunk, temperature=0.0, row_temperature=None):
+    def forward(ctx, H, W, ids, ref_logq, chunk, temperature=0.0, row_temperature=None,
+                padded=False):
         lp, kl, lse, _ = support_forward(H, W, ids, ref_logq, chunk, temperature=temperature,
-                                         row_temperature=row_temperature)
+                                         row_temperature=row_temperature, padded=padded)
         ctx.save_for_backward(H, W, ids, ref_logq, lse, lp, row_temperature)
-        ctx.cfg = (chunk, temperature)
+        ctx.cfg = (chunk, temperature, padded)
         ctx.has_kl = kl is not None
         if kl is None:
             kl = torch.zeros(H.shape[0], dtype=torch.float32, device=H.device)
@@ -435,14 +491,36 @@ class ChunkedLMHeadSupport(torch.autograd.Function):
     @staticmethod
     def backward(ctx, g_lp, g_kl):
         H, W, ids, ref_logq, lse, lp, rt = ctx.saved_tensors
-        chunk, temperature = ctx.cfg
+        chunk, temperature, padded = ctx.cfg
         gl = g_lp.to(torch.float32).contiguous() if g_lp is not None else None
         gk = g_kl.to(torch.float32).contiguous() if (g_kl is not None and ctx.has_kl) else None
         dH, dW = backward(ENTRY_SUPPORT, H, W, ids, lse, gl, chunk,
                           ref_logq=ref_logq if ctx.has_kl else None,
                           saved_lp=lp if ctx.has_kl else None, grad_kl=gk,
                           need_dH=ctx.needs_input_grad[0], need_dW=ctx.needs_input_grad[1],
-                          temperature=temperature, row_temperature=rt)
+                          temperature=temperature, row_temperature=rt, padded=padded)
+        return dH, dW, None, None, None, None, None, None
+
+
+class ChunkedLMHeadSupportKL(torch.autograd.Function):
+    """KL(q || p_hat) over each row's candidates, without a vocabulary-wide pass."""
+
+    @staticmethod
+    def forward(ctx, H, W, ids, ref_logq, temperature=0.0, row_temperature=None, padded=False):
+        kl, logp_hat, _ = support_kl_forward(H, W, ids, ref_logq, temperature=temperature,
+                                             row_temperature=row_temperature, padded=padded)
+        ctx.save_for_backward(H, W, ids, ref_logq, logp_hat, row_temperature)
+        ctx.cfg = (temperature, padded)
+        return kl
+
+    @staticmethod
+    def backward(ctx, g_kl):
+        H, W, ids, ref_logq, logp_hat, rt = ctx.saved_tensors
+        temperature, padded = ctx.cfg
+        dH, dW = backward(ENTRY_SUPPORT_KL, H, W, ids, None, None, 256, ref_logq=ref_logq,
+                          saved_lp=logp_hat, grad_kl=g_kl.to(torch.float32).contiguous(),
+                          need_dH=ctx.needs_input_grad[0], need_dW=ctx.needs_input_grad[1],
+                          temperature=temperature, row_temperature=rt, padded=padded)
         return dH, dW, None, None, None, None, None
 
 
@@ -467,6 +545,22 @@ def logprob(H, W, targets, chunk: int = 8192, temperature: float = 0.0, row_temp
 
 
 def support_logprob_kl(H, W, ids, ref_logq, chunk: int = 8192, temperature: float = 0.0,
-                       row_temperature=None, memory_budget: Optional[int] = None):
+                       row_temperature=None, memory_budget: Optional[int] = None,
+                       padded: bool = False):
     chunk = _chunk(chunk, memory_budget, H, W, ENTRY_SUPPORT, ids.shape[1])
-    return ChunkedLMHeadSupport.apply(H, W, ids, ref_logq, chunk, temperature, row_temperature)
+    return ChunkedLMHeadSupport.apply(H, W, ids, ref_logq, chunk, temperature, row_temperature,
+                                      padded)
+
+
+def support_logprob(H, W, ids, chunk: int = 8192, temperature: float = 0.0, row_temperature=None,
+                    memory_budget: Optional[int] = None, padded: bool = False):
+    """Full-vocabulary log-probabilities of the candidates (no KL)."""
+    lp, _ = support_logprob_kl(H, W, ids, None, chunk, temperature, row_temperature,
+                               memory_budget, padded)
+    return lp
+
+
+def support_kl(H, W, ids, ref_logq, temperature: float = 0.0, row_temperature=None,
+               padded: bool = False):
+    """KL(q || p_hat) per row over the candidates (KL-only entry)."""
+    return ChunkedLMHeadSupportKL.apply(H, W, ids, ref_logq, temperature, row_temperature, padded)

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblmhead.so")
-SOURCES = ["lmhead_kernels.hip", "lmhead_api.hip"]
+SOURCES = ["lmhead_kernels.hip", "lmhead_candidates.hip", "lmhead_api.hip"]
 HEADERS = ["gemm_core.h", "lmhead_kernels.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -18,7 +18,6 @@ using namespace lmhead;
 constexpr int64_t kMaxRows = int64_t(1) << 30;
 constexpr int64_t kMaxVocab = int64_t(1) << 30;
 constexpr int64_t kMaxHidden = 65536;
-constexpr int kMaxCandidates = 1024;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
@@ -29,13 +28,18 @@ struct Layout {
     size_t hdr, lse, part, zg, rows;
     // backward regions
     size_t coef_a, coef_c, Ht, G, Gt, Wt, dh_acc;
+    // backward of the KL-only entry: inverse index of the candidate ids
+    size_t counts, offsets, cursor, list;
     size_t fwd_total, bwd_total;
 };
 
+bool is_support(int entry) { return entry == LMHEAD_ENTRY_SUPPORT || entry == LMHEAD_ENTRY_SUPPORT_KL; }
+
 int validate_problem(const lmhead_problem* p, int entry) {
     if (p == nullptr) return LMHEAD_ERR_ARG;
-    if (entry < LMHEAD_ENTRY_CE_MEAN || entry > LMHEAD_ENTRY_SUPPORT) return LMHEAD_ERR_ARG;
-    if (p->flags != 0 || p->reserved != 0) return LMHEAD_ERR_ARG;
+    if (entry < LMHEAD_ENTRY_CE_MEAN || entry > LMHEAD_ENTRY_SUPPORT_KL) return LMHEAD_ERR_ARG;
+    if ((p->flags & ~LMHEAD_FLAG_PADDED_IDS) != 0 || p->reserved != 0) return LMHEAD_ERR_ARG;
+    if ((p->flags & LMHEAD_FLAG_PADDED_IDS) && !is_support(entry)) return LMHEAD_ERR_ARG;
     // scalar temperature: 0 (off) or positive and finite
     if (!(p->temperature >= 0.0f && p->temperature <= 3.402823466e38f)) return LMHEAD_ERR_ARG;
     if (p->n < 0 || p->n > kMaxRows) return LMHEAD_ERR_SHAPE;
@@ -43,7 +47,9 @@ int validate_problem(const lmhead_problem* p, int entry) {
     if (p->vocab < 1 || p->vocab > kMaxVocab) return LMHEAD_ERR_SHAPE;
     if (p->chunk < 256 || p->chunk % 256 != 0 || p->chunk > kMaxVocab + 256) return LMHEAD_ERR_SHAPE;
     if (p->num_valid < -1) return LMHEAD_ERR_SHAPE;
-    if (entry == LMHEAD_ENTRY_SUPPORT && (p->k < 1 || p->k > kMaxCandidates)) return LMHEAD_ERR_SHAPE;
+    if (is_support(entry) && (p->k < 1 || p->k > kMaxCandidates)) return LMHEAD_ERR_SHAPE;
+    // the KL-only entry indexes (row, candidate) entries with int32
+    if (entry == LMHEAD_ENTRY_SUPPORT_KL && p->n * (int64_t)p->k > INT_MAX) return LMHEAD_ERR_SHAPE;
     // one workgroup per 256 x 256 tile: keep every grid within 2^31 - 1
     if (cdiv(p->n, kTile) * cdiv(p->vocab, kTile) > INT_MAX) return LMHEAD_ERR_SHAPE;
     return LMHEAD_OK;
@@ -58,7 +64,7 @@ Layout plan(const lmhead_problem& p, int entry) {
     L.chunk = p.chunk;
     L.w_pad = round_up(p.chunk < p.vocab ? p.chunk : p.vocab, kTile);
     L.tiles_v = cdiv(p.vocab, kTile);
-    L.k = entry == LMHEAD_ENTRY_SUPPORT ? p.k : 1;
+    L.k = is_support(entry) ? p.k : 1;
     size_t off = 0;
     auto take = [&off](int64_t bytes) {
         const size_t o = off;
@@ -67,6 +73,18 @@ Layout plan(const lmhead_problem& p, int entry) {
     };
     L.hdr = take(256);
     const size_t after_hdr = off;
+    if (entry == LMHEAD_ENTRY_SUPPORT_KL) {
+        // no vocabulary-wide pass: the forward needs only the header
+        L.fwd_total = off;
+        L.coef_a = take(4 * L.n_pad);
+        L.coef_c = take(4 * L.n * L.k);
+        L.counts = take(4 * L.vocab);
+        L.offsets = take(4 * (L.vocab + 1));
+        L.cursor = take(4 * L.vocab);
+        L.list = take(4 * L.n * L.k);
+        L.bwd_total = off;
+        return L;
+    }
     L.lse = take(4 * L.n);
     L.part = take(8 * L.tiles_v * L.n);
     L.zg = take(4 * L.n * L.k);
@@ -148,9 +166,10 @@ int forward(const lmhead_problem* p, int entry, const void* H, const void* W, co
         if (loss) fill_u32(loss, 1, 0u, s);
         return launched();
     }
-    const bool support = entry == LMHEAD_ENTRY_SUPPORT;
+    const int padded = (p->flags & LMHEAD_FLAG_PADDED_IDS) ? 1 : 0;
+    const int mode = entry == LMHEAD_ENTRY_SUPPORT ? 1 + padded : 0;
     scan_labels_kernel<<<grid_1d(L.n, kThreads, 1024), kThreads, 0, s>>>(ids, L.n, (int)L.k, L.vocab,
-                                                                          support ? 1 : 0, T, hdr);
+                                                                          mode, T, hdr);
     FwdTilesArgs fa;
     fa.T = T;
     fa.H = (const bf16_bits*)H;
@@ -180,6 +199,7 @@ int forward(const lmhead_problem* p, int entry, const void* H, const void* W, co
     fin.lse = lse_out != nullptr ? lse_out : (float*)(w + L.lse);
     fin.row_out = ce ? (float*)(w + L.rows) : row_out;
     fin.kl = kl;
+    fin.padded = padded;
     finalize_rows_kernel<<<grid_1d(L.n * 8, kThreads, INT_MAX), kThreads, 0, s>>>(fin);   // 8 lanes per row
     if (ce)
         ce_reduce_kernel<<<1, kThreads, 0, s>>>(fin.row_out, L.n, hdr, p->num_valid,
@@ -195,10 +215,13 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
              size_t workspace_bytes, void* stream) {
     int st = validate_problem(p, entry);
     if (st != LMHEAD_OK) return st;
-    const bool support = entry == LMHEAD_ENTRY_SUPPORT;
+    const bool support = is_support(entry);
+    const bool kl_only = entry == LMHEAD_ENTRY_SUPPORT_KL;
     if (workspace == nullptr) return LMHEAD_ERR_ARG;
+    if (kl_only && grad != nullptr) return LMHEAD_ERR_ARG;   // the KL-only entry has no lp output
     if (p->n > 0) {
-        if (H == nullptr || W == nullptr || ids == nullptr || lse == nullptr) return LMHEAD_ERR_ARG;
+        if (H == nullptr || W == nullptr || ids == nullptr) return LMHEAD_ERR_ARG;
+        if (!kl_only && lse == nullptr) return LMHEAD_ERR_ARG;
         if (!support && grad == nullptr) return LMHEAD_ERR_ARG;
         if (support && grad_kl != nullptr && (ref_logq == nullptr || saved_lp == nullptr))
             return LMHEAD_ERR_ARG;
@@ -228,11 +251,13 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
                 dW_acc, L.vocab * L.hidden, (bf16_bits*)dW);
         return launched();
     }
+    const int padded = (p->flags & LMHEAD_FLAG_PADDED_IDS) ? 1 : 0;
     scan_labels_kernel<<<grid_1d(L.n, kThreads, 1024), kThreads, 0, s>>>(ids, L.n, (int)L.k, L.vocab,
-                                                                          support ? 1 : 0, T, hdr);
+                                                                          support ? 1 + padded : 0, T, hdr);
     CoeffArgs ca;
     ca.T = T;
-    ca.entry = entry;
+    ca.entry = support ? LMHEAD_ENTRY_SUPPORT : entry;
+    ca.padded = padded;
     ca.n = L.n;
     ca.n_pad = L.n_pad;
     ca.vocab = L.vocab;
@@ -247,6 +272,43 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
     ca.coef_a = (float*)(w + L.coef_a);
     ca.coef_c = (float*)(w + L.coef_c);
     coeffs_kernel<<<grid_1d(L.n_pad, kThreads, INT_MAX), kThreads, 0, s>>>(ca);
+    if (kl_only) {
+        // dL/dz is nonzero only at the candidates: gathers instead of contractions
+        CandBwdArgs cb;
+        cb.H = (const bf16_bits*)H;
+        cb.W = (const bf16_bits*)W;
+        cb.n = L.n;
+        cb.hidden = L.hidden;
+        cb.vocab = L.vocab;
+        cb.k = (int)L.k;
+        cb.ids = ids;
+        cb.coef_c = ca.coef_c;
+        cb.dH = (bf16_bits*)dH;
+        cb.dH_acc = dH_acc;
+        cb.dW = (bf16_bits*)dW;
+        cb.dW_acc = dW_acc;
+        int32_t* counts = (int32_t*)(w + L.counts);
+        int32_t* offsets = (int32_t*)(w + L.offsets);
+        int32_t* cursor = (int32_t*)(w + L.cursor);
+        int32_t* list = (int32_t*)(w + L.list);
+        cb.offsets = offsets;
+        cb.list = list;
+        const unsigned row_blocks = (unsigned)cdiv(L.n, kThreads / 64);
+        if (want_dh) cand_dh_kernel<<<row_blocks, kThreads, 0, s>>>(cb);
+        if (want_dw) {
+            const int64_t nk = L.n * L.k;
+            fill_u32(counts, L.vocab, 0u, s);
+            fill_u32(cursor, L.vocab, 0u, s);
+            cand_count_kernel<<<grid_1d(nk, kThreads, 4096), kThreads, 0, s>>>(ids, nk, L.vocab, counts);
+            exclusive_scan_kernel<<<1, 1024, 0, s>>>(counts, L.vocab, offsets);
+            cand_fill_kernel<<<grid_1d(nk, kThreads, 4096), kThreads, 0, s>>>(ids, nk, L.vocab, offsets,
+                                                                              cursor, list);
+            bucket_sort_kernel<<<grid_1d(L.vocab, kThreads, 4096), kThreads, 0, s>>>(offsets, L.vocab,
+                                                                                     list);
+            cand_dw_kernel<<<(unsigned)cdiv(L.vocab, kThreads / 64), kThreads, 0, s>>>(cb);
+        }
+        return launched();
+    }
 
     bf16_bits* Ht = (bf16_bits*)(w + L.Ht);
     bf16_bits* G = (bf16_bits*)(w + L.G);
@@ -347,8 +409,9 @@ int lmhead_memory_report(const lmhead_problem* p, int entry, int with_backward,
     r.chunks = cdiv(L.vocab, L.chunk);
     r.workspace_bytes = with_backward ? L.bwd_total : L.fwd_total;
     r.forward_bytes = L.fwd_total;
-    r.partials_bytes = (size_t)(8 * L.tiles_v * L.n);
-    if (with_backward) {
+    const bool kl_only = entry == LMHEAD_ENTRY_SUPPORT_KL;
+    r.partials_bytes = kl_only ? 0 : (size_t)(8 * L.tiles_v * L.n);
+    if (with_backward && !kl_only) {
         r.dz_chunk_bytes = (size_t)(4 * L.n_pad * L.w_pad);
         r.operand_copy_bytes = (size_t)(2 * L.hidden * L.n_pad + 2 * L.hidden * L.w_pad);
         r.dh_acc_bytes = (size_t)(4 * L.n * L.hidden);
@@ -357,7 +420,8 @@ int lmhead_memory_report(const lmhead_problem* p, int entry, int with_backward,
     size_t outs = (size_t)(4 * L.n);
     if (entry == LMHEAD_ENTRY_CE_MEAN || entry == LMHEAD_ENTRY_CE_SUM) outs += 4;
     else if (entry == LMHEAD_ENTRY_LOGPROB) outs += (size_t)(4 * L.n);
-    else outs += (size_t)(4 * L.n * L.k + 4 * L.n);
+    else outs += (size_t)(4 * L.n * L.k + 4 * L.n);   // lp or log p_hat [n, k], kl [n]
+    if (kl_only) outs -= (size_t)(4 * L.n);            // no lse
     if (with_backward) outs += (size_t)(2 * L.n * L.hidden + 2 * L.vocab * L.hidden);
     r.caller_output_bytes = outs;
     *out = r;
@@ -408,6 +472,54 @@ int lmhead_support_logprob_kl(const lmhead_problem* p, const void* H, const void
                    workspace_bytes, stream);
 }
 
+
+int lmhead_support_logprob(const lmhead_problem* p, const void* H, const void* W,
+                           const int32_t* ids, float* lp, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return forward(p, LMHEAD_ENTRY_SUPPORT, H, W, ids, nullptr, lp, nullptr, lse, nullptr, workspace,
+                   workspace_bytes, stream);
+}
+
+int lmhead_support_kl(const lmhead_problem* p, const void* H, const void* W, const int32_t* ids,
+                      const float* ref_logq, float* kl, float* logp_hat, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    int st = validate_problem(p, LMHEAD_ENTRY_SUPPORT_KL);
+    if (st != LMHEAD_OK) return st;
+    if (workspace == nullptr) return LMHEAD_ERR_ARG;
+    if (p->n > 0 && (H == nullptr || W == nullptr || ids == nullptr || ref_logq == nullptr ||
+                     kl == nullptr))
+        return LMHEAD_ERR_ARG;
+    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(workspace, 256) ||
+        !aligned(p->row_temperature, 4))
+        return LMHEAD_ERR_ALIGN;
+    const Layout L = plan(*p, LMHEAD_ENTRY_SUPPORT_KL);
+    if (workspace_bytes < L.fwd_total) return LMHEAD_ERR_WORKSPACE;
+    const Temperature T = temperature_of(*p);
+    st = check_device();
+    if (st != LMHEAD_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    int32_t* hdr = (int32_t*)((char*)workspace + L.hdr);
+    init_header_kernel<<<1, 64, 0, s>>>(hdr);
+    if (L.n == 0) return launched();
+    const int padded = (p->flags & LMHEAD_FLAG_PADDED_IDS) ? 1 : 0;
+    scan_labels_kernel<<<grid_1d(L.n, kThreads, 1024), kThreads, 0, s>>>(ids, L.n, (int)L.k, L.vocab,
+                                                                          1 + padded, T, hdr);
+    CandFwdArgs ca;
+    ca.H = (const bf16_bits*)H;
+    ca.W = (const bf16_bits*)W;
+    ca.n = L.n;
+    ca.hidden = L.hidden;
+    ca.vocab = L.vocab;
+    ca.k = (int)L.k;
+    ca.padded = padded;
+    ca.ids = ids;
+    ca.ref_logq = ref_logq;
+    ca.kl = kl;
+    ca.logp_hat = logp_hat;
+    ca.T = T;
+    cand_kl_fwd_kernel<<<(unsigned)cdiv(L.n, kThreads / 64), kThreads, 0, s>>>(ca);
+    return launched();
+}
 
 int lmhead_loss_bwd(const lmhead_problem* p, int entry, const void* H, const void* W,
                     const int32_t* ids, const float* ref_logq, const float* lse,

@@ -1,0 +1,263 @@
+// lmhead_candidates.hip — the KL-only support entry, which needs the logits of
+// the listed candidates only: KL(q || p_hat) renormalises the model over the
+// K candidates of a row, so neither it nor its gradient touches the other
+// V - K logits (FlashInfer PR #8059 lists support_logprob and support_kl as
+// separate entries). Every kernel is a gather over rows of W or H; there is
+// no vocabulary-wide contraction.
+//
+// Determinism: each dot product accumulates in a fixed lane order and is
+// reduced by a fixed xor-butterfly; the dW rows sum their (row, candidate)
+// entries in ascending order after a counting sort whose buckets are sorted,
+// so atomics only ever count (integers) and never order a floating-point sum.
+#include <climits>
+
+#include "lmhead_kernels.h"
+
+namespace lmhead {
+
+namespace {
+
+constexpr int kWaves = kThreads / 64;   // rows (or vocabulary rows) per workgroup
+constexpr int kSeg = 512;               // hidden elements one wave covers per step (8 per lane)
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ void fma8(float (&acc)[8], float c, const uint4& v) {
+    acc[0] = __builtin_fmaf(c, bf16_lo(v.x), acc[0]);
+    acc[1] = __builtin_fmaf(c, bf16_hi(v.x), acc[1]);
+    acc[2] = __builtin_fmaf(c, bf16_lo(v.y), acc[2]);
+    acc[3] = __builtin_fmaf(c, bf16_hi(v.y), acc[3]);
+    acc[4] = __builtin_fmaf(c, bf16_lo(v.z), acc[4]);
+    acc[5] = __builtin_fmaf(c, bf16_hi(v.z), acc[5]);
+    acc[6] = __builtin_fmaf(c, bf16_lo(v.w), acc[6]);
+    acc[7] = __builtin_fmaf(c, bf16_hi(v.w), acc[7]);
+}
+
+__device__ __forceinline__ float dot8(const uint4& a, const uint4& b, float acc) {
+    acc = __builtin_fmaf(bf16_lo(a.x), bf16_lo(b.x), acc);
+    acc = __builtin_fmaf(bf16_hi(a.x), bf16_hi(b.x), acc);
+    acc = __builtin_fmaf(bf16_lo(a.y), bf16_lo(b.y), acc);
+    acc = __builtin_fmaf(bf16_hi(a.y), bf16_hi(b.y), acc);
+    acc = __builtin_fmaf(bf16_lo(a.z), bf16_lo(b.z), acc);
+    acc = __builtin_fmaf(bf16_hi(a.z), bf16_hi(b.z), acc);
+    acc = __builtin_fmaf(bf16_lo(a.w), bf16_lo(b.w), acc);
+    acc = __builtin_fmaf(bf16_hi(a.w), bf16_hi(b.w), acc);
+    return acc;
+}
+
+// xor-butterfly over the 64 lanes: every lane ends with the same value, and the
+// association order is fixed
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ float quiet_nan_f() { return __builtin_nanf(""); }
+__device__ __forceinline__ float neg_inf_f() { return -__builtin_huge_valf(); }
+
+// Store 8 fp32 values as bf16 (RNE) and / or add them to an fp32 accumulator.
+__device__ __forceinline__ void store_row8(float (&acc)[8], float* acc_row, bf16_bits* out_row) {
+    if (acc_row != nullptr) {
+        float4* p = reinterpret_cast<float4*>(acc_row);
+        const float4 a0 = p[0], a1 = p[1];
+        acc[0] = a0.x + acc[0];
+        acc[1] = a0.y + acc[1];
+        acc[2] = a0.z + acc[2];
+        acc[3] = a0.w + acc[3];
+        acc[4] = a1.x + acc[4];
+        acc[5] = a1.y + acc[5];
+        acc[6] = a1.z + acc[6];
+        acc[7] = a1.w + acc[7];
+        p[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        p[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+    if (out_row != nullptr)
+        *reinterpret_cast<uint4*>(out_row) =
+            make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                       pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+}
+
+}  // namespace
+
+// One wave per row: the K candidate logits z_k = H[n] . W[id_k] / tau_n
+// (fp32 sums of bf16 products), then log p_hat_k = z_k - log sum_j exp z_j
+// over the row's real candidates and KL = sum_k q_k (r_k - log p_hat_k).
+__global__ __launch_bounds__(kThreads) void cand_kl_fwd_kernel(CandFwdArgs a) {
+    __shared__ float zs[kWaves][kMaxCandidates];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
+    if (row >= a.n) return;   // whole waves only; nothing below synchronises the workgroup
+    const int k = a.k;
+    const int32_t* idr = a.ids + row * k;
+    const float tau = row_tau(a.T, row);
+    bool bad = a.T.row != nullptr && !tau_ok(tau);
+    for (int kk = 0; kk < k; ++kk) {
+        const int64_t id = idr[kk];
+        bad = bad || id >= a.vocab || (id < 0 && !a.padded);
+    }
+    if (bad) {
+        if (lane == 0) a.kl[row] = quiet_nan_f();
+        if (a.logp_hat != nullptr)
+            for (int kk = lane; kk < k; kk += 64) a.logp_hat[row * k + kk] = quiet_nan_f();
+        return;
+    }
+    const float inv_tau = 1.0f / tau;
+    const bf16_bits* hrow = a.H + row * a.hidden;
+    float* z = zs[wave];
+    for (int k0 = 0; k0 < k; k0 += 4) {
+        float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        int32_t id[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) id[c] = k0 + c < k ? idr[k0 + c] : -1;
+        for (int64_t h = lane * 8; h < a.hidden; h += kSeg) {
+            const uint4 hv = *reinterpret_cast<const uint4*>(hrow + h);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (id[c] >= 0) {
+                    const uint4 wv = *reinterpret_cast<const uint4*>(a.W + (int64_t)id[c] * a.hidden + h);
+                    part[c] = dot8(hv, wv, part[c]);
+                }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float zc = wave_sum(part[c]) * inv_tau;
+            if (lane == 0 && k0 + c < k) z[k0 + c] = zc;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float mx = neg_inf_f();
+    for (int kk = lane; kk < k; kk += 64)
+        if (idr[kk] >= 0) mx = fmaxf(mx, z[kk]);
+    mx = wave_max(mx);
+    float se = 0.0f;
+    for (int kk = lane; kk < k; kk += 64)
+        if (idr[kk] >= 0) se += expf(z[kk] - mx);
+    se = wave_sum(se);
+    const float ls = mx + logf(se);
+    const float* r = a.ref_logq + row * k;
+    float kl = 0.0f;
+    for (int kk = lane; kk < k; kk += 64) {
+        const bool real = idr[kk] >= 0;
+        const float lph = real ? z[kk] - ls : 0.0f;
+        if (a.logp_hat != nullptr) a.logp_hat[row * k + kk] = lph;
+        const float q = expf(r[kk]);
+        if (real && q > 0.0f) kl += q * (r[kk] - lph);
+    }
+    kl = wave_sum(kl);
+    if (lane == 0) a.kl[row] = kl;
+}
+
+// dH[n] = sum_k c_nk W[id_nk] (ascending k), one wave per row.
+__global__ __launch_bounds__(kThreads) void cand_dh_kernel(CandBwdArgs a) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
+    if (row >= a.n) return;
+    const int32_t* idr = a.ids + row * a.k;
+    const float* cr = a.coef_c + row * a.k;
+    for (int64_t h = lane * 8; h < a.hidden; h += kSeg) {
+        float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        for (int kk = 0; kk < a.k; ++kk) {
+            const int32_t id = idr[kk];
+            const float c = cr[kk];
+            if (id < 0 || id >= a.vocab || c == 0.0f) continue;
+            fma8(acc, c, *reinterpret_cast<const uint4*>(a.W + (int64_t)id * a.hidden + h));
+        }
+        store_row8(acc, a.dH_acc != nullptr ? a.dH_acc + row * a.hidden + h : nullptr,
+                   a.dH != nullptr ? a.dH + row * a.hidden + h : nullptr);
+    }
+}
+
+// counts[v] = number of (row, candidate) entries with id v.
+__global__ void cand_count_kernel(const int32_t* ids, int64_t nk, int64_t vocab, int32_t* counts) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nk;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t id = ids[i];
+        if (id >= 0 && id < vocab) atomicAdd(counts + id, 1);
+    }
+}
+
+// offsets[v] = sum_{u < v} counts[u] for v = 0..vocab (one workgroup).
+__global__ __launch_bounds__(1024) void exclusive_scan_kernel(const int32_t* counts, int64_t vocab,
+                                                              int32_t* offsets) {
+    __shared__ int32_t part[1024];
+    const int t = threadIdx.x;
+    const int64_t per = (vocab + 1023) / 1024;
+    const int64_t b = t * per, e = (b + per) < vocab ? (b + per) : vocab;
+    int32_t s = 0;
+    for (int64_t v = b; v < e; ++v) s += counts[v];
+    part[t] = s;
+    __syncthreads();
+    // inclusive Hillis-Steele scan of the 1024 partial sums
+    for (int o = 1; o < 1024; o <<= 1) {
+        const int32_t add = t >= o ? part[t - o] : 0;
+        __syncthreads();
+        part[t] += add;
+        __syncthreads();
+    }
+    int32_t run = t > 0 ? part[t - 1] : 0;
+    for (int64_t v = b; v < e; ++v) {
+        offsets[v] = run;
+        run += counts[v];
+    }
+    if (t == 1023) offsets[vocab] = part[1023];
+}
+
+// list[offsets[id] + slot] = entry index i = row * k + candidate; the slot
+// order inside a bucket is arbitrary here and fixed by bucket_sort_kernel.
+__global__ void cand_fill_kernel(const int32_t* ids, int64_t nk, int64_t vocab, const int32_t* offsets,
+                                 int32_t* cursor, int32_t* list) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nk;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t id = ids[i];
+        if (id >= 0 && id < vocab) list[offsets[id] + atomicAdd(cursor + id, 1)] = (int32_t)i;
+    }
+}
+
+// Sort each bucket ascending (insertion sort; buckets hold few entries).
+__global__ void bucket_sort_kernel(const int32_t* offsets, int64_t vocab, int32_t* list) {
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < vocab;
+         v += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t b = offsets[v], e = offsets[v + 1];
+        for (int32_t i = b + 1; i < e; ++i) {
+            const int32_t x = list[i];
+            int32_t j = i - 1;
+            while (j >= b && list[j] > x) {
+                list[j + 1] = list[j];
+                --j;
+            }
+            list[j + 1] = x;
+        }
+    }
+}
+
+// dW[v] = sum over the entries (n, k) with id_nk = v, in ascending (n, k)
+// order, of c_nk H[n]; rows no candidate lists get 0. One wave per row v.
+__global__ __launch_bounds__(kThreads) void cand_dw_kernel(CandBwdArgs a) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t v = (int64_t)blockIdx.x * kWaves + wave;
+    if (v >= a.vocab) return;
+    const int32_t b = a.offsets[v], e = a.offsets[v + 1];
+    for (int64_t h = lane * 8; h < a.hidden; h += kSeg) {
+        float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        for (int32_t j = b; j < e; ++j) {
+            const int32_t i = a.list[j];
+            const float c = a.coef_c[i];
+            if (c == 0.0f) continue;
+            const int64_t n = i / a.k;
+            fma8(acc, c, *reinterpret_cast<const uint4*>(a.H + n * a.hidden + h));
+        }
+        store_row8(acc, a.dW_acc != nullptr ? a.dW_acc + v * a.hidden + h : nullptr,
+                   a.dW != nullptr ? a.dW + v * a.hidden + h : nullptr);
+    }
+}
+
+}  // namespace lmhead

@@ -14,6 +14,9 @@ constexpr int kEntryCeMean = 0;
 constexpr int kEntryCeSum = 1;
 constexpr int kEntryLogprob = 2;
 constexpr int kEntrySupport = 3;
+constexpr int kEntrySupportKl = 4;
+
+constexpr int kMaxCandidates = 1024;   // candidates per row, support entries
 
 // int32 words at the start of every workspace
 constexpr int kHdrErrCode = 0;
@@ -59,6 +62,7 @@ struct FinalizeArgs {
     float* lse;             // [n]
     float* row_out;         // CE: loss rows; logprob: logp [n]; support: lp [n, k]
     float* kl;              // support: [n] or null
+    int padded;             // support: a negative id is a padding slot
     Temperature T;
 };
 
@@ -75,6 +79,7 @@ struct CoeffArgs {
     int64_t num_valid;
     float* coef_a;   // [n_pad]
     float* coef_c;   // [n, k]
+    int padded;      // support: a negative id is a padding slot
     Temperature T;
 };
 
@@ -115,6 +120,35 @@ struct DhArgs {
     bf16_bits* dH;         // [n, hidden] or null
 };
 
+// KL-only support entry (candidate gathers, lmhead_candidates.hip)
+struct CandFwdArgs {
+    const bf16_bits* H;
+    const bf16_bits* W;
+    int64_t n, hidden, vocab;
+    int k;
+    int padded;              // a negative id is a padding slot
+    const int32_t* ids;      // [n, k]
+    const float* ref_logq;   // [n, k]
+    float* kl;               // [n]
+    float* logp_hat;         // [n, k] or null
+    Temperature T;
+};
+
+struct CandBwdArgs {
+    const bf16_bits* H;
+    const bf16_bits* W;
+    int64_t n, hidden, vocab;
+    int k;
+    const int32_t* ids;      // [n, k]
+    const float* coef_c;     // [n, k]: dL/dz at the candidates (0 for padding and bad rows)
+    bf16_bits* dH;           // [n, hidden] or null
+    float* dH_acc;           // caller's fp32 [n, hidden] (+=) or null
+    bf16_bits* dW;           // [vocab, hidden] or null
+    float* dW_acc;           // caller's fp32 [vocab, hidden] (+=) or null
+    const int32_t* offsets;  // [vocab + 1]: bucket v is list[offsets[v] .. offsets[v + 1])
+    const int32_t* list;     // entries i = row * k + candidate, ascending in each bucket
+};
+
 __global__ void init_header_kernel(int32_t* hdr);
 __global__ void scan_labels_kernel(const int32_t* ids, int64_t n, int k, int64_t vocab, int support,
                                    Temperature T, int32_t* hdr);
@@ -127,6 +161,14 @@ __global__ void coeffs_kernel(CoeffArgs a);
 __global__ void bwd_logit_grad_kernel(LogitGradArgs a);
 __global__ void bwd_dw_kernel(DwArgs a);
 __global__ void bwd_dh_kernel(DhArgs a);
+__global__ void cand_kl_fwd_kernel(CandFwdArgs a);
+__global__ void cand_dh_kernel(CandBwdArgs a);
+__global__ void cand_count_kernel(const int32_t* ids, int64_t nk, int64_t vocab, int32_t* counts);
+__global__ void exclusive_scan_kernel(const int32_t* counts, int64_t vocab, int32_t* offsets);
+__global__ void cand_fill_kernel(const int32_t* ids, int64_t nk, int64_t vocab, const int32_t* offsets,
+                                 int32_t* cursor, int32_t* list);
+__global__ void bucket_sort_kernel(const int32_t* offsets, int64_t vocab, int32_t* list);
+__global__ void cand_dw_kernel(CandBwdArgs a);
 __global__ void f32_to_bf16_kernel(const float* in, int64_t count, bf16_bits* out);
 __global__ void transpose_kernel(const bf16_bits* in, int64_t ld_in, int64_t rows, int64_t cols,
                                  bf16_bits* out, int64_t rows_pad);

@@ -36,7 +36,8 @@ __global__ void init_header_kernel(int32_t* hdr) {
 
 // Count valid rows (0 <= t < V) and record data errors. Labels: any negative
 // value is an ignored row, t >= V is an error (miles-ext-kernels PR #14, the
-// commit declaring the lm_head op). Candidate ids must lie in [0, V).
+// commit declaring the lm_head op). Candidate ids (support = 1) must lie in
+// [0, V); in padded lists (support = 2) a negative id is a padding slot.
 __global__ void scan_labels_kernel(const int32_t* ids, int64_t n, int k, int64_t vocab,
                                    int support, Temperature T, int32_t* hdr) {
     __shared__ int32_t s_count, s_row, s_code;
@@ -57,7 +58,7 @@ __global__ void scan_labels_kernel(const int32_t* ids, int64_t n, int k, int64_t
             const int32_t* r = ids + row * k;
             for (int kk = 0; kk < k; ++kk) {
                 const int64_t id = r[kk];
-                if (id < 0 || id >= vocab) {
+                if (id >= vocab || (id < 0 && support != 2)) {
                     code |= kDevErrCandidate;
                     row_min = row_min < row ? row_min : (int32_t)row;
                 }
@@ -192,17 +193,18 @@ __global__ void finalize_rows_kernel(FinalizeArgs a) {
         a.row_out[row] = bad ? quiet_nan() : out;
         return;
     }
-    // support entry
+    // support entry; in padded lists a negative id is a padding slot (lp = 0,
+    // no part in p_hat or the KL)
     const int k = a.k;
     const int32_t* idr = a.ids + row * k;
     const float* zc = a.zg + row * k;
     bool bad = bad_tau;
     for (int kk = 0; kk < k; ++kk) {
         const int64_t id = idr[kk];
-        bad = bad || id < 0 || id >= a.vocab;
+        bad = bad || id >= a.vocab || (id < 0 && !a.padded);
     }
     float* lp = a.row_out + row * k;
-    for (int kk = 0; kk < k; ++kk) lp[kk] = bad ? quiet_nan() : zc[kk] - lse;
+    for (int kk = 0; kk < k; ++kk) lp[kk] = bad ? quiet_nan() : (idr[kk] < 0 ? 0.0f : zc[kk] - lse);
     if (a.kl != nullptr) {
         if (bad) {
             a.kl[row] = quiet_nan();
@@ -210,15 +212,17 @@ __global__ void finalize_rows_kernel(FinalizeArgs a) {
         }
         // log p_hat_k = z_k - log sum_j exp z_j over the listed candidates
         float mx = neg_inf();
-        for (int kk = 0; kk < k; ++kk) mx = fmaxf(mx, zc[kk]);
+        for (int kk = 0; kk < k; ++kk)
+            if (idr[kk] >= 0) mx = fmaxf(mx, zc[kk]);
         float se = 0.0f;
-        for (int kk = 0; kk < k; ++kk) se += expf(zc[kk] - mx);
+        for (int kk = 0; kk < k; ++kk)
+            if (idr[kk] >= 0) se += expf(zc[kk] - mx);
         const float ls = mx + logf(se);
         const float* r = a.ref_logq + row * k;
         float kl = 0.0f;
         for (int kk = 0; kk < k; ++kk) {
             const float q = expf(r[kk]);
-            if (q > 0.0f) kl += q * (r[kk] - (zc[kk] - ls));
+            if (idr[kk] >= 0 && q > 0.0f) kl += q * (r[kk] - (zc[kk] - ls));
         }
         a.kl[row] = kl;
     }
@@ -293,7 +297,7 @@ __global__ void coeffs_kernel(CoeffArgs a) {
     bool bad = !good_tau;
     for (int kk = 0; kk < k; ++kk) {
         const int64_t id = idr[kk];
-        bad = bad || id < 0 || id >= a.vocab;
+        bad = bad || id >= a.vocab || (id < 0 && !a.padded);
     }
     float* c = a.coef_c + row * k;
     if (bad) {
@@ -304,7 +308,7 @@ __global__ void coeffs_kernel(CoeffArgs a) {
     const float* g = a.grad != nullptr ? a.grad + row * k : nullptr;
     float gsum = 0.0f;
     for (int kk = 0; kk < k; ++kk) {
-        const float gk = g ? g[kk] : 0.0f;
+        const float gk = (g != nullptr && idr[kk] >= 0) ? g[kk] : 0.0f;
         gsum += gk;
         c[kk] = gk;
     }
@@ -314,14 +318,17 @@ __global__ void coeffs_kernel(CoeffArgs a) {
         const float* lp = a.saved_lp + row * k;
         const float* r = a.ref_logq + row * k;
         float mx = neg_inf();
-        for (int kk = 0; kk < k; ++kk) mx = fmaxf(mx, lp[kk]);
+        for (int kk = 0; kk < k; ++kk)
+            if (idr[kk] >= 0) mx = fmaxf(mx, lp[kk]);
         float se = 0.0f, Q = 0.0f;
         for (int kk = 0; kk < k; ++kk) {
+            if (idr[kk] < 0) continue;
             se += expf(lp[kk] - mx);
             Q += expf(r[kk]);
         }
         const float inv = 1.0f / se;
         for (int kk = 0; kk < k; ++kk) {
+            if (idr[kk] < 0) continue;
             const float phat = expf(lp[kk] - mx) * inv;
             c[kk] += beta * (Q * phat - expf(r[kk]));
         }

@@ -78,14 +78,24 @@ enum lmhead_entry {
     LMHEAD_ENTRY_CE_MEAN = 0,  /* mean cross-entropy over valid rows */
     LMHEAD_ENTRY_CE_SUM = 1,   /* summed cross-entropy over valid rows */
     LMHEAD_ENTRY_LOGPROB = 2,  /* per-token log-probability of the label */
-    LMHEAD_ENTRY_SUPPORT = 3   /* log-probabilities of K candidates + KL */
+    LMHEAD_ENTRY_SUPPORT = 3,  /* log-probabilities of K candidates (+ KL) */
+    LMHEAD_ENTRY_SUPPORT_KL = 4 /* KL over the K candidates only (no vocabulary-wide pass) */
 };
 
-/* Device error codes recorded in the workspace's error word. */
+/* Problem flags. */
+enum lmhead_flags {
+    /* Support entries: candidate lists are padded; a negative id marks a padding
+     * slot, which has lp = log p_hat = 0 and takes no part in the
+     * renormalisation, the KL or the gradients. Without it a negative id is a
+     * data error. */
+    LMHEAD_FLAG_PADDED_IDS = 1
+};
+
+/* Device error codes recorded in the workspace's error word (bits). */
 enum lmhead_device_error {
     LMHEAD_DEVERR_NONE = 0,
     LMHEAD_DEVERR_LABEL = 1,     /* a label >= vocab ([PR14-op]) */
-    LMHEAD_DEVERR_CANDIDATE = 2, /* a candidate id outside [0, vocab) */
+    LMHEAD_DEVERR_CANDIDATE = 2, /* a candidate id >= vocab, or < 0 in unpadded lists */
     LMHEAD_DEVERR_TEMPERATURE = 4 /* a per-row temperature that is not positive and finite */
 };
 
@@ -103,9 +113,9 @@ enum lmhead_device_error {
  *   num_valid  -1: count valid rows (0 <= label < vocab) on the device,
  *              with no host synchronisation; >= 0: use this value verbatim as
  *              the CE mean's denominator ("given counts", [PR14-tests]).
- *   k          candidates per row for LMHEAD_ENTRY_SUPPORT (1..1024);
- *              ignored by the other entries.
- *   flags      reserved, must be 0.
+ *   k          candidates per row for the support entries (1..1024; the
+ *              KL-only entry also needs n * k < 2^31); ignored by the others.
+ *   flags      0, or LMHEAD_FLAG_PADDED_IDS with a support entry.
  *   temperature     scalar temperature t applied to every row; 0 = off
  *                   (t = 1). Must be finite and >= 0.
  *   reserved        must be 0.
@@ -224,6 +234,40 @@ int lmhead_support_logprob_kl(const lmhead_problem* p,
                               const void* H, const void* W, const int32_t* ids,
                               const float* ref_logq, float* lp, float* kl, float* lse,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Support-set log-probabilities without the KL ([PR8059]: the entries
+ * support_logprob and support_kl are separate): lmhead_support_logprob_kl
+ * with ref_logq = kl = NULL. Backward: lmhead_loss_bwd with
+ * LMHEAD_ENTRY_SUPPORT, grad_kl = NULL.
+ */
+int lmhead_support_logprob(const lmhead_problem* p,
+                           const void* H, const void* W, const int32_t* ids,
+                           float* lp, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * KL-only support entry ([PR8059] support_kl; "forward KL",
+ * "candidate-restricted"): KL(q || p_hat) per row, where p_hat renormalises
+ * the model over the row's k candidates. Neither the KL nor its gradient
+ * depends on logits outside the candidates, so this entry computes only the
+ * n * k candidate logits z = H[n] . W[id] (fp32 sums of bf16 products, in a
+ * fixed order) and never makes a vocabulary-wide pass.
+ *   p->k, ids, ref_logq  as for lmhead_support_logprob_kl (ref_logq required).
+ *   kl         device, fp32 [n].
+ *   logp_hat   device, fp32 [n, k] or NULL: log p_hat (0 at padding slots),
+ *              the state lmhead_loss_bwd needs (as saved_lp).
+ *   workspace  >= lmhead_workspace_size(p, LMHEAD_ENTRY_SUPPORT_KL, 0) bytes.
+ * Backward: lmhead_loss_bwd / lmhead_loss_bwd_accumulate with
+ * LMHEAD_ENTRY_SUPPORT_KL, saved_lp = logp_hat, grad = NULL, lse unused
+ * (may be NULL), grad_kl = dL/dKL [n]; dH and dW are gathers over the
+ * candidates (dW: each vocabulary row sums its (row, candidate) entries in
+ * ascending order; rows no list names get 0).
+ */
+int lmhead_support_kl(const lmhead_problem* p,
+                      const void* H, const void* W, const int32_t* ids,
+                      const float* ref_logq, float* kl, float* logp_hat,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Backward of any entry: recompute each vocabulary chunk's logits, form

@@ -32,6 +32,7 @@ def test_library_exports_every_declared_symbol():
     assert names == sorted([
         "lmhead_loss_bwd", "lmhead_loss_bwd_accumulate", "lmhead_loss_fwd", "lmhead_logprob",
         "lmhead_memory_report", "lmhead_plan_chunk", "lmhead_read_device_error",
+        "lmhead_support_kl", "lmhead_support_logprob",
         "lmhead_status_string", "lmhead_support_logprob_kl", "lmhead_workspace_size"])
     L = ctypes.CDLL(lm.LIB_PATH)
     for name in names:
@@ -164,3 +165,36 @@ def test_python_layer_rejects_cpu_tensors():
     t = torch.zeros(4, dtype=torch.int32)
     with pytest.raises(ValueError):
         lm.ce_loss(H, W, t, chunk=256)
+
+
+def test_support_split_and_padding_host_checks():
+    ws = lm.lmhead_workspace_size
+    # the padding flag belongs to the support entries only
+    assert ws(_p(flags=lm.FLAG_PADDED_IDS), lm.ENTRY_CE_MEAN, 0) == 0
+    assert ws(_p(flags=lm.FLAG_PADDED_IDS, k=8), lm.ENTRY_SUPPORT, 1) > 0
+    assert ws(_p(flags=2, k=8), lm.ENTRY_SUPPORT, 0) == 0
+    # KL-only: a small forward workspace, no chunk-sized backward buffers
+    kl_f = ws(_p(k=8), lm.ENTRY_SUPPORT_KL, 0)
+    kl_b = ws(_p(k=8), lm.ENTRY_SUPPORT_KL, 1)
+    assert 0 < kl_f <= 256 < kl_b < ws(_p(k=8), lm.ENTRY_SUPPORT, 1)
+    assert ws(_p(k=8, chunk=512), lm.ENTRY_SUPPORT_KL, 1) == kl_b
+    assert ws(_p(k=0), lm.ENTRY_SUPPORT_KL, 0) == 0
+    assert ws(_p(n=1 << 22, k=1024), lm.ENTRY_SUPPORT_KL, 0) == 0      # n * k >= 2^31
+    assert ws(_p(n=1 << 22, k=1024), lm.ENTRY_SUPPORT, 0) > 0
+    pk = _p(k=8)
+    f = lm.lmhead_support_kl
+    assert f(pk, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, BIG, 0) == lm.LMHEAD_ERR_ARG   # ref_logq
+    assert f(pk, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, BIG, 0) == lm.LMHEAD_ERR_ARG   # kl
+    assert f(pk, FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, BIG, 0) == lm.LMHEAD_ERR_ALIGN
+    assert f(pk, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0) == lm.LMHEAD_ERR_WORKSPACE
+    g = lm.lmhead_support_logprob
+    assert g(pk, FAKE, FAKE, FAKE, None, FAKE, FAKE, BIG, 0) == lm.LMHEAD_ERR_ARG          # lp
+    b = lm.lmhead_loss_bwd
+    # the KL-only backward takes no lp gradient and needs the saved log p_hat
+    assert b(pk, lm.ENTRY_SUPPORT_KL, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+             FAKE, BIG, 0) == lm.LMHEAD_ERR_ARG
+    assert b(pk, lm.ENTRY_SUPPORT_KL, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, FAKE,
+             FAKE, BIG, 0) == lm.LMHEAD_ERR_ARG
+    r = lm.memory_report(64, 256, 1024, 256, lm.ENTRY_SUPPORT_KL, True, 8)
+    assert r["partials_bytes"] == r["dz_chunk_bytes"] == r["operand_copy_bytes"] == 0
+    assert r["caller_output_bytes"] == 4 * 64 * 8 + 4 * 64 + 2 * 64 * 256 + 2 * 1024 * 256
