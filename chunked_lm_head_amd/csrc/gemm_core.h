@@ -10,9 +10,14 @@
 // is written in both layouts).
 //
 // Waves are laid out 2 x 2; each wave owns a 128 x 128 sub-tile, i.e. 4 x 4
-// blocks of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane).
-// K advances 64 at a time through two LDS stages of 64 KB (A and B tiles of
-// 256 x 64 bf16 each), filled by direct global -> LDS loads (no VGPR staging).
+// blocks of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane, in
+// AGPRs). K advances 64 at a time through two LDS stages of 64 KB (A and B
+// tiles of 256 x 64 bf16 each). Global data reaches LDS through registers:
+// each wave holds two more K steps in flight in VGPRs (2 x 64 registers), so
+// a load has about one and a half K steps to return before it is needed —
+// with only two 64 KB LDS stages, loads straight into LDS could be issued at
+// most one step ahead, and the waves then spent about a third of their time
+// waiting for them.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -33,11 +38,14 @@ constexpr int kStageBytes = 2 * kOperandBytes;      // 64 KB
 constexpr int kMainLdsBytes = 2 * kStageBytes;      // 128 KB
 constexpr int kEpiStride = kTile + 4;               // fp32 staging: floats per column
 constexpr int kEpiLdsBytes = 128 * kEpiStride * 4;  // one 128-column half, [col][row]
-constexpr int kLdsBytes = kMainLdsBytes > kEpiLdsBytes ? kMainLdsBytes : kEpiLdsBytes;
+constexpr int kRowStride = 128 + 8;                 // fp32 staging: floats per row, [row][col]
+constexpr int kRowLdsBytes = kTile * kRowStride * 4;   // one 128-column half, [row][col]
+constexpr int kLdsBytes0 = kMainLdsBytes > kEpiLdsBytes ? kMainLdsBytes : kEpiLdsBytes;
+constexpr int kLdsBytes = kLdsBytes0 > kRowLdsBytes ? kLdsBytes0 : kRowLdsBytes;
 constexpr int kGroupM = 8;                   // row tiles per group in the tile order
 
-// Row-major bf16 operand with K contiguous; rows beyond `rows` are clamped to
-// the last row (their products land in masked output rows / columns).
+// Row-major bf16 operand with K contiguous; rows at or beyond `rows` read as
+// zero (their products land in masked output rows / columns).
 struct Operand {
     const bf16_bits* ptr;
     int64_t ld;
@@ -75,119 +83,159 @@ __device__ __forceinline__ bf16x8 lds_fragment(const char* base, int row, int q)
     return *reinterpret_cast<const bf16x8*>(base + row * 128 + ((q ^ swizzle(row)) << 4));
 }
 
-// One direct global -> LDS load (16 bytes per lane, 1 KB per wave) of stage
-// data: u = 0..7 load eight rows of A, u = 8..15 eight rows of B. Wave w owns
-// rows [64 w, 64 w + 64) of both operands. The lanes of one instruction write
-// 1 KB of LDS contiguously (lane l at offset 16 l), so lane l fetches the
-// global chunk that belongs at that swizzled position.
-__device__ __forceinline__ void stage_load(const Operand& A, int64_t m0, const Operand& B, int64_t n0,
-                                           int64_t k0, char* stage, int wave, int lane, int u) {
-    const Operand& op = u < 8 ? A : B;
-    const int64_t row0 = u < 8 ? m0 : n0;
+// ------------------------------------------------------------------------
+// The K loop.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer load of one 16-byte chunk per lane. The descriptor starts at the
+// tile's first row and ends at the operand's last row, so rows past the end
+// read as zero (no clamping). voff: the lane's byte offset within an 8-row
+// group; soff: the group's byte offset plus the K offset (uniform).
+__device__ __forceinline__ u32x4_t stage_fetch_b(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, 0));
+}
+
+// Staging chunk u of a wave (u = 0..7: eight rows of A, 8..15: of B; wave w
+// owns rows [64 w, 64 w + 64)) into its swizzled LDS position.
+__device__ __forceinline__ void stage_put(char* stage, int wave, int lane, int u, const u32x4_t& v) {
     char* base = stage + (u < 8 ? 0 : kOperandBytes);
-    const int i = u & 7;
-    const int r = wave * 64 + i * 8 + (lane >> 3);
+    const int r = wave * 64 + (u & 7) * 8 + (lane >> 3);
     const int q = (lane & 7) ^ swizzle(r);
-    int64_t row = row0 + r;
-    row = row < op.rows ? row : op.rows - 1;
-    const bf16_bits* g = op.ptr + row * op.ld + k0 + q * 8;
-    __builtin_amdgcn_global_load_lds((const void*)g,
-                                     (__attribute__((address_space(3))) void*)(base + (wave * 64 + i * 8) * 128),
-                                     16, 0, 0);
+    *reinterpret_cast<u32x4_t*>(base + r * 128 + (q << 4)) = v;
+}
+
+struct PgCtx {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    uint32_t voff_a, voff_b;     // lane offsets (bytes) within an 8-row group, wave's rows included
+    uint32_t step_a, step_b;     // bytes per 8 rows
+    int64_t KT;
+    char* smem;
+    int wave, lane, arow, brow, qh;
+};
+
+__device__ __forceinline__ u32x4_t pg_fetch(const PgCtx& c, int64_t k0, int u) {
+    const uint32_t kb = (uint32_t)(k0 * 2);
+    if (u < 8) return stage_fetch_b(c.ra, c.voff_a, (uint32_t)(u & 7) * c.step_a + kb);
+    return stage_fetch_b(c.rb, c.voff_b, (uint32_t)(u & 7) * c.step_b + kb);
+}
+
+// One 64-wide K step kt of parity P (four 16-wide substeps of 16 MFMAs).
+// Register set [1 - P] holds step kt+1, whose first half went to LDS in the
+// previous step; set [P] holds step kt+2 (loads in flight).
+//   substep 0: the second half of step kt+1 goes to LDS (one store per two MFMAs);
+//   substeps 1-2: loads for step kt+3 into set [1 - P] (one per two MFMAs);
+//   every other MFMA is followed by one fragment read for the next substep;
+//   the stage barrier sits in the middle of substep 3; after it, step kt+1's
+//   first fragments are read and step kt+2's first half is stored into the
+//   LDS buffer step kt has just released.
+// The compiler's vmcnt waits before each store are per register, so only the
+// oldest loads are waited for. sched_barrier pins the order.
+template <int P>
+__device__ __forceinline__ void pg_step(const PgCtx& c, int64_t kt, floatx16 (&acc)[4][4], bf16x8 (&fa)[2][4],
+                                        bf16x8 (&fb)[2][4], u32x4_t (&s0)[16], u32x4_t (&s1)[16]) {
+    u32x4_t (&sn)[16] = P ? s0 : s1;    // step kt+1, then kt+3
+    u32x4_t (&sf)[16] = P ? s1 : s0;    // step kt+2
+    const char* cur = c.smem + P * kStageBytes;
+    char* nxt = c.smem + (1 - P) * kStageBytes;
+    const int64_t k3 = (kt + 3 < c.KT ? kt + 3 : c.KT - 1) * kTileK;
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) {
+        const int cb = ks & 1;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int i = t >> 2, j = t & 3;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][i], fb[cb][j], acc[i][j], 0, 0, 0);
+            if (ks == 0 && (t & 1) == 0) stage_put(nxt, c.wave, c.lane, 8 + (t >> 1), sn[8 + (t >> 1)]);
+            if (ks > 0 && (t & 1) == 0) {
+                const int u = (ks - 1) * 8 + (t >> 1);
+                sn[u] = pg_fetch(c, k3, u);
+            }
+            if (t & 1) {
+                const int r = t >> 1;
+                if (r & 1) fb[cb ^ 1][r >> 1] = lds_fragment(cur + kOperandBytes, c.brow + 32 * (r >> 1), (ks + 1) * 2 + c.qh);
+                else fa[cb ^ 1][r >> 1] = lds_fragment(cur, c.arow + 32 * (r >> 1), (ks + 1) * 2 + c.qh);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int i = t >> 2, j = t & 3;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 8; t < 16; ++t) {
+        const int i = t >> 2, j = t & 3;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][j], acc[i][j], 0, 0, 0);
+        const int r = t - 8;
+        if (r & 1) fb[0][r >> 1] = lds_fragment(nxt + kOperandBytes, c.brow + 32 * (r >> 1), c.qh);
+        else fa[0][r >> 1] = lds_fragment(nxt, c.arow + 32 * (r >> 1), c.qh);
+        // step kt+2's first half into the buffer step kt just released
+        stage_put(c.smem + P * kStageBytes, c.wave, c.lane, t - 8, sf[t - 8]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // acc[i][j] covers rows wr*128 + 32 i .. +32 and columns wc*128 + 32 j .. +32 of
 // the tile. Lane l, register e of a 32x32 block holds row 8*(e/4) + 4*(l/32) +
-// e%4 and column l%32.
-//
-// Schedule of one 64-wide K step (four 16-wide substeps of 16 MFMAs each):
-// every other MFMA is followed by one fragment read for the next substep and
-// every fourth by one stage load for step kt+1, so LDS reads and the global ->
-// LDS traffic run under the MFMAs. The stage barrier sits in the middle of the
-// last substep: after it, step kt+1's fragments are read and step kt+2's loads
-// start into the buffer step kt just finished with, which gives every load a
-// full step of latency cover. sched_barrier pins this order.
-__device__ __forceinline__ void gemm_mainloop(const Operand& A, int64_t m0, const Operand& B,
-                                              int64_t n0, int64_t K, char* smem,
-                                              floatx16 (&acc)[4][4]) {
+// e%4 and column l%32. K must be a multiple of 64.
+__device__ __forceinline__ void gemm_mainloop_pg(const Operand& A, int64_t m0, const Operand& B, int64_t n0,
+                                                 int64_t K, char* smem, floatx16 (&acc)[4][4]) {
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wr = wave >> 1, wc = wave & 1;
+    PgCtx c;
+    c.KT = K / kTileK;
+    c.smem = smem;
+    c.lane = tid & 63;
+    c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    c.arow = (c.wave >> 1) * 128 + (c.lane & 31);
+    c.brow = (c.wave & 1) * 128 + (c.lane & 31);
+    c.qh = c.lane >> 5;
+    {
+        const int64_t ra_rows = A.rows - m0 < kTile ? A.rows - m0 : kTile;
+        const int64_t rb_rows = B.rows - n0 < kTile ? B.rows - n0 : kTile;
+        c.ra = __builtin_amdgcn_make_buffer_rsrc((void*)(A.ptr + m0 * A.ld), 0, (int)(ra_rows * A.ld * 2), 0x00020000);
+        c.rb = __builtin_amdgcn_make_buffer_rsrc((void*)(B.ptr + n0 * B.ld), 0, (int)(rb_rows * B.ld * 2), 0x00020000);
+        const int r = c.wave * 64 + (c.lane >> 3);
+        c.voff_a = (uint32_t)((r * A.ld + (c.lane & 7) * 8) * 2);
+        c.voff_b = (uint32_t)((r * B.ld + (c.lane & 7) * 8) * 2);
+        c.step_a = (uint32_t)(8 * A.ld * 2);
+        c.step_b = (uint32_t)(8 * B.ld * 2);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    const int64_t KT = K / kTileK;
-    const int arow = wr * 128 + (lane & 31);
-    const int brow = wc * 128 + (lane & 31);
-    const int qh = lane >> 5;
-
-    // prologue: step 0 resident, the first quarter of step 1 in flight, step 0's first fragments
+    auto kof = [&](int64_t s) { return (s < c.KT ? s : c.KT - 1) * kTileK; };
+    u32x4_t s0[16], s1[16];
+    // prologue: step 0 -> set 0 -> LDS buffer 0; step 1 -> set 1 (first half to LDS buffer 1); step 2 -> set 0
 #pragma unroll
-    for (int u = 0; u < 16; ++u) stage_load(A, m0, B, n0, 0, smem, wave, lane, u);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    for (int u = 0; u < 16; ++u) s0[u] = pg_fetch(c, kof(0), u);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) s1[u] = pg_fetch(c, kof(1), u);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) stage_put(smem, c.wave, c.lane, u, s0[u]);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) s0[u] = pg_fetch(c, kof(2), u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) stage_put(smem + kStageBytes, c.wave, c.lane, u, s1[u]);
     __syncthreads();
-    const int64_t k1 = (KT > 1 ? 1 : 0) * kTileK;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) stage_load(A, m0, B, n0, k1, smem + kStageBytes, wave, lane, u);
     bf16x8 fa[2][4], fb[2][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        fa[0][i] = lds_fragment(smem, arow + 32 * i, qh);
-        fb[0][i] = lds_fragment(smem + kOperandBytes, brow + 32 * i, qh);
+        fa[0][i] = lds_fragment(smem, c.arow + 32 * i, c.qh);
+        fb[0][i] = lds_fragment(smem + kOperandBytes, c.brow + 32 * i, c.qh);
     }
-
-    for (int64_t kt = 0; kt < KT; ++kt) {
-        const char* cur = smem + (kt & 1) * kStageBytes;
-        char* nxt = smem + ((kt + 1) & 1) * kStageBytes;    // step kt+1
-        char* nxt2 = smem + (kt & 1) * kStageBytes;         // step kt+2, after the barrier
-        // past the end, loads repeat the last step into the idle buffer (never read)
-        const int64_t kn1 = (kt + 1 < KT ? kt + 1 : KT - 1) * kTileK;
-        const int64_t kn2 = (kt + 2 < KT ? kt + 2 : KT - 1) * kTileK;
-#pragma unroll
-        for (int ks = 0; ks < 3; ++ks) {
-            const int c = ks & 1;
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const int i = t >> 2, j = t & 3;
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][j], acc[i][j], 0, 0, 0);
-                if ((t & 3) == 0) stage_load(A, m0, B, n0, kn1, nxt, wave, lane, 4 + ks * 4 + (t >> 2));
-                if (t & 1) {
-                    const int r = t >> 1;   // fa0 fb0 fa1 fb1 ...
-                    if (r & 1)
-                        fb[c ^ 1][r >> 1] = lds_fragment(cur + kOperandBytes, brow + 32 * (r >> 1), (ks + 1) * 2 + qh);
-                    else
-                        fa[c ^ 1][r >> 1] = lds_fragment(cur, arow + 32 * (r >> 1), (ks + 1) * 2 + qh);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int i = t >> 2, j = t & 3;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][j], acc[i][j], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 8; t < 16; ++t) {
-            const int i = t >> 2, j = t & 3;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][j], acc[i][j], 0, 0, 0);
-            const int r = t - 8;
-            if (r & 1)
-                fb[0][r >> 1] = lds_fragment(nxt + kOperandBytes, brow + 32 * (r >> 1), qh);
-            else
-                fa[0][r >> 1] = lds_fragment(nxt, arow + 32 * (r >> 1), qh);
-            if ((t & 1) == 0) stage_load(A, m0, B, n0, kn2, nxt2, wave, lane, (t - 8) >> 1);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+    int64_t kt = 0;
+    for (; kt + 1 < c.KT; kt += 2) {
+        pg_step<0>(c, kt, acc, fa, fb, s0, s1);
+        pg_step<1>(c, kt + 1, acc, fa, fb, s0, s1);
     }
-    // the trailing loads land before the epilogue reuses the LDS
+    if (kt < c.KT) pg_step<0>(c, kt, acc, fa, fb, s0, s1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 }
@@ -210,6 +258,24 @@ __device__ __forceinline__ void stage_half(float* S, const floatx16 (&acc)[4][4]
                 v[2] = acc[i][j][4 * g + 2];
                 v[3] = acc[i][j][4 * g + 3];
                 *reinterpret_cast<floatx4*>(S + col * kEpiStride + row) = v;
+            }
+}
+
+// The same half tile laid out [row 0..255][column 0..127] with a row stride of
+// kRowStride floats (8 mod 64 banks: the two row groups one 32-bit store
+// instruction writes, 4 rows apart, fall 32 banks apart). Afterwards 32 lanes
+// can read one row's 128 values as float4s, conflict-free, for coalesced
+// row-major global traffic.
+__device__ __forceinline__ void stage_half_rows(float* S, const floatx16 (&acc)[4][4], int wr, int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = wr * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                const int col = j * 32 + (lane & 31);
+                S[row * kRowStride + col] = acc[i][j][e];
             }
 }
 

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTilesArgs a) 
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
 
     floatx16 acc[4][4];
-    gemm_mainloop(Operand{a.H, a.hidden, a.n}, m0, Operand{a.W, a.hidden, a.vocab}, n0, a.hidden,
+    gemm_mainloop_pg(Operand{a.H, a.hidden, a.n}, m0, Operand{a.W, a.hidden, a.vocab}, n0, a.hidden,
                   smem, acc);
 
     float* S = reinterpret_cast<float*>(smem);
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
 
     floatx16 acc[4][4];
-    gemm_mainloop(Operand{a.H, a.hidden, a.n}, m0, Operand{a.Wc, a.hidden, a.width}, n0, a.hidden,
+    gemm_mainloop_pg(Operand{a.H, a.hidden, a.n}, m0, Operand{a.Wc, a.hidden, a.width}, n0, a.hidden,
                   smem, acc);
 
     float* S = reinterpret_cast<float*>(smem);
@@ -379,17 +379,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
             }
         }
         __syncthreads();
-        if (a.G != nullptr) {
-            // row-major copy: thread = row, 16-byte stores of 8 columns
-            bf16_bits* g = a.G + row * a.w_pad + col0;
-            for (int c8 = 0; c8 < 16; ++c8) {
-                uint32_t w[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    w[i] = pack_bf16x2(Sr[(c8 * 8 + 2 * i) * kEpiStride], Sr[(c8 * 8 + 2 * i + 1) * kEpiStride]);
-                *reinterpret_cast<uint4*>(g + c8 * 8) = make_uint4(w[0], w[1], w[2], w[3]);
-            }
-        }
         if (a.Gt != nullptr) {
             // transposed copy: 32 lanes cover one column's 256 rows (8 rows, 16 bytes each)
             const int rg = tid & 31;
@@ -400,6 +389,33 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
                 const uint4 v = make_uint4(pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w),
                                            pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w));
                 *reinterpret_cast<uint4*>(a.Gt + (col0 + c) * a.n_pad + m0 + rg * 8) = v;
+            }
+        }
+        if (a.G != nullptr) {
+            // row-major copy, 64 columns at a time: each thread packs its row's
+            // values to bf16 in registers, the rows go back to LDS as [row][64]
+            // (16-byte chunk q of row r at q ^ ((r >> 1) & 7), over columns
+            // 0..31 of S, which are consumed), and 8 lanes then store one row's
+            // 128 contiguous bytes
+            uint16_t* Gl = reinterpret_cast<uint16_t*>(smem);
+#pragma unroll 1
+            for (int q = 0; q < 2; ++q) {
+                uint32_t w[32];
+#pragma unroll
+                for (int i = 0; i < 32; ++i)
+                    w[i] = pack_bf16x2(Sr[(q * 64 + 2 * i) * kEpiStride], Sr[(q * 64 + 2 * i + 1) * kEpiStride]);
+                __syncthreads();
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    *reinterpret_cast<uint4*>(Gl + tid * 64 + ((j ^ swizzle(tid)) << 3)) =
+                        make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
+                __syncthreads();
+                for (int it = 0; it < 8; ++it) {
+                    const int r = wave * 64 + it * 8 + (lane >> 3);
+                    const int ch = lane & 7;
+                    const uint4 v = *reinterpret_cast<const uint4*>(Gl + r * 64 + ((ch ^ swizzle(r)) << 3));
+                    *reinterpret_cast<uint4*>(a.G + (m0 + r) * a.w_pad + col0 + q * 64 + ch * 8) = v;
+                }
             }
         }
         __syncthreads();
@@ -416,42 +432,36 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dw_kernel(DwArgs a) {
     map_tile(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
     floatx16 acc[4][4];
-    gemm_mainloop(Operand{a.Gt, a.n_pad, a.w_pad}, m0, Operand{a.Ht, a.n_pad, a.hidden}, n0, a.n_pad,
+    gemm_mainloop_pg(Operand{a.Gt, a.n_pad, a.w_pad}, m0, Operand{a.Ht, a.n_pad, a.hidden}, n0, a.n_pad,
                   smem, acc);
     float* S = reinterpret_cast<float*>(smem);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
-    const int64_t v = m0 + tid;   // chunk-local vocabulary row
-    const float* Sr = S + tid;
+    // 32 lanes per dW row (4 columns each), two rows per wave and step: coalesced
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
-        if (wc == half) stage_half(S, acc, wr, lane);
+        if (wc == half) stage_half_rows(S, acc, wr, lane);
         __syncthreads();
-        const int64_t h0 = n0 + half * 128;
-        if (v < a.width && a.dw_acc == nullptr) {
-            bf16_bits* out = a.dW + (a.v0 + v) * a.hidden + h0;
-            for (int c8 = 0; c8 < 16; ++c8) {
-                if (h0 + c8 * 8 >= a.hidden) break;
-                uint32_t w[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    w[i] = pack_bf16x2(Sr[(c8 * 8 + 2 * i) * kEpiStride], Sr[(c8 * 8 + 2 * i + 1) * kEpiStride]);
-                *reinterpret_cast<uint4*>(out + c8 * 8) = make_uint4(w[0], w[1], w[2], w[3]);
-            }
-        } else if (v < a.width) {
-            const int64_t o = (a.v0 + v) * a.hidden + h0;
-            for (int c4 = 0; c4 < 32; ++c4) {
-                if (h0 + c4 * 4 >= a.hidden) break;
-                const float4 p = *reinterpret_cast<const float4*>(a.dw_acc + o + c4 * 4);
-                float4 x;
-                x.x = p.x + Sr[(c4 * 4 + 0) * kEpiStride];
-                x.y = p.y + Sr[(c4 * 4 + 1) * kEpiStride];
-                x.z = p.z + Sr[(c4 * 4 + 2) * kEpiStride];
-                x.w = p.w + Sr[(c4 * 4 + 3) * kEpiStride];
-                *reinterpret_cast<float4*>(a.dw_acc + o + c4 * 4) = x;
+        const int c = 4 * (lane & 31);
+        const int64_t h = n0 + half * 128 + c;
+        for (int it = 0; it < 32; ++it) {
+            const int r = wave * 64 + it * 2 + (lane >> 5);
+            const int64_t v = m0 + r;   // chunk-local vocabulary row
+            if (v >= a.width || h >= a.hidden) continue;
+            const float4 x = *reinterpret_cast<const float4*>(S + r * kRowStride + c);
+            const int64_t o = (a.v0 + v) * a.hidden + h;
+            if (a.dw_acc == nullptr) {
+                *reinterpret_cast<uint2*>(a.dW + o) = make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
+            } else {
+                const float4 p = *reinterpret_cast<const float4*>(a.dw_acc + o);
+                float4 y;
+                y.x = p.x + x.x;
+                y.y = p.y + x.y;
+                y.z = p.z + x.z;
+                y.w = p.w + x.w;
+                *reinterpret_cast<float4*>(a.dw_acc + o) = y;
                 if (a.dW != nullptr)
-                    *reinterpret_cast<uint2*>(a.dW + o + c4 * 4) =
-                        make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
+                    *reinterpret_cast<uint2*>(a.dW + o) = make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
             }
         }
         __syncthreads();
@@ -468,38 +478,35 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(DhArgs a) {
     map_tile(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
     floatx16 acc[4][4];
-    gemm_mainloop(Operand{a.G, a.w_pad, a.n_pad}, m0, Operand{a.Wt, a.w_pad, a.hidden}, n0, a.w_pad,
+    gemm_mainloop_pg(Operand{a.G, a.w_pad, a.n_pad}, m0, Operand{a.Wt, a.w_pad, a.hidden}, n0, a.w_pad,
                   smem, acc);
     float* S = reinterpret_cast<float*>(smem);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
-    const int64_t r = m0 + tid;
-    const float* Sr = S + tid;
+    // 32 lanes per row (4 columns each), two rows per wave and step: the fp32
+    // read-modify-write of dh_acc is coalesced
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
-        if (wc == half) stage_half(S, acc, wr, lane);
+        if (wc == half) stage_half_rows(S, acc, wr, lane);
         __syncthreads();
-        const int64_t h0 = n0 + half * 128;
-        if (r < a.n) {
-            const int64_t o = r * a.hidden + h0;
-            for (int c4 = 0; c4 < 32; ++c4) {
-                if (h0 + c4 * 4 >= a.hidden) break;
-                float4 v = make_float4(Sr[(c4 * 4 + 0) * kEpiStride], Sr[(c4 * 4 + 1) * kEpiStride],
-                                       Sr[(c4 * 4 + 2) * kEpiStride], Sr[(c4 * 4 + 3) * kEpiStride]);
-                if (!a.first) {
-                    const float4 p = *reinterpret_cast<const float4*>(a.dh_acc + o + c4 * 4);
-                    v.x = p.x + v.x;
-                    v.y = p.y + v.y;
-                    v.z = p.z + v.z;
-                    v.w = p.w + v.w;
-                }
-                if (a.last && a.dH != nullptr) {
-                    const uint32_t lo = pack_bf16x2(v.x, v.y);
-                    const uint32_t hi = pack_bf16x2(v.z, v.w);
-                    *reinterpret_cast<uint2*>(a.dH + o + c4 * 4) = make_uint2(lo, hi);
-                }
-                if (!a.last || a.keep_acc) *reinterpret_cast<float4*>(a.dh_acc + o + c4 * 4) = v;
+        const int c = 4 * (lane & 31);
+        const int64_t h = n0 + half * 128 + c;
+        for (int it = 0; it < 32; ++it) {
+            const int r = wave * 64 + it * 2 + (lane >> 5);
+            const int64_t row = m0 + r;
+            if (row >= a.n || h >= a.hidden) continue;
+            float4 v = *reinterpret_cast<const float4*>(S + r * kRowStride + c);
+            const int64_t o = row * a.hidden + h;
+            if (!a.first) {
+                const float4 p = *reinterpret_cast<const float4*>(a.dh_acc + o);
+                v.x = p.x + v.x;
+                v.y = p.y + v.y;
+                v.z = p.z + v.z;
+                v.w = p.w + v.w;
             }
+            if (a.last && a.dH != nullptr)
+                *reinterpret_cast<uint2*>(a.dH + o) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+            if (!a.last || a.keep_acc) *reinterpret_cast<float4*>(a.dh_acc + o) = v;
         }
         __syncthreads();
     }
