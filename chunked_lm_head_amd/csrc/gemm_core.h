@@ -9,8 +9,8 @@
 // (the host-side plan transposes H and the W chunk once, and the dL/dz tile
 // is written in both layouts).
 //
-// Waves are laid out 2 x 2; each wave owns a 128 x 128 sub-tile, i.e. 4 x 4
-// blocks of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane, in
+// Waves are laid out 2 x 2; each wave owns a 128 x 128 sub-tile, i.e. 8 x 8
+// blocks of v_mfma_f32_16x16x32_bf16 (256 fp32 accumulators per lane, in
 // AGPRs). K advances 64 at a time through two LDS stages of 64 KB (A and B
 // tiles of 256 x 64 bf16 each). Global data reaches LDS through registers:
 // each wave holds two more K steps in flight in VGPRs (2 x 64 registers), so
@@ -27,7 +27,6 @@ namespace lmhead {
 
 typedef uint16_t bf16_bits;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
@@ -38,7 +37,7 @@ constexpr int kStageBytes = 2 * kOperandBytes;      // 64 KB
 constexpr int kMainLdsBytes = 2 * kStageBytes;      // 128 KB
 constexpr int kEpiStride = kTile + 4;               // fp32 staging: floats per column
 constexpr int kEpiLdsBytes = 128 * kEpiStride * 4;  // one 128-column half, [col][row]
-constexpr int kRowStride = 128 + 8;                 // fp32 staging: floats per row, [row][col]
+constexpr int kRowStride = 128 + 4;                 // fp32 staging: floats per row, [row][col]
 constexpr int kRowLdsBytes = kTile * kRowStride * 4;   // one 128-column half, [row][col]
 constexpr int kLdsBytes0 = kMainLdsBytes > kEpiLdsBytes ? kMainLdsBytes : kEpiLdsBytes;
 constexpr int kLdsBytes = kLdsBytes0 > kRowLdsBytes ? kLdsBytes0 : kRowLdsBytes;
@@ -52,18 +51,19 @@ struct Operand {
     int64_t rows;
 };
 
-// Workgroup id -> (row tile, column tile). Workgroups are dispatched
-// round-robin over the 8 XCDs, so id i runs on XCD i % 8. Each XCD is given a
-// contiguous range of the logical tile order, and that order walks kGroupM row
-// tiles for each column tile: the workgroups resident on one XCD at a time
-// share A and B tiles in that XCD's L2. The mapping is a bijection that
-// depends only on the grid shape.
-__device__ __forceinline__ void map_tile(int64_t bid, int64_t tiles_m, int64_t tiles_n,
-                                         int64_t& tm, int64_t& tn) {
-    const int64_t total = tiles_m * tiles_n;
+// Workgroups are dispatched round-robin over the 8 XCDs, so id i runs on XCD
+// i % 8. xcd_order gives each XCD a contiguous range of a logical tile order
+// (a bijection of [0, total) that depends only on total); group_tile walks
+// that order kGroupM row tiles per column tile, so the workgroups resident on
+// one XCD at a time share A and B tiles in that XCD's L2.
+__device__ __forceinline__ int64_t xcd_order(int64_t bid, int64_t total) {
     const int64_t q = total / 8, r = total % 8;
     const int64_t x = bid % 8, j = bid / 8;
-    const int64_t L = x * q + (x < r ? x : r) + j;
+    return x * q + (x < r ? x : r) + j;
+}
+
+__device__ __forceinline__ void group_tile(int64_t L, int64_t tiles_m, int64_t tiles_n, int64_t& tm,
+                                           int64_t& tn) {
     const int64_t group = (int64_t)kGroupM * tiles_n;
     const int64_t g = L / group;
     const int64_t first_m = g * kGroupM;
@@ -71,6 +71,12 @@ __device__ __forceinline__ void map_tile(int64_t bid, int64_t tiles_m, int64_t t
     const int64_t in = L - g * group;
     tm = first_m + in % gm;
     tn = in / gm;
+}
+
+// Workgroup id -> (row tile, column tile) of one GEMM.
+__device__ __forceinline__ void map_tile(int64_t bid, int64_t tiles_m, int64_t tiles_n,
+                                         int64_t& tm, int64_t& tn) {
+    group_tile(xcd_order(bid, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
 }
 
 // LDS tile layout: a tile row is 64 bf16 = 128 B = eight 16-byte chunks. The
@@ -110,7 +116,7 @@ struct PgCtx {
     uint32_t step_a, step_b;     // bytes per 8 rows
     int64_t KT;
     char* smem;
-    int wave, lane, arow, brow, qh;
+    int wave, lane;
 };
 
 __device__ __forceinline__ u32x4_t pg_fetch(const PgCtx& c, int64_t k0, int u) {
@@ -119,80 +125,103 @@ __device__ __forceinline__ u32x4_t pg_fetch(const PgCtx& c, int64_t k0, int u) {
     return stage_fetch_b(c.rb, c.voff_b, (uint32_t)(u & 7) * c.step_b + kb);
 }
 
-// One 64-wide K step kt of parity P (four 16-wide substeps of 16 MFMAs).
-// Register set [1 - P] holds step kt+1, whose first half went to LDS in the
-// previous step; set [P] holds step kt+2 (loads in flight).
-//   substep 0: the second half of step kt+1 goes to LDS (one store per two MFMAs);
-//   substeps 1-2: loads for step kt+3 into set [1 - P] (one per two MFMAs);
-//   every other MFMA is followed by one fragment read for the next substep;
-//   the stage barrier sits in the middle of substep 3; after it, step kt+1's
-//   first fragments are read and step kt+2's first half is stored into the
-//   LDS buffer step kt has just released.
-// The compiler's vmcnt waits before each store are per register, so only the
-// oldest loads are waited for. sched_barrier pins the order.
+// The accumulators: each wave's 128 x 128 sub-tile as 8 x 8 blocks of
+// v_mfma_f32_16x16x32_bf16 (block (i, j) covers rows wr*128 + 16 i .. +16 and
+// columns wc*128 + 16 j .. +16; lane l, register e holds row 4*(l/16) + e and
+// column l%16 of its block). 256 fp32 per lane, in AGPRs. The 16x16x32 form
+// moves half as many accumulator bytes per flop as 32x32x16 and sustains a
+// higher clock under the board's power limit.
+typedef floatx4 AccTile[8][8];
+
+// acc += a * b in place. Issued from inline assembly because the compiler,
+// given 64 separate accumulator quads, otherwise copies them between AGPRs
+// around every MFMA. The hazard recognizer does not see these MFMAs: each
+// accumulator is reused only 64 MFMAs later, A / B registers are overwritten
+// only by LDS reads (whose data returns long after the MFMA has read its
+// operands), and mma_drain() separates the last MFMA from any read of acc.
+__device__ __forceinline__ void mma16(floatx4& acc, const bf16x8& a, const bf16x8& b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mma_drain() { asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory"); }
+
+// Fragment of 16 rows x 32 k for substep s of a stage: lane l reads row
+// rb + l % 16, 16-byte chunk 4 s + l / 16.
+__device__ __forceinline__ bf16x8 frag16(const char* base, int rb, int s, int lane) {
+    const int row = rb + (lane & 15);
+    const int q = 4 * s + (lane >> 4);
+    return *reinterpret_cast<const bf16x8*>(base + row * 128 + ((q ^ swizzle(row)) << 4));
+}
+
+// One 64-wide K step kt of parity P: two 32-wide substeps of 64 MFMAs, each
+// in two passes (columns blocks 0-3, then 4-7). Fragments are single
+// buffered: during pass 1 the substep's B blocks 4-7 are read; during pass 2
+// each A block is re-read for the next substep right after its last use, and B
+// blocks 0-3 too. Register set [1 - P] holds step kt+1 and set [P] step kt+2
+// (loads in flight): over the first 96 MFMAs, chunk u of step kt+1 is stored
+// to the LDS buffer that step kt-1 released and its registers are at once
+// reloaded with chunk u of step kt+3 (16 evenly spaced store / load pairs, two
+// full K steps of latency cover per chunk; the compiler's vmcnt wait before
+// each store is per register). The stage barrier sits between the passes of
+// the second substep; the reads after it fetch step kt+1's first fragments.
+// sched_barrier pins the order.
 template <int P>
-__device__ __forceinline__ void pg_step(const PgCtx& c, int64_t kt, floatx16 (&acc)[4][4], bf16x8 (&fa)[2][4],
-                                        bf16x8 (&fb)[2][4], u32x4_t (&s0)[16], u32x4_t (&s1)[16]) {
+__device__ __forceinline__ void pg_step(const PgCtx& c, int64_t kt, AccTile& acc, bf16x8 (&fa)[8], bf16x8 (&fb)[8],
+                                        u32x4_t (&s0)[16], u32x4_t (&s1)[16]) {
     u32x4_t (&sn)[16] = P ? s0 : s1;    // step kt+1, then kt+3
-    u32x4_t (&sf)[16] = P ? s1 : s0;    // step kt+2
     const char* cur = c.smem + P * kStageBytes;
     char* nxt = c.smem + (1 - P) * kStageBytes;
     const int64_t k3 = (kt + 3 < c.KT ? kt + 3 : c.KT - 1) * kTileK;
+    const int ar = (c.wave >> 1) * 128, br = (c.wave & 1) * 128;
 #pragma unroll
-    for (int ks = 0; ks < 3; ++ks) {
-        const int cb = ks & 1;
+    for (int s = 0; s < 2; ++s) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const int i = t >> 2, j = t & 3;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][i], fb[cb][j], acc[i][j], 0, 0, 0);
-            if (ks == 0 && (t & 1) == 0) stage_put(nxt, c.wave, c.lane, 8 + (t >> 1), sn[8 + (t >> 1)]);
-            if (ks > 0 && (t & 1) == 0) {
-                const int u = (ks - 1) * 8 + (t >> 1);
-                sn[u] = pg_fetch(c, k3, u);
-            }
-            if (t & 1) {
-                const int r = t >> 1;
-                if (r & 1) fb[cb ^ 1][r >> 1] = lds_fragment(cur + kOperandBytes, c.brow + 32 * (r >> 1), (ks + 1) * 2 + c.qh);
-                else fa[cb ^ 1][r >> 1] = lds_fragment(cur, c.arow + 32 * (r >> 1), (ks + 1) * 2 + c.qh);
-            }
+        for (int t = 0; t < 32; ++t) {
+            const int bi = t >> 2, bj = t & 3;
+            mma16(acc[bi][bj], fa[bi], fb[bj]);
+            if ((t & 7) == 1) fb[4 + (t >> 3)] = frag16(cur + kOperandBytes, br + 16 * (4 + (t >> 3)), s, c.lane);
+            const int pos = s * 64 + t;
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (u * 6 == pos) {
+                    stage_put(nxt, c.wave, c.lane, u, sn[u]);
+                    sn[u] = pg_fetch(c, k3, u);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (s == 1) {
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const char* src = s == 0 ? cur : nxt;
+        const int s2 = s == 0 ? 1 : 0;
+#pragma unroll
+        for (int t = 0; t < 32; ++t) {
+            const int bi = t >> 2, bj = 4 + (t & 3);
+            mma16(acc[bi][bj], fa[bi], fb[bj]);
+            if ((t & 3) == 3) fa[bi] = frag16(src, ar + 16 * bi, s2, c.lane);
+            if ((t & 7) == 1) fb[t >> 3] = frag16(src + kOperandBytes, br + 16 * (t >> 3), s2, c.lane);
+            const int pos = s * 64 + 32 + t;
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (u * 6 == pos) {
+                    stage_put(nxt, c.wave, c.lane, u, sn[u]);
+                    sn[u] = pg_fetch(c, k3, u);
+                }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const int i = t >> 2, j = t & 3;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][j], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t = 8; t < 16; ++t) {
-        const int i = t >> 2, j = t & 3;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][j], acc[i][j], 0, 0, 0);
-        const int r = t - 8;
-        if (r & 1) fb[0][r >> 1] = lds_fragment(nxt + kOperandBytes, c.brow + 32 * (r >> 1), c.qh);
-        else fa[0][r >> 1] = lds_fragment(nxt, c.arow + 32 * (r >> 1), c.qh);
-        // step kt+2's first half into the buffer step kt just released
-        stage_put(c.smem + P * kStageBytes, c.wave, c.lane, t - 8, sf[t - 8]);
-        __builtin_amdgcn_sched_barrier(0);
-    }
 }
 
-// acc[i][j] covers rows wr*128 + 32 i .. +32 and columns wc*128 + 32 j .. +32 of
-// the tile. Lane l, register e of a 32x32 block holds row 8*(e/4) + 4*(l/32) +
-// e%4 and column l%32. K must be a multiple of 64.
-__device__ __forceinline__ void gemm_mainloop_pg(const Operand& A, int64_t m0, const Operand& B, int64_t n0,
-                                                 int64_t K, char* smem, floatx16 (&acc)[4][4]) {
+// C[m0.., n0..] = A[m0.., :K] B[n0.., :K]^T for one 256 x 256 tile. K must
+// be a multiple of 64.
+__device__ __forceinline__ void gemm_mainloop(const Operand& A, int64_t m0, const Operand& B, int64_t n0,
+                                              int64_t K, char* smem, AccTile& acc) {
     const int tid = threadIdx.x;
     PgCtx c;
     c.KT = K / kTileK;
     c.smem = smem;
     c.lane = tid & 63;
     c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    c.arow = (c.wave >> 1) * 128 + (c.lane & 31);
-    c.brow = (c.wave & 1) * 128 + (c.lane & 31);
-    c.qh = c.lane >> 5;
     {
         const int64_t ra_rows = A.rows - m0 < kTile ? A.rows - m0 : kTile;
         const int64_t rb_rows = B.rows - n0 < kTile ? B.rows - n0 : kTile;
@@ -205,14 +234,14 @@ __device__ __forceinline__ void gemm_mainloop_pg(const Operand& A, int64_t m0, c
         c.step_b = (uint32_t)(8 * B.ld * 2);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
     auto kof = [&](int64_t s) { return (s < c.KT ? s : c.KT - 1) * kTileK; };
     u32x4_t s0[16], s1[16];
-    // prologue: step 0 -> set 0 -> LDS buffer 0; step 1 -> set 1 (first half to LDS buffer 1); step 2 -> set 0
+    // prologue: step 0 -> set 0 -> LDS buffer 0; step 1 -> set 1 (stored during step 0); step 2 -> set 0
 #pragma unroll
     for (int u = 0; u < 16; ++u) s0[u] = pg_fetch(c, kof(0), u);
 #pragma unroll
@@ -221,21 +250,20 @@ __device__ __forceinline__ void gemm_mainloop_pg(const Operand& A, int64_t m0, c
     for (int u = 0; u < 16; ++u) stage_put(smem, c.wave, c.lane, u, s0[u]);
 #pragma unroll
     for (int u = 0; u < 16; ++u) s0[u] = pg_fetch(c, kof(2), u);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) stage_put(smem + kStageBytes, c.wave, c.lane, u, s1[u]);
     __syncthreads();
-    bf16x8 fa[2][4], fb[2][4];
+    bf16x8 fa[8], fb[8];
+    const int ar = (c.wave >> 1) * 128, br = (c.wave & 1) * 128;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        fa[0][i] = lds_fragment(smem, c.arow + 32 * i, c.qh);
-        fb[0][i] = lds_fragment(smem + kOperandBytes, c.brow + 32 * i, c.qh);
-    }
+    for (int i = 0; i < 8; ++i) fa[i] = frag16(smem, ar + 16 * i, 0, c.lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = frag16(smem + kOperandBytes, br + 16 * j, 0, c.lane);
     int64_t kt = 0;
     for (; kt + 1 < c.KT; kt += 2) {
         pg_step<0>(c, kt, acc, fa, fb, s0, s1);
         pg_step<1>(c, kt + 1, acc, fa, fb, s0, s1);
     }
     if (kt < c.KT) pg_step<0>(c, kt, acc, fa, fb, s0, s1);
+    mma_drain();
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 }
@@ -243,38 +271,31 @@ __device__ __forceinline__ void gemm_mainloop_pg(const Operand& A, int64_t m0, c
 // Write the accumulators of the waves whose column half is `half` into the
 // fp32 staging area S laid out [column 0..127][row 0..255] (stride kEpiStride):
 // afterwards thread t can walk row t of that half with conflict-free reads.
-__device__ __forceinline__ void stage_half(float* S, const floatx16 (&acc)[4][4], int wr, int lane) {
+__device__ __forceinline__ void stage_half(float* S, const AccTile& acc, int wr, int lane) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int col = j * 32 + (lane & 31);
-                const int row = wr * 128 + i * 32 + 8 * g + 4 * (lane >> 5);
-                floatx4 v;
-                v[0] = acc[i][j][4 * g + 0];
-                v[1] = acc[i][j][4 * g + 1];
-                v[2] = acc[i][j][4 * g + 2];
-                v[3] = acc[i][j][4 * g + 3];
-                *reinterpret_cast<floatx4*>(S + col * kEpiStride + row) = v;
-            }
+        for (int j = 0; j < 8; ++j) {
+            const int col = j * 16 + (lane & 15);
+            const int row = wr * 128 + i * 16 + 4 * (lane >> 4);
+            *reinterpret_cast<floatx4*>(S + col * kEpiStride + row) = acc[i][j];
+        }
 }
 
 // The same half tile laid out [row 0..255][column 0..127] with a row stride of
-// kRowStride floats (8 mod 64 banks: the two row groups one 32-bit store
-// instruction writes, 4 rows apart, fall 32 banks apart). Afterwards 32 lanes
+// kRowStride floats (4 mod 64 banks: the four row groups one 32-bit store
+// instruction writes, 4 rows apart, fall 16 banks apart). Afterwards 32 lanes
 // can read one row's 128 values as float4s, conflict-free, for coalesced
 // row-major global traffic.
-__device__ __forceinline__ void stage_half_rows(float* S, const floatx16 (&acc)[4][4], int wr, int lane) {
+__device__ __forceinline__ void stage_half_rows(float* S, const AccTile& acc, int wr, int lane) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = wr * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                const int col = j * 32 + (lane & 31);
+            for (int e = 0; e < 4; ++e) {
+                const int row = wr * 128 + i * 16 + 4 * (lane >> 4) + e;
+                const int col = j * 16 + (lane & 15);
                 S[row * kRowStride + col] = acc[i][j][e];
             }
 }

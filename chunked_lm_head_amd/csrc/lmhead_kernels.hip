@@ -92,8 +92,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTilesArgs a) 
     map_tile(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
 
-    floatx16 acc[4][4];
-    gemm_mainloop_pg(Operand{a.H, a.hidden, a.n}, m0, Operand{a.W, a.hidden, a.vocab}, n0, a.hidden,
+    AccTile acc;
+    gemm_mainloop(Operand{a.H, a.hidden, a.n}, m0, Operand{a.W, a.hidden, a.vocab}, n0, a.hidden,
                   smem, acc);
 
     float* S = reinterpret_cast<float*>(smem);
@@ -346,8 +346,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
     map_tile(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
 
-    floatx16 acc[4][4];
-    gemm_mainloop_pg(Operand{a.H, a.hidden, a.n}, m0, Operand{a.Wc, a.hidden, a.width}, n0, a.hidden,
+    AccTile acc;
+    gemm_mainloop(Operand{a.H, a.hidden, a.n}, m0, Operand{a.Wc, a.hidden, a.width}, n0, a.hidden,
                   smem, acc);
 
     float* S = reinterpret_cast<float*>(smem);
@@ -431,8 +431,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dw_kernel(DwArgs a) {
     int64_t tm, tn;
     map_tile(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
-    floatx16 acc[4][4];
-    gemm_mainloop_pg(Operand{a.Gt, a.n_pad, a.w_pad}, m0, Operand{a.Ht, a.n_pad, a.hidden}, n0, a.n_pad,
+    AccTile acc;
+    gemm_mainloop(Operand{a.Gt, a.n_pad, a.w_pad}, m0, Operand{a.Ht, a.n_pad, a.hidden}, n0, a.n_pad,
                   smem, acc);
     float* S = reinterpret_cast<float*>(smem);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -477,8 +477,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(DhArgs a) {
     int64_t tm, tn;
     map_tile(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
-    floatx16 acc[4][4];
-    gemm_mainloop_pg(Operand{a.G, a.w_pad, a.n_pad}, m0, Operand{a.Wt, a.w_pad, a.hidden}, n0, a.w_pad,
+    AccTile acc;
+    gemm_mainloop(Operand{a.G, a.w_pad, a.n_pad}, m0, Operand{a.Wt, a.w_pad, a.hidden}, n0, a.w_pad,
                   smem, acc);
     float* S = reinterpret_cast<float*>(smem);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
