@@ -154,9 +154,9 @@ __device__ __forceinline__ bf16x8 frag16(const char* base, int rb, int s, int la
 
 // One 64-wide K step kt of parity P: two 32-wide substeps of 64 MFMAs, each
 // in two passes (columns blocks 0-3, then 4-7). Fragments are single
-// buffered: during pass 1 the substep's B blocks 4-7 are read; during pass 2
-// each A block is re-read for the next substep right after its last use, and B
-// blocks 0-3 too. Register set [1 - P] holds step kt+1 and set [P] step kt+2
+// buffered: early in pass 1 the substep's B blocks 4-7 are read; early in pass
+// 2 the next substep's B blocks 0-3, and each A block for the next substep
+// right after its last use. Register set [1 - P] holds step kt+1 and set [P] step kt+2
 // (loads in flight): over the first 96 MFMAs, chunk u of step kt+1 is stored
 // to the LDS buffer that step kt-1 released and its registers are at once
 // reloaded with chunk u of step kt+3 (16 evenly spaced store / load pairs, two
@@ -178,7 +178,7 @@ __device__ __forceinline__ void pg_step(const PgCtx& c, int64_t kt, AccTile& acc
         for (int t = 0; t < 32; ++t) {
             const int bi = t >> 2, bj = t & 3;
             mma16(acc[bi][bj], fa[bi], fb[bj]);
-            if ((t & 7) == 1) fb[4 + (t >> 3)] = frag16(cur + kOperandBytes, br + 16 * (4 + (t >> 3)), s, c.lane);
+            if ((t & 1) && t < 8) fb[4 + (t >> 1)] = frag16(cur + kOperandBytes, br + 16 * (4 + (t >> 1)), s, c.lane);
             const int pos = s * 64 + t;
 #pragma unroll
             for (int u = 0; u < 16; ++u)
@@ -199,7 +199,7 @@ __device__ __forceinline__ void pg_step(const PgCtx& c, int64_t kt, AccTile& acc
             const int bi = t >> 2, bj = 4 + (t & 3);
             mma16(acc[bi][bj], fa[bi], fb[bj]);
             if ((t & 3) == 3) fa[bi] = frag16(src, ar + 16 * bi, s2, c.lane);
-            if ((t & 7) == 1) fb[t >> 3] = frag16(src + kOperandBytes, br + 16 * (t >> 3), s2, c.lane);
+            if ((t & 1) && t < 8) fb[t >> 1] = frag16(src + kOperandBytes, br + 16 * (t >> 1), s2, c.lane);
             const int pos = s * 64 + 32 + t;
 #pragma unroll
             for (int u = 0; u < 16; ++u)
