@@ -85,7 +85,6 @@ class lmhead_memory_figures(ctypes.Structure):
         ("forward_bytes", ctypes.c_size_t),
         ("partials_bytes", ctypes.c_size_t),
         ("dz_chunk_bytes", ctypes.c_size_t),
-        ("operand_copy_bytes", ctypes.c_size_t),
         ("dh_acc_bytes", ctypes.c_size_t),
         ("caller_output_bytes", ctypes.c_size_t),
     ]

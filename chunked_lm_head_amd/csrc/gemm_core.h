@@ -2,12 +2,12 @@
 // contraction of the chunked LM-head path.
 //
 // One workgroup = 256 threads = 4 wave64s computes a 256 x 256 fp32 tile
-// C[m0:m0+256, n0:n0+256] = A[m0:, :] * B[n0:, :]^T where both operands are
-// row-major with the contraction dimension K contiguous ("NT" form). The
-// logits GEMM (z = H W^T) is natively NT; the two backward contractions are
-// brought to NT form by giving them operands stored contraction-contiguous
-// (the host-side plan transposes H and the W chunk once, and the dL/dz tile
-// is written in both layouts).
+// C[m0:m0+256, n0:n0+256] = sum_k A[m, k] B[n, k]. Each operand is stored
+// either K-major (row-major [mn][k], the contraction contiguous) or MN-major
+// (row-major [k][mn]). The logits GEMM (z = H W^T) has both operands K-major;
+// dW = G^T H reads G and H MN-major, and dH = G W_c reads W_c MN-major, so no
+// operand is ever transposed in HBM: an MN-major tile is staged in LDS as
+// [k][mn] and its MFMA fragments come from gfx950's transposing LDS reads.
 //
 // Waves are laid out 2 x 2; each wave owns a 128 x 128 sub-tile, i.e. 8 x 8
 // blocks of v_mfma_f32_16x16x32_bf16 (256 fp32 accumulators per lane, in
@@ -32,9 +32,10 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kTile = 256;                   // output tile edge (M and N)
 constexpr int kTileK = 64;                   // K step per LDS stage
-constexpr int kOperandBytes = kTile * kTileK * 2;   // 32 KB
-constexpr int kStageBytes = 2 * kOperandBytes;      // 64 KB
-constexpr int kMainLdsBytes = 2 * kStageBytes;      // 128 KB
+constexpr int kTPitch = 2 * kTile + 32;             // MN-major LDS tile: bytes per k row (512 + pad)
+constexpr int kOperandBytes = kTileK * kTPitch;     // 34 KB slot (a K-major tile uses 32 KB of it)
+constexpr int kStageBytes = 2 * kOperandBytes;      // 68 KB
+constexpr int kMainLdsBytes = 2 * kStageBytes;      // 136 KB
 constexpr int kEpiStride = kTile + 4;               // fp32 staging: floats per column
 constexpr int kEpiLdsBytes = 128 * kEpiStride * 4;  // one 128-column half, [col][row]
 constexpr int kRowStride = 128 + 4;                 // fp32 staging: floats per row, [row][col]
@@ -43,8 +44,12 @@ constexpr int kLdsBytes0 = kMainLdsBytes > kEpiLdsBytes ? kMainLdsBytes : kEpiLd
 constexpr int kLdsBytes = kLdsBytes0 > kRowLdsBytes ? kLdsBytes0 : kRowLdsBytes;
 constexpr int kGroupM = 8;                   // row tiles per group in the tile order
 
-// Row-major bf16 operand with K contiguous; rows at or beyond `rows` read as
-// zero (their products land in masked output rows / columns).
+// Row-major bf16 operand. K-major: element (mn, k) at ptr[mn * ld + k], and
+// rows (mn) at or beyond `rows` read as zero (their products land in masked
+// output rows / columns). MN-major: element (mn, k) at ptr[k * ld + mn], and
+// K rows at or beyond `rows` read as zero; columns past the operand's MN
+// extent read whatever follows in memory (or zero past the K rows' end) and
+// only reach output rows / columns that are masked.
 struct Operand {
     const bf16_bits* ptr;
     int64_t ld;
@@ -102,28 +107,97 @@ __device__ __forceinline__ u32x4_t stage_fetch_b(__amdgpu_buffer_rsrc_t rsrc, ui
 }
 
 // Staging chunk u of a wave (u = 0..7: eight rows of A, 8..15: of B; wave w
-// owns rows [64 w, 64 w + 64)) into its swizzled LDS position.
-__device__ __forceinline__ void stage_put(char* stage, int wave, int lane, int u, const u32x4_t& v) {
-    char* base = stage + (u < 8 ? 0 : kOperandBytes);
+// owns rows [64 w, 64 w + 64)) into its swizzled LDS position: the K-major
+// form, a tile row being 64 k of one mn.
+__device__ __forceinline__ void stage_put(char* base, int wave, int lane, int u, const u32x4_t& v) {
     const int r = wave * 64 + (u & 7) * 8 + (lane >> 3);
     const int q = (lane & 7) ^ swizzle(r);
     *reinterpret_cast<u32x4_t*>(base + r * 128 + (q << 4)) = v;
 }
 
+// MN-major LDS tile: 64 k rows of 256 mn (512 B) at a pitch of kTPitch =
+// 17 x 32 bytes, k row r stored as LDS row trow(r) (bits 2 and 3 of r
+// swapped). A transposing fragment read takes four consecutive k rows per
+// 16-lane group (k = 8 g + 0..3, or + 4..7, for group g) and 32 lanes are
+// served together: the swap makes their eight k rows eight consecutive LDS
+// rows, whose 32-byte pieces at one column then fall in eight distinct bank
+// groups (17 r mod 8). No XOR: every fragment address is one per-lane base
+// plus an immediate offset. Stores (16 lanes, 256 contiguous bytes of one
+// row) are conflict-free.
+__device__ __forceinline__ int trow(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// Staging chunk u of a wave for an MN-major tile: k row 8 (u & 7) + 2 w +
+// lane / 32, bytes 16 (lane % 32) .. + 16 of the row.
+__device__ __forceinline__ void stage_put_t(char* base, int wave, int lane, int u, const u32x4_t& v) {
+    const int r = (u & 7) * 8 + wave * 2 + (lane >> 5);
+    *reinterpret_cast<u32x4_t*>(base + trow(r) * kTPitch + ((lane & 31) << 4)) = v;
+}
+
+// One operand's K stream. K-major: a descriptor over the tile's 256 rows (the
+// K offset goes into the scalar offset). MN-major: the descriptor is rebuilt
+// for each K step over that step's 64 k rows, so offsets stay small and k rows
+// past `krows` read as zero.
+struct OpStream {
+    __amdgpu_buffer_rsrc_t rsrc;  // K-major only
+    const char* base;             // MN-major: address of (k = 0, mn = mn0)
+    int64_t ld_bytes;             // MN-major: bytes per k row
+    int64_t krows;                // MN-major: k rows that exist
+    uint32_t voff;                // lane offset (bytes) within an 8-row group, wave's rows included
+    uint32_t step;                // bytes per 8 rows (K-major) or 8 k rows (MN-major)
+};
+
+template <bool T>
+__device__ __forceinline__ OpStream make_stream(const Operand& X, int64_t mn0, int wave, int lane) {
+    OpStream o;
+    if (!T) {
+        const int64_t rows = X.rows - mn0 < kTile ? X.rows - mn0 : kTile;
+        o.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(X.ptr + mn0 * X.ld), 0, (int)(rows * X.ld * 2),
+                                                   0x00020000);
+        o.base = nullptr;
+        o.ld_bytes = 0;
+        o.krows = 0;
+        const int r = wave * 64 + (lane >> 3);
+        o.voff = (uint32_t)((r * X.ld + (lane & 7) * 8) * 2);
+        o.step = (uint32_t)(8 * X.ld * 2);
+    } else {
+        o.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)X.ptr, 0, 0, 0x00020000);
+        o.base = reinterpret_cast<const char*>(X.ptr + mn0);
+        o.ld_bytes = X.ld * 2;
+        o.krows = X.rows;
+        o.voff = (uint32_t)((wave * 2 + (lane >> 5)) * o.ld_bytes + (lane & 31) * 16);
+        o.step = (uint32_t)(8 * o.ld_bytes);
+    }
+    return o;
+}
+
+// The descriptor for K step kt (k0 = 64 kt).
+template <bool T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t step_rsrc(const OpStream& o, int64_t k0) {
+    if (!T) return o.rsrc;
+    int64_t rows = o.krows - k0;
+    rows = rows < 0 ? 0 : (rows > kTileK ? kTileK : rows);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(o.base + k0 * o.ld_bytes), 0, (int)(rows * o.ld_bytes),
+                                             0x00020000);
+}
+
+template <bool T>
+__device__ __forceinline__ u32x4_t op_fetch(const OpStream& o, __amdgpu_buffer_rsrc_t r, int64_t k0, int u) {
+    if (!T) return stage_fetch_b(r, o.voff, (uint32_t)(u & 7) * o.step + (uint32_t)(k0 * 2));
+    return stage_fetch_b(r, o.voff, (uint32_t)(u & 7) * o.step);
+}
+
+template <bool T>
+__device__ __forceinline__ void op_put(char* base, int wave, int lane, int u, const u32x4_t& v) {
+    if (!T) stage_put(base, wave, lane, u, v);
+    else stage_put_t(base, wave, lane, u, v);
+}
+
 struct PgCtx {
-    __amdgpu_buffer_rsrc_t ra, rb;
-    uint32_t voff_a, voff_b;     // lane offsets (bytes) within an 8-row group, wave's rows included
-    uint32_t step_a, step_b;     // bytes per 8 rows
+    OpStream a, b;
     int64_t KT;
     char* smem;
     int wave, lane;
 };
-
-__device__ __forceinline__ u32x4_t pg_fetch(const PgCtx& c, int64_t k0, int u) {
-    const uint32_t kb = (uint32_t)(k0 * 2);
-    if (u < 8) return stage_fetch_b(c.ra, c.voff_a, (uint32_t)(u & 7) * c.step_a + kb);
-    return stage_fetch_b(c.rb, c.voff_b, (uint32_t)(u & 7) * c.step_b + kb);
-}
 
 // The accumulators: each wave's 128 x 128 sub-tile as 8 x 8 blocks of
 // v_mfma_f32_16x16x32_bf16 (block (i, j) covers rows wr*128 + 16 i .. +16 and
@@ -152,6 +226,29 @@ __device__ __forceinline__ bf16x8 frag16(const char* base, int rb, int s, int la
     return *reinterpret_cast<const bf16x8*>(base + row * 128 + ((q ^ swizzle(row)) << 4));
 }
 
+// The same fragment from an MN-major tile: lane l needs mn = rb + l % 16 and
+// k = 32 s + 8 (l / 16) + 0..7. ds_read_b64_tr_b16 hands lane i of each
+// 16-lane group element i % 4 of the 8-byte piece addressed by lane
+// 4 j + i / 4, as its element j; so lane p of the group addresses k row
+// 32 s + 8 g + p / 4 at mn rb + 4 (p % 4), and a second read 4 k rows further
+// (8 LDS rows on) gives k + 4..7.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+__device__ __forceinline__ bf16x8 frag16_t(const char* base, int rb, int s, int lane) {
+    const int p = lane & 15;
+    const int r = 32 * s + 8 * (lane >> 4) + (p >> 2);
+    const char* a = base + trow(r) * kTPitch + rb * 2 + ((p & 3) << 3);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + 8 * kTPitch));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <bool T>
+__device__ __forceinline__ bf16x8 op_frag(const char* base, int rb, int s, int lane) {
+    if (!T) return frag16(base, rb, s, lane);
+    return frag16_t(base, rb, s, lane);
+}
+
 // One 64-wide K step kt of parity P: two 32-wide substeps of 64 MFMAs, each
 // in two passes (columns blocks 0-3, then 4-7). Fragments are single
 // buffered: early in pass 1 the substep's B blocks 4-7 are read; early in pass
@@ -164,28 +261,37 @@ __device__ __forceinline__ bf16x8 frag16(const char* base, int rb, int s, int la
 // each store is per register). The stage barrier sits between the passes of
 // the second substep; the reads after it fetch step kt+1's first fragments.
 // sched_barrier pins the order.
-template <int P>
+template <bool TA, bool TB, int P>
 __device__ __forceinline__ void pg_step(const PgCtx& c, int64_t kt, AccTile& acc, bf16x8 (&fa)[8], bf16x8 (&fb)[8],
                                         u32x4_t (&s0)[16], u32x4_t (&s1)[16]) {
     u32x4_t (&sn)[16] = P ? s0 : s1;    // step kt+1, then kt+3
     const char* cur = c.smem + P * kStageBytes;
     char* nxt = c.smem + (1 - P) * kStageBytes;
     const int64_t k3 = (kt + 3 < c.KT ? kt + 3 : c.KT - 1) * kTileK;
+    const __amdgpu_buffer_rsrc_t ra3 = step_rsrc<TA>(c.a, k3);
+    const __amdgpu_buffer_rsrc_t rb3 = step_rsrc<TB>(c.b, k3);
     const int ar = (c.wave >> 1) * 128, br = (c.wave & 1) * 128;
+    auto put_fetch = [&](int u) {
+        if (u < 8) {
+            op_put<TA>(nxt, c.wave, c.lane, u, sn[u]);
+            sn[u] = op_fetch<TA>(c.a, ra3, k3, u);
+        } else {
+            op_put<TB>(nxt + kOperandBytes, c.wave, c.lane, u, sn[u]);
+            sn[u] = op_fetch<TB>(c.b, rb3, k3, u);
+        }
+    };
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
         for (int t = 0; t < 32; ++t) {
             const int bi = t >> 2, bj = t & 3;
             mma16(acc[bi][bj], fa[bi], fb[bj]);
-            if ((t & 1) && t < 8) fb[4 + (t >> 1)] = frag16(cur + kOperandBytes, br + 16 * (4 + (t >> 1)), s, c.lane);
+            if ((t & 1) && t < 8)
+                fb[4 + (t >> 1)] = op_frag<TB>(cur + kOperandBytes, br + 16 * (4 + (t >> 1)), s, c.lane);
             const int pos = s * 64 + t;
 #pragma unroll
             for (int u = 0; u < 16; ++u)
-                if (u * 6 == pos) {
-                    stage_put(nxt, c.wave, c.lane, u, sn[u]);
-                    sn[u] = pg_fetch(c, k3, u);
-                }
+                if (u * 6 == pos) put_fetch(u);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (s == 1) {
@@ -198,22 +304,20 @@ __device__ __forceinline__ void pg_step(const PgCtx& c, int64_t kt, AccTile& acc
         for (int t = 0; t < 32; ++t) {
             const int bi = t >> 2, bj = 4 + (t & 3);
             mma16(acc[bi][bj], fa[bi], fb[bj]);
-            if ((t & 3) == 3) fa[bi] = frag16(src, ar + 16 * bi, s2, c.lane);
-            if ((t & 1) && t < 8) fb[t >> 1] = frag16(src + kOperandBytes, br + 16 * (t >> 1), s2, c.lane);
+            if ((t & 3) == 3) fa[bi] = op_frag<TA>(src, ar + 16 * bi, s2, c.lane);
+            if ((t & 1) && t < 8) fb[t >> 1] = op_frag<TB>(src + kOperandBytes, br + 16 * (t >> 1), s2, c.lane);
             const int pos = s * 64 + 32 + t;
 #pragma unroll
             for (int u = 0; u < 16; ++u)
-                if (u * 6 == pos) {
-                    stage_put(nxt, c.wave, c.lane, u, sn[u]);
-                    sn[u] = pg_fetch(c, k3, u);
-                }
+                if (u * 6 == pos) put_fetch(u);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
 
-// C[m0.., n0..] = A[m0.., :K] B[n0.., :K]^T for one 256 x 256 tile. K must
-// be a multiple of 64.
+// C[m0.., n0..] = sum_k A(m, k) B(n, k) for one 256 x 256 tile; TA / TB
+// select the MN-major form of an operand. K must be a multiple of 64.
+template <bool TA, bool TB>
 __device__ __forceinline__ void gemm_mainloop(const Operand& A, int64_t m0, const Operand& B, int64_t n0,
                                               int64_t K, char* smem, AccTile& acc) {
     const int tid = threadIdx.x;
@@ -222,17 +326,8 @@ __device__ __forceinline__ void gemm_mainloop(const Operand& A, int64_t m0, cons
     c.smem = smem;
     c.lane = tid & 63;
     c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    {
-        const int64_t ra_rows = A.rows - m0 < kTile ? A.rows - m0 : kTile;
-        const int64_t rb_rows = B.rows - n0 < kTile ? B.rows - n0 : kTile;
-        c.ra = __builtin_amdgcn_make_buffer_rsrc((void*)(A.ptr + m0 * A.ld), 0, (int)(ra_rows * A.ld * 2), 0x00020000);
-        c.rb = __builtin_amdgcn_make_buffer_rsrc((void*)(B.ptr + n0 * B.ld), 0, (int)(rb_rows * B.ld * 2), 0x00020000);
-        const int r = c.wave * 64 + (c.lane >> 3);
-        c.voff_a = (uint32_t)((r * A.ld + (c.lane & 7) * 8) * 2);
-        c.voff_b = (uint32_t)((r * B.ld + (c.lane & 7) * 8) * 2);
-        c.step_a = (uint32_t)(8 * A.ld * 2);
-        c.step_b = (uint32_t)(8 * B.ld * 2);
-    }
+    c.a = make_stream<TA>(A, m0, c.wave, c.lane);
+    c.b = make_stream<TB>(B, n0, c.wave, c.lane);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -240,29 +335,36 @@ __device__ __forceinline__ void gemm_mainloop(const Operand& A, int64_t m0, cons
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
     auto kof = [&](int64_t s) { return (s < c.KT ? s : c.KT - 1) * kTileK; };
+    auto fetch = [&](int64_t k0, int u) {
+        return u < 8 ? op_fetch<TA>(c.a, step_rsrc<TA>(c.a, k0), k0, u)
+                     : op_fetch<TB>(c.b, step_rsrc<TB>(c.b, k0), k0, u);
+    };
     u32x4_t s0[16], s1[16];
     // prologue: step 0 -> set 0 -> LDS buffer 0; step 1 -> set 1 (stored during step 0); step 2 -> set 0
 #pragma unroll
-    for (int u = 0; u < 16; ++u) s0[u] = pg_fetch(c, kof(0), u);
+    for (int u = 0; u < 16; ++u) s0[u] = fetch(kof(0), u);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) s1[u] = pg_fetch(c, kof(1), u);
+    for (int u = 0; u < 16; ++u) s1[u] = fetch(kof(1), u);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) stage_put(smem, c.wave, c.lane, u, s0[u]);
+    for (int u = 0; u < 16; ++u) {
+        if (u < 8) op_put<TA>(smem, c.wave, c.lane, u, s0[u]);
+        else op_put<TB>(smem + kOperandBytes, c.wave, c.lane, u, s0[u]);
+    }
 #pragma unroll
-    for (int u = 0; u < 16; ++u) s0[u] = pg_fetch(c, kof(2), u);
+    for (int u = 0; u < 16; ++u) s0[u] = fetch(kof(2), u);
     __syncthreads();
     bf16x8 fa[8], fb[8];
     const int ar = (c.wave >> 1) * 128, br = (c.wave & 1) * 128;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) fa[i] = frag16(smem, ar + 16 * i, 0, c.lane);
+    for (int i = 0; i < 8; ++i) fa[i] = op_frag<TA>(smem, ar + 16 * i, 0, c.lane);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[j] = frag16(smem + kOperandBytes, br + 16 * j, 0, c.lane);
+    for (int j = 0; j < 4; ++j) fb[j] = op_frag<TB>(smem + kOperandBytes, br + 16 * j, 0, c.lane);
     int64_t kt = 0;
     for (; kt + 1 < c.KT; kt += 2) {
-        pg_step<0>(c, kt, acc, fa, fb, s0, s1);
-        pg_step<1>(c, kt + 1, acc, fa, fb, s0, s1);
+        pg_step<TA, TB, 0>(c, kt, acc, fa, fb, s0, s1);
+        pg_step<TA, TB, 1>(c, kt + 1, acc, fa, fb, s0, s1);
     }
-    if (kt < c.KT) pg_step<0>(c, kt, acc, fa, fb, s0, s1);
+    if (kt < c.KT) pg_step<TA, TB, 0>(c, kt, acc, fa, fb, s0, s1);
     mma_drain();
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();

@@ -27,7 +27,7 @@ struct Layout {
     // forward regions
     size_t hdr, lse, part, zg, rows;
     // backward regions
-    size_t coef_a, coef_c, Ht, G, Gt, Wt, dh_acc;
+    size_t coef_a, coef_c, G, dh_acc;
     // backward of the KL-only entry: inverse index of the candidate ids
     size_t counts, offsets, cursor, list;
     size_t fwd_total, bwd_total;
@@ -93,10 +93,7 @@ Layout plan(const lmhead_problem& p, int entry) {
     off = after_hdr;
     L.coef_a = take(4 * L.n_pad);
     L.coef_c = take(4 * L.n * L.k);
-    L.Ht = take(2 * L.hidden * L.n_pad);
     L.G = take(2 * L.n_pad * L.w_pad);
-    L.Gt = take(2 * L.w_pad * L.n_pad);
-    L.Wt = take(2 * L.hidden * L.w_pad);
     L.dh_acc = take(4 * L.n * L.hidden);
     L.bwd_total = off > L.fwd_total ? off : L.fwd_total;
     return L;
@@ -310,15 +307,7 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
         return launched();
     }
 
-    bf16_bits* Ht = (bf16_bits*)(w + L.Ht);
     bf16_bits* G = (bf16_bits*)(w + L.G);
-    bf16_bits* Gt = (bf16_bits*)(w + L.Gt);
-    bf16_bits* Wt = (bf16_bits*)(w + L.Wt);
-    if (want_dw) {
-        dim3 grid((unsigned)(L.hidden / 64), (unsigned)(L.n_pad / 64));
-        transpose_kernel<<<grid, kThreads, 0, s>>>((const bf16_bits*)H, L.hidden, L.n, L.hidden, Ht,
-                                                   L.n_pad);
-    }
     const int64_t nchunks = cdiv(L.vocab, L.chunk);
     const int64_t tiles_rows = L.n_pad / kTile;
     const int64_t tiles_hidden = cdiv(L.hidden, kTile);
@@ -345,14 +334,14 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
         ga.ids = ids;
         ga.k = (int)L.k;
         ga.lse = lse;
-        ga.G = want_dh ? G : nullptr;
-        ga.Gt = want_dw ? Gt : nullptr;
+        ga.G = G;
         bwd_logit_grad_kernel<<<(unsigned)(ga.tiles_m * ga.tiles_n), kThreads, 0, s>>>(ga);
 
         if (want_dw) {
             DwArgs da;
-            da.Gt = Gt;
-            da.Ht = Ht;
+            da.G = G;
+            da.H = (const bf16_bits*)H;
+            da.n = L.n;
             da.n_pad = L.n_pad;
             da.hidden = L.hidden;
             da.v0 = v0;
@@ -365,11 +354,10 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
             bwd_dw_kernel<<<(unsigned)(da.tiles_m * da.tiles_n), kThreads, 0, s>>>(da);
         }
         if (want_dh) {
-            dim3 grid((unsigned)(L.hidden / 64), (unsigned)(w_pad / 64));
-            transpose_kernel<<<grid, kThreads, 0, s>>>(Wc, L.hidden, width, L.hidden, Wt, w_pad);
             DhArgs ha;
             ha.G = G;
-            ha.Wt = Wt;
+            ha.Wc = Wc;
+            ha.width = width;
             ha.n = L.n;
             ha.n_pad = L.n_pad;
             ha.hidden = L.hidden;
@@ -412,8 +400,7 @@ int lmhead_memory_report(const lmhead_problem* p, int entry, int with_backward,
     const bool kl_only = entry == LMHEAD_ENTRY_SUPPORT_KL;
     r.partials_bytes = kl_only ? 0 : (size_t)(8 * L.tiles_v * L.n);
     if (with_backward && !kl_only) {
-        r.dz_chunk_bytes = (size_t)(4 * L.n_pad * L.w_pad);
-        r.operand_copy_bytes = (size_t)(2 * L.hidden * L.n_pad + 2 * L.hidden * L.w_pad);
+        r.dz_chunk_bytes = (size_t)(2 * L.n_pad * L.w_pad);
         r.dh_acc_bytes = (size_t)(4 * L.n * L.hidden);
     }
     // fp32 outputs: lse [n] plus loss [1] / logp [n] / lp [n, k] and kl [n]

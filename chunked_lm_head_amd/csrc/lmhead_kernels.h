@@ -94,15 +94,14 @@ struct LogitGradArgs {
     const int32_t* ids;
     int k;
     const float* lse;
-    bf16_bits* G;          // [n_pad, w_pad] or null
-    bf16_bits* Gt;         // [w_pad, n_pad] or null
+    bf16_bits* G;          // [n_pad, w_pad]
     Temperature T;
 };
 
 struct DwArgs {
-    const bf16_bits* Gt;   // [w_pad, n_pad]
-    const bf16_bits* Ht;   // [hidden, n_pad]
-    int64_t n_pad, hidden, v0, width, w_pad;
+    const bf16_bits* G;    // [n_pad, w_pad]
+    const bf16_bits* H;    // [n, hidden]
+    int64_t n, n_pad, hidden, v0, width, w_pad;
     int64_t tiles_m, tiles_n;
     bf16_bits* dW;         // [vocab, hidden] or null
     float* dw_acc;         // caller's fp32 [vocab, hidden] (+=) or null
@@ -110,8 +109,8 @@ struct DwArgs {
 
 struct DhArgs {
     const bf16_bits* G;    // [n_pad, w_pad]
-    const bf16_bits* Wt;   // [hidden, w_pad]
-    int64_t n, n_pad, hidden, w_pad;
+    const bf16_bits* Wc;   // first row of the chunk: [width, hidden]
+    int64_t n, n_pad, hidden, width, w_pad;
     int64_t tiles_m, tiles_n;
     int first;             // chunk 0 of a fresh sum: dh_acc is written, not read
     int last;              // last chunk: the bf16 dH is written (if dH is set)
@@ -170,7 +169,5 @@ __global__ void cand_fill_kernel(const int32_t* ids, int64_t nk, int64_t vocab, 
 __global__ void bucket_sort_kernel(const int32_t* offsets, int64_t vocab, int32_t* list);
 __global__ void cand_dw_kernel(CandBwdArgs a);
 __global__ void f32_to_bf16_kernel(const float* in, int64_t count, bf16_bits* out);
-__global__ void transpose_kernel(const bf16_bits* in, int64_t ld_in, int64_t rows, int64_t cols,
-                                 bf16_bits* out, int64_t rows_pad);
 
 }  // namespace lmhead

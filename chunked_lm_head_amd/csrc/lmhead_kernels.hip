@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTilesArgs a) 
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
 
     AccTile acc;
-    gemm_mainloop(Operand{a.H, a.hidden, a.n}, m0, Operand{a.W, a.hidden, a.vocab}, n0, a.hidden,
+    gemm_mainloop<false, false>(Operand{a.H, a.hidden, a.n}, m0, Operand{a.W, a.hidden, a.vocab}, n0, a.hidden,
                   smem, acc);
 
     float* S = reinterpret_cast<float*>(smem);
@@ -338,8 +338,8 @@ __global__ void coeffs_kernel(CoeffArgs a) {
 
 // Recompute one chunk's logits tile and write dL/dz in bf16: G[n, j] = a_n
 // exp(z - lse_n) for chunk columns j < width, plus c_nk where v0 + j = id_nk;
-// zero elsewhere. G is written row-major [n_pad, w_pad] (operand of dH) and
-// transposed [w_pad, n_pad] (operand of dW).
+// zero elsewhere. G is written row-major [n_pad, w_pad]; it is the K-major
+// operand of dH and the MN-major operand of dW.
 __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
     int64_t tm, tn;
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
 
     AccTile acc;
-    gemm_mainloop(Operand{a.H, a.hidden, a.n}, m0, Operand{a.Wc, a.hidden, a.width}, n0, a.hidden,
+    gemm_mainloop<false, false>(Operand{a.H, a.hidden, a.n}, m0, Operand{a.Wc, a.hidden, a.width}, n0, a.hidden,
                   smem, acc);
 
     float* S = reinterpret_cast<float*>(smem);
@@ -379,18 +379,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
             }
         }
         __syncthreads();
-        if (a.Gt != nullptr) {
-            // transposed copy: 32 lanes cover one column's 256 rows (8 rows, 16 bytes each)
-            const int rg = tid & 31;
-            for (int it = 0; it < 16; ++it) {
-                const int c = it * 8 + (tid >> 5);
-                const float4 lo = *reinterpret_cast<const float4*>(S + c * kEpiStride + rg * 8);
-                const float4 hi = *reinterpret_cast<const float4*>(S + c * kEpiStride + rg * 8 + 4);
-                const uint4 v = make_uint4(pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w),
-                                           pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w));
-                *reinterpret_cast<uint4*>(a.Gt + (col0 + c) * a.n_pad + m0 + rg * 8) = v;
-            }
-        }
         if (a.G != nullptr) {
             // row-major copy, 64 columns at a time: each thread packs its row's
             // values to bf16 in registers, the rows go back to LDS as [row][64]
@@ -422,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
     }
 }
 
-// dW rows of one chunk: dW[v0 + i, h] = sum_n G^T[i, n] H^T[h, n], a single
+// dW rows of one chunk: dW[v0 + i, h] = sum_n G[n, i] H[n, h], a single
 // K-loop over every row n in ascending order; bf16 store of the fp32 sum.
 // With a caller accumulator the fp32 sum is first added to it (dw_acc +=),
 // and the bf16 output, if any, is the cast of the updated accumulator.
@@ -432,8 +420,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dw_kernel(DwArgs a) {
     map_tile(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
     AccTile acc;
-    gemm_mainloop(Operand{a.Gt, a.n_pad, a.w_pad}, m0, Operand{a.Ht, a.n_pad, a.hidden}, n0, a.n_pad,
-                  smem, acc);
+    // both operands MN-major: G [n_pad, w_pad] and H [n, hidden], k = n
+    gemm_mainloop<true, true>(Operand{a.G, a.w_pad, a.n_pad}, m0, Operand{a.H, a.hidden, a.n}, n0, a.n_pad,
+                              smem, acc);
     float* S = reinterpret_cast<float*>(smem);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
@@ -468,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dw_kernel(DwArgs a) {
     }
 }
 
-// dH contribution of one chunk: acc = sum_j G[n, j] W_c^T[h, j] over the
+// dH contribution of one chunk: acc = sum_j G[n, j] W[v0 + j, h] over the
 // chunk's columns; the fp32 running sum over chunks (chunk order) lives in
 // dh_acc and the last chunk writes the bf16 result. A caller accumulator is
 // dh_acc itself: read from chunk 0 on and stored after the last chunk too.
@@ -478,8 +467,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(DhArgs a) {
     map_tile(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
     AccTile acc;
-    gemm_mainloop(Operand{a.G, a.w_pad, a.n_pad}, m0, Operand{a.Wt, a.w_pad, a.hidden}, n0, a.w_pad,
-                  smem, acc);
+    // B = the chunk of W, MN-major [width, hidden], k = chunk column
+    gemm_mainloop<false, true>(Operand{a.G, a.w_pad, a.n_pad}, m0, Operand{a.Wc, a.hidden, a.width}, n0, a.w_pad,
+                               smem, acc);
     float* S = reinterpret_cast<float*>(smem);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
@@ -518,41 +508,6 @@ __global__ void f32_to_bf16_kernel(const float* in, int64_t count, bf16_bits* ou
          i += (int64_t)gridDim.x * blockDim.x * 2) {
         const float2 v = *reinterpret_cast<const float2*>(in + i);
         *reinterpret_cast<uint32_t*>(out + i) = pack_bf16x2(v.x, v.y);
-    }
-}
-
-// out[c, r] = in[r, c] for r < rows, 0 for rows <= r < rows_pad; columns are a
-// multiple of 64, rows_pad a multiple of 64. 64 x 64 tiles through LDS.
-__global__ void transpose_kernel(const bf16_bits* in, int64_t ld_in, int64_t rows, int64_t cols,
-                                 bf16_bits* out, int64_t rows_pad) {
-    __shared__ bf16_bits tile[64][64 + 8];
-    const int tid = threadIdx.x;
-    const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
-    {
-        const int r = tid >> 2, seg = (tid & 3) * 16;
-        uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
-        if (r0 + r < rows) {
-            const uint4* src = reinterpret_cast<const uint4*>(in + (r0 + r) * ld_in + c0 + seg);
-            v0 = src[0];
-            v1 = src[1];
-        }
-        const bf16_bits* p0 = reinterpret_cast<const bf16_bits*>(&v0);
-        const bf16_bits* p1 = reinterpret_cast<const bf16_bits*>(&v1);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            tile[r][seg + i] = p0[i];
-            tile[r][seg + 8 + i] = p1[i];
-        }
-    }
-    __syncthreads();
-    {
-        const int c = tid >> 2, seg = (tid & 3) * 16;
-        bf16_bits vals[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) vals[i] = tile[seg + i][c];
-        uint4* dst = reinterpret_cast<uint4*>(out + (c0 + c) * rows_pad + r0 + seg);
-        dst[0] = *reinterpret_cast<const uint4*>(&vals[0]);
-        dst[1] = *reinterpret_cast<const uint4*>(&vals[8]);
     }
 }
 

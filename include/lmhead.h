@@ -143,8 +143,8 @@ typedef struct lmhead_problem {
  * Bytes of device workspace an entry needs ("workspace reporting",
  * [PR8059]). Pure host function: no device is touched. `with_backward`
  * != 0 sizes the workspace for lmhead_loss_bwd (which needs more: one
- * chunk of dL/dz in two layouts, transposed operands and the fp32 dH
- * accumulator). Returns 0 for an invalid problem or entry.
+ * chunk of dL/dz and the fp32 dH accumulator). Returns 0 for an invalid
+ * problem or entry.
  */
 size_t lmhead_workspace_size(const lmhead_problem* p, int entry, int with_backward);
 
@@ -159,8 +159,7 @@ typedef struct lmhead_memory_figures {
     size_t workspace_bytes;      /* = lmhead_workspace_size(p, entry, with_backward) */
     size_t forward_bytes;        /* workspace the forward uses */
     size_t partials_bytes;       /* forward: (max, sum-exp) per 256-column tile and row */
-    size_t dz_chunk_bytes;       /* backward: one chunk of dL/dz, bf16, row- and column-major */
-    size_t operand_copy_bytes;   /* backward: H^T and one chunk of W^T, bf16 */
+    size_t dz_chunk_bytes;       /* backward: one chunk of dL/dz, bf16, row-major */
     size_t dh_acc_bytes;         /* backward: fp32 running sum of dH over the chunks */
     size_t caller_output_bytes;  /* buffers the caller allocates: the entry's fp32 outputs
                                     (loss / logp / lp, kl, lse), plus bf16 dH and dW

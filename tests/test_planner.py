@@ -21,15 +21,14 @@ def test_report_matches_workspace_and_layout():
         r = lm.memory_report(8192, 4096, 151936, 8192, entry, True, k)
         assert r["workspace_bytes"] == _ws(8192, entry, k)
         assert r["chunk"] == 8192 and r["chunks"] == 19
-        assert r["dz_chunk_bytes"] == 2 * 2 * 8192 * 8192          # G and its transpose, bf16
-        assert r["operand_copy_bytes"] == 2 * 4096 * 8192 * 2      # H^T and W_chunk^T
+        assert r["dz_chunk_bytes"] == 2 * 8192 * 8192              # one chunk of G, bf16
         assert r["dh_acc_bytes"] == 4 * 8192 * 4096
         assert r["partials_bytes"] == 8 * 594 * 8192
-        parts = r["dz_chunk_bytes"] + r["operand_copy_bytes"] + r["dh_acc_bytes"]
+        parts = r["dz_chunk_bytes"] + r["dh_acc_bytes"]
         assert parts <= r["workspace_bytes"] <= parts + (1 << 20) + 4 * 8192 * (k + 2) * 2
         f = lm.memory_report(8192, 4096, 151936, 8192, entry, False, k)
         assert f["workspace_bytes"] == f["forward_bytes"] == r["forward_bytes"]
-        assert f["dz_chunk_bytes"] == f["operand_copy_bytes"] == f["dh_acc_bytes"] == 0
+        assert f["dz_chunk_bytes"] == f["dh_acc_bytes"] == 0
         assert f["partials_bytes"] <= f["forward_bytes"]
     # caller outputs: CE: loss + lse; backward adds bf16 dH and dW
     r = lm.memory_report(8192, 4096, 151936, 8192, 0, True, 1)
