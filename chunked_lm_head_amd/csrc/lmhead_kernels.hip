@@ -112,13 +112,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTilesArgs a) 
         const int64_t col0 = n0 + half * 128;
         const int64_t rem = a.vocab - col0;
         const int ncol = rem <= 0 ? 0 : (rem >= 128 ? 128 : (int)rem);
-        if (inv_tau != 1.0f)
-            for (int c = 0; c < ncol; ++c) Sr[c * kEpiStride] *= inv_tau;
+        // the row's 128 values in registers: one pass of reads, all in flight
+        // (one wave per SIMD hides no LDS latency). Columns at or past ncol
+        // read as -inf: they leave the max alone and add exp2(-inf) = +0 to
+        // the sum (a half with ncol = 0 is never merged).
+        float x[128];
+#pragma unroll
+        for (int c = 0; c < 128; ++c) x[c] = Sr[c * kEpiStride] * inv_tau;
+        if (ncol < 128) {
+#pragma unroll
+            for (int c = 0; c < 128; ++c) x[c] = c < ncol ? x[c] : neg_inf();
+        }
         float m = neg_inf();
-        for (int c = 0; c < ncol; ++c) m = fmaxf(m, Sr[c * kEpiStride]);
+#pragma unroll
+        for (int c = 0; c < 128; ++c) m = fmaxf(m, x[c]);
         const float mb = m * kLog2e;
         float s = 0.0f;
-        for (int c = 0; c < ncol; ++c) s += exp2_fast(__builtin_fmaf(Sr[c * kEpiStride], kLog2e, -mb));
+#pragma unroll
+        for (int c = 0; c < 128; ++c) s += exp2_fast(__builtin_fmaf(x[c], kLog2e, -mb));
         if (half == 0) {
             run_m = m;
             run_s = s;
@@ -131,7 +142,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTilesArgs a) 
             const int32_t* idr = a.ids + row * a.k;
             for (int kk = 0; kk < a.k; ++kk) {
                 const int64_t j = (int64_t)idr[kk] - col0;
-                if (j >= 0 && j < ncol) a.zg[row * a.k + kk] = Sr[j * kEpiStride];
+                if (j >= 0 && j < ncol) a.zg[row * a.k + kk] = Sr[j * kEpiStride] * inv_tau;
             }
         }
         __syncthreads();
@@ -366,9 +377,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
         const int64_t col0 = n0 + half * 128;   // chunk-local column
         const int64_t rem = a.width - col0;
         const int ncol = rem <= 0 ? 0 : (rem >= 128 ? 128 : (int)rem);
-        for (int c = 0; c < 128; ++c) {
-            const float x = Sr[c * kEpiStride];
-            Sr[c * kEpiStride] = (c < ncol && ca != 0.0f) ? ca * exp2_fast(__builtin_fmaf(x, xs, -lb)) : 0.0f;
+        // branch-free in batches of 32: the reads of a batch are all in flight
+        // before the first exp (one wave per SIMD hides no LDS latency)
+        const bool live = ca != 0.0f;
+#pragma unroll 1
+        for (int c0 = 0; c0 < 128; c0 += 32) {
+            float x[32];
+#pragma unroll
+            for (int u = 0; u < 32; ++u) x[u] = Sr[(c0 + u) * kEpiStride];
+#pragma unroll
+            for (int u = 0; u < 32; ++u) {
+                const float g = ca * exp2_fast(__builtin_fmaf(x[u], xs, -lb));
+                Sr[(c0 + u) * kEpiStride] = (live && c0 + u < ncol) ? g : 0.0f;
+            }
         }
         if (row_ok) {
             const int32_t* idr = a.ids + row * a.k;
