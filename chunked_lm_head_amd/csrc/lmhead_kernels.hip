@@ -454,24 +454,41 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dw_kernel(DwArgs a) {
         __syncthreads();
         const int c = 4 * (lane & 31);
         const int64_t h = n0 + half * 128 + c;
-        for (int it = 0; it < 32; ++it) {
-            const int r = wave * 64 + it * 2 + (lane >> 5);
-            const int64_t v = m0 + r;   // chunk-local vocabulary row
-            if (v >= a.width || h >= a.hidden) continue;
-            const float4 x = *reinterpret_cast<const float4*>(S + r * kRowStride + c);
-            const int64_t o = (a.v0 + v) * a.hidden + h;
-            if (a.dw_acc == nullptr) {
-                *reinterpret_cast<uint2*>(a.dW + o) = make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
-            } else {
-                const float4 p = *reinterpret_cast<const float4*>(a.dw_acc + o);
-                float4 y;
-                y.x = p.x + x.x;
-                y.y = p.y + x.y;
-                y.z = p.z + x.z;
-                y.w = p.w + x.w;
-                *reinterpret_cast<float4*>(a.dw_acc + o) = y;
-                if (a.dW != nullptr)
-                    *reinterpret_cast<uint2*>(a.dW + o) = make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
+        const bool hok = h < a.hidden;
+        // 16 rows at a time; with a caller accumulator all 16 of its values
+        // are loaded (unconditionally, from in-bounds places for masked
+        // elements) before the first is used
+        const int64_t hc = hok ? h : 0;
+#pragma unroll 1
+        for (int i0 = 0; i0 < 32; i0 += 16) {
+            float4 p[16];
+            if (a.dw_acc != nullptr) {
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const int64_t v = m0 + wave * 64 + (i0 + u) * 2 + (lane >> 5);
+                    const int64_t vc = v < a.width ? v : a.width - 1;
+                    p[u] = *reinterpret_cast<const float4*>(a.dw_acc + (a.v0 + vc) * a.hidden + hc);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int r = wave * 64 + (i0 + u) * 2 + (lane >> 5);
+                const int64_t v = m0 + r;   // chunk-local vocabulary row
+                if (v >= a.width || !hok) continue;
+                const float4 x = *reinterpret_cast<const float4*>(S + r * kRowStride + c);
+                const int64_t o = (a.v0 + v) * a.hidden + h;
+                if (a.dw_acc == nullptr) {
+                    *reinterpret_cast<uint2*>(a.dW + o) = make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
+                } else {
+                    float4 y;
+                    y.x = p[u].x + x.x;
+                    y.y = p[u].y + x.y;
+                    y.z = p[u].z + x.z;
+                    y.w = p[u].w + x.w;
+                    *reinterpret_cast<float4*>(a.dw_acc + o) = y;
+                    if (a.dW != nullptr)
+                        *reinterpret_cast<uint2*>(a.dW + o) = make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
+                }
             }
         }
         __syncthreads();
@@ -502,22 +519,41 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(DhArgs a) {
         __syncthreads();
         const int c = 4 * (lane & 31);
         const int64_t h = n0 + half * 128 + c;
-        for (int it = 0; it < 32; ++it) {
-            const int r = wave * 64 + it * 2 + (lane >> 5);
-            const int64_t row = m0 + r;
-            if (row >= a.n || h >= a.hidden) continue;
-            float4 v = *reinterpret_cast<const float4*>(S + r * kRowStride + c);
-            const int64_t o = row * a.hidden + h;
+        const bool hok = h < a.hidden;
+        // 16 rows at a time: the running sums of all 16 are loaded before the
+        // first is used (one wave per SIMD hides no memory latency). The loads
+        // are unconditional, from an in-bounds row and column for lanes whose
+        // element is masked, so the compiler can count them and wait for each
+        // one alone rather than for every earlier load and store.
+        const int64_t hc = hok ? h : 0;
+#pragma unroll 1
+        for (int i0 = 0; i0 < 32; i0 += 16) {
+            float4 p[16];
             if (!a.first) {
-                const float4 p = *reinterpret_cast<const float4*>(a.dh_acc + o);
-                v.x = p.x + v.x;
-                v.y = p.y + v.y;
-                v.z = p.z + v.z;
-                v.w = p.w + v.w;
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const int64_t row = m0 + wave * 64 + (i0 + u) * 2 + (lane >> 5);
+                    const int64_t rc = row < a.n ? row : a.n - 1;
+                    p[u] = *reinterpret_cast<const float4*>(a.dh_acc + rc * a.hidden + hc);
+                }
             }
-            if (a.last && a.dH != nullptr)
-                *reinterpret_cast<uint2*>(a.dH + o) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
-            if (!a.last || a.keep_acc) *reinterpret_cast<float4*>(a.dh_acc + o) = v;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int r = wave * 64 + (i0 + u) * 2 + (lane >> 5);
+                const int64_t row = m0 + r;
+                if (row >= a.n || !hok) continue;
+                float4 v = *reinterpret_cast<const float4*>(S + r * kRowStride + c);
+                const int64_t o = row * a.hidden + h;
+                if (!a.first) {
+                    v.x = p[u].x + v.x;
+                    v.y = p[u].y + v.y;
+                    v.z = p[u].z + v.z;
+                    v.w = p[u].w + v.w;
+                }
+                if (a.last && a.dH != nullptr)
+                    *reinterpret_cast<uint2*>(a.dH + o) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+                if (!a.last || a.keep_acc) *reinterpret_cast<float4*>(a.dh_acc + o) = v;
+            }
         }
         __syncthreads();
     }
