@@ -407,7 +407,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
             // 0..31 of S, which are consumed), and 8 lanes then store one row's
             // 128 contiguous bytes
             uint16_t* Gl = reinterpret_cast<uint16_t*>(smem);
-#pragma unroll 1
+#pragma unroll
             for (int q = 0; q < 2; ++q) {
                 uint32_t w[32];
 #pragma unroll
