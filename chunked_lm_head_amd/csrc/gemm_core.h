@@ -48,8 +48,9 @@ constexpr int kGroupM = 8;                   // row tiles per group in the tile 
 // rows (mn) at or beyond `rows` read as zero (their products land in masked
 // output rows / columns). MN-major: element (mn, k) at ptr[k * ld + mn], and
 // K rows at or beyond `rows` read as zero; columns past the operand's MN
-// extent read whatever follows in memory (or zero past the K rows' end) and
-// only reach output rows / columns that are masked.
+// extent read the next row's first elements (zero after the last row; never
+// memory beyond the operand) and only reach output rows / columns that are
+// masked.
 struct Operand {
     const bf16_bits* ptr;
     int64_t ld;
@@ -139,7 +140,7 @@ __device__ __forceinline__ void stage_put_t(char* base, int wave, int lane, int 
 // past `krows` read as zero.
 struct OpStream {
     __amdgpu_buffer_rsrc_t rsrc;  // K-major only
-    const char* base;             // MN-major: address of (k = 0, mn = mn0)
+    const char* base;             // MN-major: address of k row 0 (mn = 0)
     int64_t ld_bytes;             // MN-major: bytes per k row
     int64_t krows;                // MN-major: k rows that exist
     uint32_t voff;                // lane offset (bytes) within an 8-row group, wave's rows included
@@ -161,16 +162,20 @@ __device__ __forceinline__ OpStream make_stream(const Operand& X, int64_t mn0, i
         o.step = (uint32_t)(8 * X.ld * 2);
     } else {
         o.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)X.ptr, 0, 0, 0x00020000);
-        o.base = reinterpret_cast<const char*>(X.ptr + mn0);
+        // the tile's column offset goes into the lane offset, not the base:
+        // the range of a step's descriptor then ends with its last k row, and
+        // the columns a tile reads past the end of that row read zero
+        o.base = reinterpret_cast<const char*>(X.ptr);
         o.ld_bytes = X.ld * 2;
         o.krows = X.rows;
-        o.voff = (uint32_t)((wave * 2 + (lane >> 5)) * o.ld_bytes + (lane & 31) * 16);
+        o.voff = (uint32_t)((wave * 2 + (lane >> 5)) * o.ld_bytes + mn0 * 2 + (lane & 31) * 16);
         o.step = (uint32_t)(8 * o.ld_bytes);
     }
     return o;
 }
 
-// The descriptor for K step kt (k0 = 64 kt).
+// The descriptor for K step kt (k0 = 64 kt): k rows k0 .. k0 + 63, cut at
+// the operand's last k row (rows past it read zero).
 template <bool T>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t step_rsrc(const OpStream& o, int64_t k0) {
     if (!T) return o.rsrc;
