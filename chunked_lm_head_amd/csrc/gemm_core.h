@@ -11,12 +11,12 @@
 //
 // Waves are laid out 2 x 2; each wave owns a 128 x 128 sub-tile, i.e. 8 x 8
 // blocks of v_mfma_f32_16x16x32_bf16 (256 fp32 accumulators per lane, in
-// AGPRs). K advances 64 at a time through two LDS stages of 64 KB (A and B
-// tiles of 256 x 64 bf16 each). Global data reaches LDS through registers:
-// each wave holds two more K steps in flight in VGPRs (2 x 64 registers), so
-// a load has about one and a half K steps to return before it is needed —
-// with only two 64 KB LDS stages, loads straight into LDS could be issued at
-// most one step ahead, and the waves then spent about a third of their time
+// AGPRs). K advances 64 at a time through two LDS stages (A and B tiles of
+// 256 x 64 bf16 each, in 34 KB slots). Global data reaches LDS through
+// registers: each wave holds two more K steps in flight in VGPRs (2 x 64
+// registers), so a load has two K steps to return before it is stored —
+// with only two LDS stages, loads straight into LDS could be issued at most
+// one step ahead, and the waves then spent about a third of their time
 // waiting for them.
 #pragma once
 
@@ -99,10 +99,10 @@ __device__ __forceinline__ bf16x8 lds_fragment(const char* base, int row, int q)
 // The K loop.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// Buffer load of one 16-byte chunk per lane. The descriptor starts at the
-// tile's first row and ends at the operand's last row, so rows past the end
-// read as zero (no clamping). voff: the lane's byte offset within an 8-row
-// group; soff: the group's byte offset plus the K offset (uniform).
+// Buffer load of one 16-byte chunk per lane. The descriptor's range ends at
+// the operand's last row, so rows past the end read as zero (no clamping).
+// voff: the lane's byte offset within an 8-row group; soff: the group's byte
+// offset (plus, K-major, the K offset), uniform.
 __device__ __forceinline__ u32x4_t stage_fetch_b(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, 0));
 }
