@@ -80,6 +80,38 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t count, uint32_t value) {
         p[i] = value;
 }
 
+// Scan of a row's k ids against the tile columns [col0, col0 + ncol): ids
+// are taken 32 at a time (loads clamped to the row's last slot), each gives
+// one bit of a hit mask with a 32-bit compare and no branch, and only the hits
+// are visited, in ascending slot order. A row has about k * 256 / V hits per
+// tile, so the per-id cost is what matters. visit(kk, j) gets the slot and
+// the column within the tile.
+// The differences are taken modulo 2^32: with 0 <= col0 < 2^30 an id lands
+// in [0, ncol) exactly when id - col0 does over the integers.
+template <class Visit>
+__device__ __forceinline__ void scan_ids(const int32_t* idr, int k, uint32_t col0, int ncol, Visit visit) {
+    if (k == 1) {
+        const uint32_t d = (uint32_t)idr[0] - col0;
+        if (d < (uint32_t)ncol) visit(0, (int)d);
+        return;
+    }
+#pragma unroll 1
+    for (int k0 = 0; k0 < k; k0 += 32) {
+        const int last = k - 1 - k0;
+        uint32_t hits = 0u;
+#pragma unroll
+        for (int u = 0; u < 32; ++u) {
+            const uint32_t d = (uint32_t)idr[k0 + (u < last ? u : last)] - col0;
+            hits |= (u <= last && d < (uint32_t)ncol) ? (1u << u) : 0u;
+        }
+        while (hits != 0u) {
+            const int u = __builtin_ctz(hits);
+            hits &= hits - 1u;
+            visit(k0 + u, (int)((uint32_t)idr[k0 + u] - col0));
+        }
+    }
+}
+
 // ------------------------------------------------------------- forward tiles
 
 // One 256-row x 256-column logits tile: z = H W^T on MFMA, then per row the
@@ -138,13 +170,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTilesArgs a) 
             run_s = run_s * exp2_fast((run_m - M) * kLog2e) + s * exp2_fast((m - M) * kLog2e);
             run_m = M;
         }
-        if (row_ok) {
-            const int32_t* idr = a.ids + row * a.k;
-            for (int kk = 0; kk < a.k; ++kk) {
-                const int64_t j = (int64_t)idr[kk] - col0;
-                if (j >= 0 && j < ncol) a.zg[row * a.k + kk] = Sr[j * kEpiStride] * inv_tau;
-            }
-        }
+        if (row_ok)
+            scan_ids(a.ids + row * a.k, a.k, (uint32_t)col0, ncol, [&](int kk, int j) {
+                a.zg[row * a.k + kk] = Sr[j * kEpiStride] * inv_tau;
+            });
         __syncthreads();
     }
     if (row_ok) a.part[tn * a.n + row] = make_float2(run_m, run_s);
@@ -392,12 +421,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
             }
         }
         if (row_ok) {
-            const int32_t* idr = a.ids + row * a.k;
+            // c_nk at the row's ids in the tile, in ascending k
             const float* cr = a.coef_c + row * a.k;
-            for (int kk = 0; kk < a.k; ++kk) {
-                const int64_t j = (int64_t)idr[kk] - a.v0 - col0;
-                if (j >= 0 && j < ncol) Sr[j * kEpiStride] += cr[kk];
-            }
+            scan_ids(a.ids + row * a.k, a.k, (uint32_t)(a.v0 + col0), ncol, [&](int kk, int j) {
+                Sr[j * kEpiStride] += cr[kk];
+            });
         }
         __syncthreads();
         if (a.G != nullptr) {
