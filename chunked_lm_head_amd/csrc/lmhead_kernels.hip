@@ -80,34 +80,50 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t count, uint32_t value) {
         p[i] = value;
 }
 
-// Scan of a row's k ids against the tile columns [col0, col0 + ncol): ids
-// are taken 32 at a time (loads clamped to the row's last slot), each gives
-// one bit of a hit mask with a 32-bit compare and no branch, and only the hits
-// are visited, in ascending slot order. A row has about k * 256 / V hits per
-// tile, so the per-id cost is what matters. visit(kk, j) gets the slot and
-// the column within the tile.
-// The differences are taken modulo 2^32: with 0 <= col0 < 2^30 an id lands
-// in [0, ncol) exactly when id - col0 does over the integers.
+// Scans of the rows' candidate ids against a tile's columns [col0, col0 +
+// ncol). The differences are taken modulo 2^32: with 0 <= col0 < 2^30 an id
+// lands in [0, ncol) exactly when id - col0 does over the integers. A row has
+// about k * 256 / V hits per tile, so the per-id cost is what matters.
+//
+// k = 1: each thread checks its own row's id.
+__device__ __forceinline__ bool id_in_tile(const int32_t* idr, uint32_t col0, int ncol, int& j) {
+    const uint32_t d = (uint32_t)idr[0] - col0;
+    j = (int)d;
+    return d < (uint32_t)ncol;
+}
+
+// k > 1: the wave walks its 64 rows (row0 + 0..63), 16 at a time. The lanes
+// load a row's ids at slots k0 + lane, so each load instruction reads one
+// row's contiguous ids instead of one id from each of 64 rows; the hits of
+// a row (a ballot) are visited in ascending slot order by the row's own lane
+// (lane r holds row row0 + r), as visit(slot, column within the tile). Every
+// lane of the wave must call it.
 template <class Visit>
-__device__ __forceinline__ void scan_ids(const int32_t* idr, int k, uint32_t col0, int ncol, Visit visit) {
-    if (k == 1) {
-        const uint32_t d = (uint32_t)idr[0] - col0;
-        if (d < (uint32_t)ncol) visit(0, (int)d);
-        return;
-    }
+__device__ __forceinline__ void scan_ids_wave(const int32_t* ids, int64_t row0, int64_t n, int k,
+                                              uint32_t col0, int ncol, int lane, Visit visit) {
 #pragma unroll 1
-    for (int k0 = 0; k0 < k; k0 += 32) {
-        const int last = k - 1 - k0;
-        uint32_t hits = 0u;
+    for (int r0 = 0; r0 < 64; r0 += 16) {
+        if (row0 + r0 >= n) break;
+#pragma unroll 1
+        for (int k0 = 0; k0 < k; k0 += 64) {
+            const bool slot_ok = k0 + lane < k;
+            const int kk = slot_ok ? k0 + lane : k - 1;
+            uint32_t d[16];
 #pragma unroll
-        for (int u = 0; u < 32; ++u) {
-            const uint32_t d = (uint32_t)idr[k0 + (u < last ? u : last)] - col0;
-            hits |= (u <= last && d < (uint32_t)ncol) ? (1u << u) : 0u;
-        }
-        while (hits != 0u) {
-            const int u = __builtin_ctz(hits);
-            hits &= hits - 1u;
-            visit(k0 + u, (int)((uint32_t)idr[k0 + u] - col0));
+            for (int i = 0; i < 16; ++i) {
+                const int64_t row = row0 + r0 + i < n ? row0 + r0 + i : n - 1;
+                d[i] = (uint32_t)ids[row * k + kk] - col0;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                uint64_t hits = __ballot(slot_ok && row0 + r0 + i < n && d[i] < (uint32_t)ncol);
+                while (hits != 0u) {
+                    const int b = __builtin_ctzll(hits);
+                    hits &= hits - 1u;
+                    const int j = __builtin_amdgcn_readlane((int)d[i], b);
+                    if (lane == r0 + i) visit(k0 + b, j);
+                }
+            }
         }
     }
 }
@@ -170,10 +186,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTilesArgs a) 
             run_s = run_s * exp2_fast((run_m - M) * kLog2e) + s * exp2_fast((m - M) * kLog2e);
             run_m = M;
         }
-        if (row_ok)
-            scan_ids(a.ids + row * a.k, a.k, (uint32_t)col0, ncol, [&](int kk, int j) {
-                a.zg[row * a.k + kk] = Sr[j * kEpiStride] * inv_tau;
-            });
+        auto gather = [&](int kk, int j) { a.zg[row * a.k + kk] = Sr[j * kEpiStride] * inv_tau; };
+        if (a.k == 1) {
+            int j;
+            if (row_ok && id_in_tile(a.ids + row, (uint32_t)col0, ncol, j)) gather(0, j);
+        } else {
+            scan_ids_wave(a.ids, m0 + wave * 64, a.n, a.k, (uint32_t)col0, ncol, lane, gather);
+        }
         __syncthreads();
     }
     if (row_ok) a.part[tn * a.n + row] = make_float2(run_m, run_s);
@@ -420,12 +439,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
                 Sr[(c0 + u) * kEpiStride] = (live && c0 + u < ncol) ? g : 0.0f;
             }
         }
-        if (row_ok) {
-            // c_nk at the row's ids in the tile, in ascending k
-            const float* cr = a.coef_c + row * a.k;
-            scan_ids(a.ids + row * a.k, a.k, (uint32_t)(a.v0 + col0), ncol, [&](int kk, int j) {
-                Sr[j * kEpiStride] += cr[kk];
-            });
+        // c_nk at the row's ids in the tile, in ascending k
+        auto add_c = [&](int kk, int j) { Sr[j * kEpiStride] += a.coef_c[row * a.k + kk]; };
+        if (a.k == 1) {
+            int j;
+            if (row_ok && id_in_tile(a.ids + row, (uint32_t)(a.v0 + col0), ncol, j)) add_c(0, j);
+        } else {
+            scan_ids_wave(a.ids, m0 + wave * 64, a.n, a.k, (uint32_t)(a.v0 + col0), ncol, lane, add_c);
         }
         __syncthreads();
         if (a.G != nullptr) {
