@@ -201,3 +201,37 @@ def test_kl_only_full_size_sampled():
                                           threads=16)
         dw_ref = oracle.grad_weight(rv["dz"][:, [v]], inp.H, listing, threads=16)
         grad_check(f"dW row {v}", bf16_to_np(got["dW"][int(v)][None]), dw_ref)
+
+
+@pytest.mark.parametrize("k, pad", [(100, 0.0), (130, 0.3)])
+def test_more_candidates_than_wave_lanes(k, pad):
+    """k above 64: the tile epilogues scan a row's ids in several 64-slot
+    batches (the last one ragged), one wave over its 64 rows (the last wave
+    partly past n); with duplicate ids within and across batches and, for
+    padded lists, padding slots and a row with no real candidate."""
+    padded = pad > 0.0
+    inp = _inputs(n=150, vocab=1500, k=k, seed=760 + k, pad_frac=pad)
+    inp.ids[5, 1] = inp.ids[5, 0]           # duplicate within a batch
+    if padded:
+        inp.ids[140, :] = -1
+    else:
+        inp.ids[9, 70] = inp.ids[9, 3]      # duplicates across batches
+        inp.ids[149, k - 1] = inp.ids[149, 0]
+    d = Dev(inp)
+    lp, kl, lse, _ = lm.support_forward(d.H, d.W, d.ids, d.ref_logq, 512, padded=padded)
+    dH, dW = lm.backward(lm.ENTRY_SUPPORT, d.H, d.W, d.ids, lse, d.grad, 512, ref_logq=d.ref_logq,
+                         saved_lp=lp, grad_kl=d.grad_kl, padded=padded)
+    torch.cuda.synchronize()
+    ref = oracle.run(3, inp.H, inp.W, ids=inp.ids, ref_logq=inp.ref_logq, grad=inp.grad,
+                     grad_kl=inp.grad_kl, padded=padded)
+    rel_check("lp", to_np(lp), ref["lp"])
+    rel_check("kl", to_np(kl), ref["kl"])
+    rel_check("lse", to_np(lse), ref["lse"])
+    grad_check("dH", bf16_to_np(dH), ref["dH"])
+    grad_check("dW", bf16_to_np(dW), ref["dW"])
+    # repeat: bitwise
+    lp2, kl2, lse2, _ = lm.support_forward(d.H, d.W, d.ids, d.ref_logq, 512, padded=padded)
+    dH2, dW2 = lm.backward(lm.ENTRY_SUPPORT, d.H, d.W, d.ids, lse2, d.grad, 512,
+                           ref_logq=d.ref_logq, saved_lp=lp2, grad_kl=d.grad_kl, padded=padded)
+    torch.cuda.synchronize()
+    assert torch.equal(lp, lp2) and torch.equal(kl, kl2) and torch.equal(dH, dH2) and torch.equal(dW, dW2)
