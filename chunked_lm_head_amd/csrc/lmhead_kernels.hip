@@ -417,6 +417,36 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
     const float ca = row_ok ? a.coef_a[row] : 0.0f;
     const float lb = row_ok ? a.lse[row] * kLog2e : 0.0f;
     const float xs = row_ok ? kLog2e / row_tau(a.T, row) : kLog2e;   // log2(e) / tau_n
+    // a_n exp(z - lse_n) in the accumulators, by all four waves at once: each
+    // lane holds 32 rows (4 per block row), whose constants thread t, row t,
+    // shares through the LDS past the staging area (the K loop is done with it)
+    static_assert(kEpiLdsBytes + 3 * kTile * 4 <= kLdsBytes, "row constants must fit past the staging area");
+    {
+        float* K3 = S + 128 * kEpiStride;
+        K3[tid] = ca;
+        K3[kTile + tid] = lb;
+        K3[2 * kTile + tid] = xs;
+        __syncthreads();
+        const int64_t cb = n0 + wc * 128 + (lane & 15);   // chunk-local column of block 0
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r0 = wr * 128 + i * 16 + 4 * (lane >> 4);
+            const floatx4 ca4 = *reinterpret_cast<const floatx4*>(K3 + r0);
+            const floatx4 lb4 = *reinterpret_cast<const floatx4*>(K3 + kTile + r0);
+            const floatx4 xs4 = *reinterpret_cast<const floatx4*>(K3 + 2 * kTile + r0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const bool col_ok = cb + 16 * j < a.width;
+                floatx4 v = acc[i][j];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float g = ca4[e] * exp2_fast(__builtin_fmaf(v[e], xs4[e], -lb4[e]));
+                    v[e] = (ca4[e] != 0.0f && col_ok) ? g : 0.0f;
+                }
+                acc[i][j] = v;
+            }
+        }
+    }
     float* Sr = S + tid;
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
@@ -425,20 +455,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
         const int64_t col0 = n0 + half * 128;   // chunk-local column
         const int64_t rem = a.width - col0;
         const int ncol = rem <= 0 ? 0 : (rem >= 128 ? 128 : (int)rem);
-        // branch-free in batches of 32: the reads of a batch are all in flight
-        // before the first exp (one wave per SIMD hides no LDS latency)
-        const bool live = ca != 0.0f;
-#pragma unroll 1
-        for (int c0 = 0; c0 < 128; c0 += 32) {
-            float x[32];
-#pragma unroll
-            for (int u = 0; u < 32; ++u) x[u] = Sr[(c0 + u) * kEpiStride];
-#pragma unroll
-            for (int u = 0; u < 32; ++u) {
-                const float g = ca * exp2_fast(__builtin_fmaf(x[u], xs, -lb));
-                Sr[(c0 + u) * kEpiStride] = (live && c0 + u < ncol) ? g : 0.0f;
-            }
-        }
         // c_nk at the row's ids in the tile, in ascending k
         auto add_c = [&](int kk, int j) { Sr[j * kEpiStride] += a.coef_c[row * a.k + kk]; };
         if (a.k == 1) {
