@@ -29,7 +29,7 @@ struct Layout {
     // backward regions
     size_t coef_a, coef_c, G, dh_acc;
     // backward of the KL-only entry: inverse index of the candidate ids
-    size_t counts, offsets, cursor, list;
+    size_t counts, offsets, cursor, list, tsum, tprefix;
     size_t fwd_total, bwd_total;
 };
 
@@ -82,6 +82,8 @@ Layout plan(const lmhead_problem& p, int entry) {
         L.offsets = take(4 * (L.vocab + 1));
         L.cursor = take(4 * L.vocab);
         L.list = take(4 * L.n * L.k);
+        L.tsum = take(4 * cdiv(L.vocab, kScanTile));
+        L.tprefix = take(4 * (cdiv(L.vocab, kScanTile) + 1));
         L.bwd_total = off;
         return L;
     }
@@ -268,7 +270,10 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
     ca.num_valid = p->num_valid;
     ca.coef_a = (float*)(w + L.coef_a);
     ca.coef_c = (float*)(w + L.coef_c);
-    coeffs_kernel<<<grid_1d(L.n_pad, kThreads, INT_MAX), kThreads, 0, s>>>(ca);
+    if (support)
+        coeffs_support_kernel<<<(unsigned)cdiv(L.n_pad, kThreads / 64), kThreads, 0, s>>>(ca);
+    else
+        coeffs_kernel<<<grid_1d(L.n_pad, kThreads, INT_MAX), kThreads, 0, s>>>(ca);
     if (kl_only) {
         // dL/dz is nonzero only at the candidates: gathers instead of contractions
         CandBwdArgs cb;
@@ -297,7 +302,12 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
             fill_u32(counts, L.vocab, 0u, s);
             fill_u32(cursor, L.vocab, 0u, s);
             cand_count_kernel<<<grid_1d(nk, kThreads, 4096), kThreads, 0, s>>>(ids, nk, L.vocab, counts);
-            exclusive_scan_kernel<<<1, 1024, 0, s>>>(counts, L.vocab, offsets);
+            const int64_t tiles = cdiv(L.vocab, kScanTile);
+            int32_t* tsum = (int32_t*)(w + L.tsum);
+            int32_t* tprefix = (int32_t*)(w + L.tprefix);
+            tile_sums_kernel<<<(unsigned)tiles, 256, 0, s>>>(counts, L.vocab, tsum);
+            exclusive_scan_kernel<<<1, 1024, 0, s>>>(tsum, tiles, tprefix);
+            scan_tiles_kernel<<<(unsigned)tiles, 256, 0, s>>>(counts, L.vocab, tprefix, tiles, offsets);
             cand_fill_kernel<<<grid_1d(nk, kThreads, 4096), kThreads, 0, s>>>(ids, nk, L.vocab, offsets,
                                                                               cursor, list);
             bucket_sort_kernel<<<grid_1d(L.vocab, kThreads, 4096), kThreads, 0, s>>>(offsets, L.vocab,

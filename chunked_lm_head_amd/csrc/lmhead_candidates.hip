@@ -211,6 +211,59 @@ __global__ __launch_bounds__(1024) void exclusive_scan_kernel(const int32_t* cou
     if (t == 1023) offsets[vocab] = part[1023];
 }
 
+// The bucket offsets over the whole vocabulary, in three launches: the sum of
+// each 1024-count tile, an exclusive scan of those sums (exclusive_scan_kernel
+// on the tile sums, one workgroup, ceil(V / 1024) values), then each tile's
+// own exclusive scan plus its prefix. Integer sums are exact, so the result
+// is the plain exclusive scan whatever the grouping.
+__global__ __launch_bounds__(256) void tile_sums_kernel(const int32_t* counts, int64_t vocab, int32_t* sums) {
+    __shared__ int32_t wsum[4];
+    const int64_t base = (int64_t)blockIdx.x * kScanTile;
+    const int t = threadIdx.x;
+    int32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < kScanTile / 256; ++i) {
+        const int64_t v = base + i * 256 + t;
+        if (v < vocab) s += counts[v];
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o);
+    if ((t & 63) == 0) wsum[t >> 6] = s;
+    __syncthreads();
+    if (t == 0) sums[blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+}
+
+// offsets[v] for v in one tile: prefix[tile] plus the exclusive scan of the
+// tile's counts (thread t holds counts 4 t .. 4 t + 3); the first tile also
+// writes offsets[vocab] = prefix[tiles].
+__global__ __launch_bounds__(256) void scan_tiles_kernel(const int32_t* counts, int64_t vocab,
+                                                         const int32_t* prefix, int64_t tiles,
+                                                         int32_t* offsets) {
+    __shared__ int32_t wtot[4];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int64_t v0 = (int64_t)blockIdx.x * kScanTile + 4 * t;
+    int32_t c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = v0 + i < vocab ? counts[v0 + i] : 0;
+    const int32_t own = c[0] + c[1] + c[2] + c[3];
+    int32_t inc = own;   // inclusive scan over the wave's lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t u = __shfl_up(inc, o);
+        if (lane >= o) inc += u;
+    }
+    if (lane == 63) wtot[w] = inc;
+    __syncthreads();
+    int32_t run = prefix[blockIdx.x] + inc - own;
+    for (int i = 0; i < w; ++i) run += wtot[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (v0 + i < vocab) offsets[v0 + i] = run;
+        run += c[i];
+    }
+    if (blockIdx.x == 0 && t == 0) offsets[vocab] = prefix[tiles];
+}
+
 // list[offsets[id] + slot] = entry index i = row * k + candidate; the slot
 // order inside a bucket is arbitrary here and fixed by bucket_sort_kernel.
 __global__ void cand_fill_kernel(const int32_t* ids, int64_t nk, int64_t vocab, const int32_t* offsets,

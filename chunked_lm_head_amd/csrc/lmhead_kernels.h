@@ -157,6 +157,7 @@ __global__ void finalize_rows_kernel(FinalizeArgs a);
 __global__ void ce_reduce_kernel(const float* rows, int64_t n, const int32_t* hdr, int64_t num_valid,
                                  int mean, float* loss);
 __global__ void coeffs_kernel(CoeffArgs a);
+__global__ void coeffs_support_kernel(CoeffArgs a);
 __global__ void bwd_logit_grad_kernel(LogitGradArgs a);
 __global__ void bwd_dw_kernel(DwArgs a);
 __global__ void bwd_dh_kernel(DhArgs a);
@@ -164,6 +165,10 @@ __global__ void cand_kl_fwd_kernel(CandFwdArgs a);
 __global__ void cand_dh_kernel(CandBwdArgs a);
 __global__ void cand_count_kernel(const int32_t* ids, int64_t nk, int64_t vocab, int32_t* counts);
 __global__ void exclusive_scan_kernel(const int32_t* counts, int64_t vocab, int32_t* offsets);
+constexpr int kScanTile = 1024;   // counts per workgroup of the multi-block scan
+__global__ void tile_sums_kernel(const int32_t* counts, int64_t vocab, int32_t* sums);
+__global__ void scan_tiles_kernel(const int32_t* counts, int64_t vocab, const int32_t* prefix, int64_t tiles,
+                                  int32_t* offsets);
 __global__ void cand_fill_kernel(const int32_t* ids, int64_t nk, int64_t vocab, const int32_t* offsets,
                                  int32_t* cursor, int32_t* list);
 __global__ void bucket_sort_kernel(const int32_t* offsets, int64_t vocab, int32_t* list);

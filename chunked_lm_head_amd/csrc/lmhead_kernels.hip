@@ -320,6 +320,8 @@ __global__ void ce_reduce_kernel(const float* rows, int64_t n, const int32_t* hd
 //   logprob:  a = -valid gamma_n,   c = valid gamma_n
 //   support:  a = -sum_k gamma_nk,  c_k = gamma_nk + beta_n (Q p_hat_k - q_k), Q = sum q
 // Rows past n (tile padding) and rows with a data error get a = c = 0.
+// coeffs_kernel (one thread per row) serves the single-id entries,
+// coeffs_support_kernel (one wave per row) the support entries.
 __global__ void coeffs_kernel(CoeffArgs a) {
     const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (row >= a.n_pad) return;
@@ -332,7 +334,7 @@ __global__ void coeffs_kernel(CoeffArgs a) {
     const float tau = row_tau(a.T, row);
     const bool good_tau = a.T.row == nullptr || tau_ok(tau);
     const float inv_tau = good_tau ? 1.0f / tau : 0.0f;
-    if (a.entry != kEntrySupport) {
+    {
         const int64_t t = a.ids[row];
         const bool valid = t >= 0 && t < a.vocab && good_tau;
         float ca = 0.0f, cc = 0.0f;
@@ -350,49 +352,82 @@ __global__ void coeffs_kernel(CoeffArgs a) {
         }
         a.coef_a[row] = ca * inv_tau;
         a.coef_c[row] = cc * inv_tau;
+    }
+}
+
+// Support entries, one wave per row: lane l takes the slots l, l + 64, ...
+// in ascending order, and each row sum (of gamma, of exp(lp - max), of q) is
+// the lanes' partial sums combined by a fixed xor butterfly, so the
+// association order depends on k only. A row with a bad id (or a bad
+// per-row temperature) gets a = c = 0, like a row past n.
+__device__ __forceinline__ float wave_sum64(float v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__device__ __forceinline__ float wave_max64(float v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__global__ __launch_bounds__(256) void coeffs_support_kernel(CoeffArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+    if (row >= a.n_pad) return;
+    if (row >= a.n) {
+        if (lane == 0) a.coef_a[row] = 0.0f;
         return;
     }
+    const int k = a.k;
+    const float tau = row_tau(a.T, row);
+    const bool good_tau = a.T.row == nullptr || tau_ok(tau);
+    const float inv_tau = good_tau ? 1.0f / tau : 0.0f;
     const int32_t* idr = a.ids + row * k;
-    bool bad = !good_tau;
-    for (int kk = 0; kk < k; ++kk) {
-        const int64_t id = idr[kk];
-        bad = bad || id >= a.vocab || (id < 0 && !a.padded);
-    }
     float* c = a.coef_c + row * k;
-    if (bad) {
-        a.coef_a[row] = 0.0f;
-        for (int kk = 0; kk < k; ++kk) c[kk] = 0.0f;
+    bool bad_l = false;
+    for (int kk = lane; kk < k; kk += 64) {
+        const int32_t id = idr[kk];
+        bad_l = bad_l || id >= a.vocab || (id < 0 && !a.padded);
+    }
+    if (!good_tau || __any(bad_l)) {
+        for (int kk = lane; kk < k; kk += 64) c[kk] = 0.0f;
+        if (lane == 0) a.coef_a[row] = 0.0f;
         return;
     }
     const float* g = a.grad != nullptr ? a.grad + row * k : nullptr;
-    float gsum = 0.0f;
-    for (int kk = 0; kk < k; ++kk) {
+    float gs = 0.0f;
+    for (int kk = lane; kk < k; kk += 64) {
         const float gk = (g != nullptr && idr[kk] >= 0) ? g[kk] : 0.0f;
-        gsum += gk;
+        gs += gk;
         c[kk] = gk;
     }
-    a.coef_a[row] = -gsum * inv_tau;
+    const float gsum = wave_sum64(gs);
+    if (lane == 0) a.coef_a[row] = -gsum * inv_tau;
     if (a.grad_kl != nullptr) {
         const float beta = a.grad_kl[row];
         const float* lp = a.saved_lp + row * k;
         const float* r = a.ref_logq + row * k;
         float mx = neg_inf();
-        for (int kk = 0; kk < k; ++kk)
+        for (int kk = lane; kk < k; kk += 64)
             if (idr[kk] >= 0) mx = fmaxf(mx, lp[kk]);
+        mx = wave_max64(mx);
         float se = 0.0f, Q = 0.0f;
-        for (int kk = 0; kk < k; ++kk) {
+        for (int kk = lane; kk < k; kk += 64) {
             if (idr[kk] < 0) continue;
             se += expf(lp[kk] - mx);
             Q += expf(r[kk]);
         }
+        se = wave_sum64(se);
+        Q = wave_sum64(Q);
         const float inv = 1.0f / se;
-        for (int kk = 0; kk < k; ++kk) {
+        for (int kk = lane; kk < k; kk += 64) {
             if (idr[kk] < 0) continue;
             const float phat = expf(lp[kk] - mx) * inv;
             c[kk] += beta * (Q * phat - expf(r[kk]));
         }
     }
-    for (int kk = 0; kk < k; ++kk) c[kk] *= inv_tau;
+    for (int kk = lane; kk < k; kk += 64) c[kk] *= inv_tau;
 }
 
 // Recompute one chunk's logits tile and write dL/dz in bf16: G[n, j] = a_n
