@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle sample")
+    ap.add_argument("--kl-only", action="store_true",
+                    help="with --workload support: time the KL-only support entry "
+                         "(lmhead_support_kl + its backward) instead of the dense one")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run one device-to-device copy of BYTES (counter calibration)")
     return ap.parse_args()
@@ -98,6 +101,9 @@ def main():
         return
 
     wl = workloads.WORKLOADS[args.workload]
+    if args.kl_only and wl.entry != workloads.ENTRY_SUPPORT:
+        print("--kl-only needs a support workload (--workload support)", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()
@@ -108,8 +114,8 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
     H, W = bf16(inp.H), bf16(inp.W)
-    entry = wl.entry
-    k = wl.k if entry == workloads.ENTRY_SUPPORT else 1
+    entry = workloads.ENTRY_SUPPORT_KL if args.kl_only else wl.entry
+    k = wl.k if entry in (workloads.ENTRY_SUPPORT, workloads.ENTRY_SUPPORT_KL) else 1
     idx = torch.from_numpy(inp.targets if inp.targets is not None else inp.ids).to(dev)
     grad = torch.from_numpy(inp.grad).to(dev)
     ref_logq = torch.from_numpy(inp.ref_logq).to(dev) if inp.ref_logq is not None else None
@@ -133,16 +139,22 @@ def main():
             st = lm.lmhead_loss_fwd(p, entry, H, W, idx, loss, lse, ws, ws_bytes, sp)
         elif entry == workloads.ENTRY_LOGPROB:
             st = lm.lmhead_logprob(p, H, W, idx, row_out, lse, ws, ws_bytes, sp)
-        else:
+        elif entry == workloads.ENTRY_SUPPORT:
             st = lm.lmhead_support_logprob_kl(p, H, W, idx, ref_logq, row_out, kl, lse, ws,
                                               ws_bytes, sp)
+        else:   # KL-only: row_out holds log p_hat
+            st = lm.lmhead_support_kl(p, H, W, idx, ref_logq, kl, row_out, ws, ws_bytes, sp)
         if st:
             raise lm.LMHeadError(st, "forward")
 
     def bwd():
-        saved = row_out if entry == workloads.ENTRY_SUPPORT else None
-        st = lm.lmhead_loss_bwd(p, entry, H, W, idx, ref_logq, lse, saved, grad, grad_kl, dH, dW,
-                                ws, ws_bytes, sp)
+        if entry == workloads.ENTRY_SUPPORT_KL:
+            st = lm.lmhead_loss_bwd(p, entry, H, W, idx, ref_logq, None, row_out, None, grad_kl,
+                                    dH, dW, ws, ws_bytes, sp)
+        else:
+            saved = row_out if entry == workloads.ENTRY_SUPPORT else None
+            st = lm.lmhead_loss_bwd(p, entry, H, W, idx, ref_logq, lse, saved, grad, grad_kl, dH,
+                                    dW, ws, ws_bytes, sp)
         if st:
             raise lm.LMHeadError(st, "backward")
 
@@ -209,7 +221,7 @@ def main():
         "data": "synthetic (seeded normals, no checkpoint or dataset)",
         "config": {
             "workload": f"{wl.name}: N={wl.n} tokens, Hd={wl.hidden}, V={wl.vocab}, "
-                        f"chunk {wl.chunk}, entry {['ce_mean', 'ce_sum', 'logprob', 'support'][entry]}"
+                        f"chunk {wl.chunk}, entry {['ce_mean', 'ce_sum', 'logprob', 'support', 'support_kl'][entry]}"
                         + (f", K={wl.k}" if k > 1 else "") + ", forward + backward (dH, dW)",
             "n": wl.n, "hidden": wl.hidden, "vocab": wl.vocab, "chunk": wl.chunk,
             "seed": wl.seed,
@@ -232,18 +244,42 @@ def main():
                       "and loss reduction add <1% next to the tiles kernel)",
         },
     }
+    if entry == workloads.ENTRY_SUPPORT_KL:
+        # the KL-only entry gathers rows instead of contracting over V: its
+        # forward kernel reads one W row per (row, candidate) and H once
+        gather_bytes = 2.0 * wl.n * k * wl.hidden + 2.0 * wl.n * wl.hidden + 12.0 * wl.n * k + 4.0 * wl.n
+        gbs = gather_bytes / (fwd_avg_ms * 1e-3) / 1e9
+        for key in ("tflops_8nvh", "tflops_6nvh_model", "pct_bf16_peak"):
+            out.pop(key)
+        out["metric"] = "KL-only support entry fwd+bwd tokens/s at V=151936, K=64"
+        out["config"]["workload"] = (f"{wl.name}: N={wl.n} tokens, Hd={wl.hidden}, V={wl.vocab}, "
+                                     f"K={k}, entry support_kl (KL(q_ref || p_hat) over the candidates, "
+                                     "no vocabulary-wide pass), forward + backward (dH, dW)")
+        out["roofline"] = {
+            "kernel": "cand_kl_fwd_kernel (one wave per row gathers its K rows of W)",
+            "bound": "hbm",
+            "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": int(gather_bytes),
+            "timing": "HIP events around lmhead_support_kl on its stream (the id scan adds <2%); "
+                      "W rows repeat across rows, so part of the gathered bytes come from the caches",
+        }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds, entry)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(wl, inp, target_s):
+def cpu_baseline(wl, inp, target_s, entry=None):
     """The fp64 oracle, as it stands, on a bounded sample of rows of the same
     workload: for each sampled row the full forward (logits over the whole
     vocabulary, lse, loss) and backward (dL/dz, its dH row and its share of
     every dW row). Throughput is scaled to tokens/s."""
     import oracle
 
+    entry = wl.entry if entry is None else entry
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
     rng = np.random.default_rng(wl.seed + 77)
 
@@ -251,11 +287,14 @@ def cpu_baseline(wl, inp, target_s):
         rows = np.sort(rows)
         t0 = time.perf_counter()
         z = oracle.logits(inp.H, inp.W, rows, threads=threads)
-        if wl.entry in (0, 1):
+        if entry == oracle.ENTRY_SUPPORT_KL:
+            oracle.support_kl_forward(z, inp.ids[rows], inp.ref_logq[rows])
+            dz = oracle.support_dz(z, inp.ids[rows], inp.ref_logq[rows], None, inp.grad_kl[rows])
+        elif entry in (0, 1):
             t = inp.targets[rows]
             f = oracle.ce_forward(z, t, -1, "mean")
             dz = oracle.ce_dz(z, t, 1.0, max(f["count"], 1), "mean")
-        elif wl.entry == 2:
+        elif entry == 2:
             t = inp.targets[rows]
             oracle.logprob_forward(z, t)
             dz = oracle.logprob_dz(z, t, inp.grad[rows])
@@ -281,9 +320,9 @@ def cpu_baseline(wl, inp, target_s):
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{n_rows} rows of the {wl.name} workload (fp64 C oracle: logits over all "
-                  f"{wl.vocab} ids, lse, loss, dL/dz, the rows' dH and their dW contribution over "
-                  f"all vocabulary rows), {dt:.1f}s wall",
+        "sample": f"{n_rows} rows of the {wl.name} workload (fp64 C oracle, entry {entry}: logits "
+                  f"over all {wl.vocab} ids, the entry's outputs, dL/dz, the rows' dH and their dW "
+                  f"contribution over all vocabulary rows), {dt:.1f}s wall",
         "seconds": round(dt, 2),
     }
 
