@@ -22,7 +22,11 @@ def _oracle(entry, inp, num_valid=-1, with_kl=True):
                       grad_kl=inp.grad_kl if with_kl else None, num_valid=num_valid)
 
 
-def _compare(entry, got, ref, label):
+def _compare(entry, got, ref, label, inp=None):
+    """Compare one entry's outputs with the oracle. With the inputs given, dW
+    is checked a second time on the vocabulary rows that are no row's label or
+    candidate, against their own largest magnitude: the label rows dominate
+    max|ref|, so the first check alone would be loose for the others."""
     print(f"[{label}]", flush=True)
     rel_check(f"{label} lse", to_np(got["lse"]), ref["lse"])
     if entry in (lm.ENTRY_CE_MEAN, lm.ENTRY_CE_SUM):
@@ -36,7 +40,14 @@ def _compare(entry, got, ref, label):
     if got.get("dH") is not None:
         grad_check(f"{label} dH", bf16_to_np(got["dH"]), ref["dH"])
     if got.get("dW") is not None:
-        grad_check(f"{label} dW", bf16_to_np(got["dW"]), ref["dW"])
+        gw = bf16_to_np(got["dW"])
+        grad_check(f"{label} dW", gw, ref["dW"])
+        if inp is not None:
+            idx = inp.ids if entry == lm.ENTRY_SUPPORT else inp.targets
+            other = np.ones(gw.shape[0], dtype=bool)
+            other[idx[idx >= 0]] = False
+            if other.any():
+                grad_check(f"{label} dW (non-label rows)", gw[other], ref["dW"][other])
 
 
 def _ragged(entry, **kw):
@@ -54,7 +65,7 @@ def test_tiny_config_ce_mean():
     wl = wlmod.WORKLOADS["tiny"]
     inp = wlmod.make_inputs(wl)
     got = run_entry(Dev(inp), lm.ENTRY_CE_MEAN, wl.chunk)
-    _compare(lm.ENTRY_CE_MEAN, got, _oracle(lm.ENTRY_CE_MEAN, inp), "tiny")
+    _compare(lm.ENTRY_CE_MEAN, got, _oracle(lm.ENTRY_CE_MEAN, inp), "tiny", inp)
 
 
 @pytest.mark.parametrize("entry", [0, 1, 2, 3])
@@ -63,7 +74,7 @@ def test_ragged_all_entries(entry):
     (two chunks, the second 488 wide), 10 % ignored rows."""
     inp = _ragged(entry)
     got = run_entry(Dev(inp), entry, 512)
-    _compare(entry, got, _oracle(entry, inp), f"ragged entry {entry}")
+    _compare(entry, got, _oracle(entry, inp), f"ragged entry {entry}", inp)
 
 
 @pytest.mark.parametrize("shape", [
@@ -76,7 +87,7 @@ def test_ragged_all_entries(entry):
 def test_shapes_ce(shape):
     inp = wlmod.make_inputs(wlmod.custom(seed=300, ignore_frac=0.1, **shape))
     got = run_entry(Dev(inp), lm.ENTRY_CE_MEAN, shape["chunk"])
-    _compare(0, got, _oracle(0, inp), f"shape {shape}")
+    _compare(0, got, _oracle(0, inp), f"shape {shape}", inp)
 
 
 def test_support_without_kl():
@@ -84,13 +95,13 @@ def test_support_without_kl():
     got = run_entry(Dev(inp), 3, 512, with_kl=False)
     ref = _oracle(3, inp, with_kl=False)
     assert got["kl"] is None
-    _compare(3, got, ref, "support no KL")
+    _compare(3, got, ref, "support no KL", inp)
 
 
 def test_given_count_and_sum():
     inp = _ragged(0)
     got = run_entry(Dev(inp), 0, 512, num_valid=1000)
-    _compare(0, got, _oracle(0, inp, num_valid=1000), "given count 1000")
+    _compare(0, got, _oracle(0, inp, num_valid=1000), "given count 1000", inp)
 
 
 # ----------------------------------------------------------- closed forms
