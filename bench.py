@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--kl-only", action="store_true",
                     help="with --workload support: time the KL-only support entry "
                          "(lmhead_support_kl + its backward) instead of the dense one")
+    ap.add_argument("--vendor-line", action="store_true",
+                    help="also time the vendor library's plain bf16 GEMMs (torch.matmul) at the "
+                         "path's shapes, outside the timed region, and report them under vendor_gemm")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run one device-to-device copy of BYTES (counter calibration)")
     return ap.parse_args()
@@ -267,9 +270,56 @@ def main():
             "timing": "HIP events around lmhead_support_kl on its stream (the id scan adds <2%); "
                       "W rows repeat across rows, so part of the gathered bytes come from the caches",
         }
+    if args.vendor_line and entry != workloads.ENTRY_SUPPORT_KL:
+        out["vendor_gemm"] = vendor_gemm(torch, H, W, wl, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds, entry)
     print(json.dumps(out), flush=True)
+
+
+def vendor_gemm(torch, H, W, wl, stream, reps=5):
+    """The vendor library's plain bf16 GEMMs (torch.matmul, i.e. hipBLASLt) at
+    the shapes of the path, for comparison only: the full logits H W^T (bf16
+    output, no epilogue), and per vocabulary chunk the logits, G^T H and G W_c
+    with a random bf16 G. An unfused step built from these GEMMs alone would
+    take at least full + chunks x (chunk logits + dW + dH)."""
+    n, C = wl.n, min(wl.chunk, wl.vocab)
+    g = torch.Generator(device=H.device)
+    g.manual_seed(wl.seed + 5)
+    G = (torch.randn(n, C, device=H.device, generator=g) * 0.01).to(torch.bfloat16)
+    Wc = W[:C]
+
+    def timed(f):
+        with torch.cuda.stream(stream):
+            for _ in range(2):
+                f()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                f()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    full = timed(lambda: torch.matmul(H, W.t()))
+    cl = timed(lambda: torch.matmul(H, Wc.t()))
+    dw = timed(lambda: torch.matmul(G.t(), H))
+    dh = timed(lambda: torch.matmul(G, Wc))
+    chunks = -(-wl.vocab // C)
+    gf = lambda ms, flop: round(flop / (ms * 1e-3) / 1e12, 1)
+    fl_full = 2.0 * n * wl.vocab * wl.hidden
+    fl_c = 2.0 * n * C * wl.hidden
+    rec = {
+        "library": "torch.matmul (hipBLASLt) bf16, plain GEMMs without the path's epilogues",
+        "logits_full_ms": round(full, 4), "logits_full_tflops": gf(full, fl_full),
+        "chunk_logits_us": round(cl * 1e3, 1), "chunk_logits_tflops": gf(cl, fl_c),
+        "dw_chunk_us": round(dw * 1e3, 1), "dw_chunk_tflops": gf(dw, fl_c),
+        "dh_chunk_us": round(dh * 1e3, 1), "dh_chunk_tflops": gf(dh, fl_c),
+        "unfused_step_lower_bound_ms": round(full + chunks * (cl + dw + dh), 3),
+    }
+    log(f"vendor GEMMs: full logits {full:.3f} ms; per chunk logits {cl * 1e3:.1f} us, "
+        f"dW {dw * 1e3:.1f} us, dH {dh * 1e3:.1f} us")
+    return rec
 
 
 def cpu_baseline(wl, inp, target_s, entry=None):
