@@ -235,3 +235,32 @@ def test_more_candidates_than_wave_lanes(k, pad):
                            ref_logq=d.ref_logq, saved_lp=lp2, grad_kl=d.grad_kl, padded=padded)
     torch.cuda.synchronize()
     assert torch.equal(lp, lp2) and torch.equal(kl, kl2) and torch.equal(dH, dH2) and torch.equal(dW, dW2)
+
+
+@pytest.mark.parametrize("pad", [0.0, 0.2])
+def test_maximum_candidate_count(pad):
+    """k = 1024, the largest count the library accepts: sixteen 64-id batches
+    per row in the tile epilogues, the per-row coefficient pass and the
+    KL-only entry's gathers and counting sort, for both the dense support
+    entry and the KL-only one (n = 70: two waves, the second ragged)."""
+    padded = pad > 0.0
+    k = 1024
+    inp = _inputs(n=70, hidden=128, vocab=2500, k=k, seed=790, pad_frac=pad)
+    d = Dev(inp)
+    lp, kl, lse, _ = lm.support_forward(d.H, d.W, d.ids, d.ref_logq, 512, padded=padded)
+    dH, dW = lm.backward(lm.ENTRY_SUPPORT, d.H, d.W, d.ids, lse, d.grad, 512, ref_logq=d.ref_logq,
+                         saved_lp=lp, grad_kl=d.grad_kl, padded=padded)
+    ko = _kl_only(d, padded=padded)
+    torch.cuda.synchronize()
+    ref = oracle.run(3, inp.H, inp.W, ids=inp.ids, ref_logq=inp.ref_logq, grad=inp.grad,
+                     grad_kl=inp.grad_kl, padded=padded)
+    rel_check("lp", to_np(lp), ref["lp"])
+    rel_check("kl", to_np(kl), ref["kl"])
+    rel_check("lse", to_np(lse), ref["lse"])
+    grad_check("dH", bf16_to_np(dH), ref["dH"])
+    grad_check("dW", bf16_to_np(dW), ref["dW"])
+    ref_kl = oracle.run(oracle.ENTRY_SUPPORT_KL, inp.H, inp.W, ids=inp.ids, ref_logq=inp.ref_logq,
+                        grad_kl=inp.grad_kl, padded=padded)
+    rel_check("kl-only kl", to_np(ko["kl"]), ref_kl["kl"])
+    grad_check("kl-only dH", bf16_to_np(ko["dH"]), ref_kl["dH"])
+    grad_check("kl-only dW", bf16_to_np(ko["dW"]), ref_kl["dW"])
