@@ -83,6 +83,7 @@ def test_ragged_all_entries(entry):
     dict(n=257, hidden=320, vocab=777, chunk=256),      # hidden not a multiple of 256
     dict(n=64, hidden=256, vocab=2048, chunk=4096),     # chunk larger than vocab
     dict(n=130, hidden=192, vocab=1537, chunk=768),     # three-tile chunks, 1-wide tail tile
+    dict(n=70, hidden=65536, vocab=300, chunk=256),     # the largest hidden size accepted
 ])
 def test_shapes_ce(shape):
     inp = wlmod.make_inputs(wlmod.custom(seed=300, ignore_frac=0.1, **shape))
