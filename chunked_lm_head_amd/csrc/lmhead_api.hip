@@ -6,6 +6,8 @@
 #include <limits.h>
 #include <string.h>
 
+#include <atomic>
+
 #include <hip/hip_runtime.h>
 
 #include "lmhead.h"
@@ -113,12 +115,17 @@ Temperature temperature_of(const lmhead_problem& p) {
 int check_device() {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return LMHEAD_ERR_DEVICE;
-    static int cache[256];  // 0 unknown, 1 gfx950, 2 other
-    if (dev < 256 && cache[dev] != 0) return cache[dev] == 1 ? LMHEAD_OK : LMHEAD_ERR_DEVICE;
+    // 0 unknown, 1 gfx950, 2 other; atomic so that threads calling at once on
+    // different devices (or the same one) neither race nor tear
+    static std::atomic<int> cache[256];
+    if (dev < 256) {
+        const int known = cache[dev].load(std::memory_order_relaxed);
+        if (known != 0) return known == 1 ? LMHEAD_OK : LMHEAD_ERR_DEVICE;
+    }
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return LMHEAD_ERR_DEVICE;
     const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-    if (dev < 256) cache[dev] = ok ? 1 : 2;
+    if (dev < 256) cache[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
     return ok ? LMHEAD_OK : LMHEAD_ERR_DEVICE;
 }
 
