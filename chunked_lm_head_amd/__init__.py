@@ -24,6 +24,7 @@ Two layers:
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional
 
@@ -245,18 +246,56 @@ def lmhead_read_device_error(workspace, stream=None):
 
 # ------------------------------------------------------------- torch helpers
 
-def _check_inputs(H: torch.Tensor, W: torch.Tensor, idx: torch.Tensor):
+def _check_inputs(H: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, support: bool = False):
+    """H bf16 [n, hidden], W bf16 [vocab, hidden], targets int32 [n] (support:
+    ids int32 [n, k]), contiguous, all on one GPU."""
     for name, t in (("H", H), ("W", W), ("targets/ids", idx)):
         if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
             raise ValueError(f"{name} must be a tensor on a GPU device")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+    if W.device != H.device or idx.device != H.device:
+        raise ValueError("H, W and the targets / ids must be on the same device")
     if H.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
         raise ValueError("H and W must be bfloat16")
     if idx.dtype != torch.int32:
         raise ValueError("targets / candidate ids must be int32")
     if H.dim() != 2 or W.dim() != 2 or H.shape[1] != W.shape[1]:
         raise ValueError("expected H [n, hidden] and W [vocab, hidden]")
+    if support:
+        if idx.dim() != 2 or idx.shape[0] != H.shape[0]:
+            raise ValueError("candidate ids must be int32 [n, k] with n = H.shape[0]")
+    elif idx.dim() != 1 or idx.shape[0] != H.shape[0]:
+        raise ValueError("targets must be int32 [n] with n = H.shape[0]")
+
+
+def _check_f32(name, t, shape, device, required: bool = False):
+    """An fp32 side input (lse, upstream gradients, reference log-probs)."""
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return
+    if not isinstance(t, torch.Tensor) or t.device != device:
+        raise ValueError(f"{name} must be a tensor on the inputs' device")
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)}")
+
+
+def _check_side(entry: int, H, idx, lse, grad, ref_logq, saved_lp, grad_kl):
+    """Shapes of the backward's fp32 side inputs for one entry."""
+    n = H.shape[0]
+    dev = H.device
+    if entry in (ENTRY_CE_MEAN, ENTRY_CE_SUM, ENTRY_LOGPROB):
+        _check_f32("lse", lse, (n,), dev, required=n > 0)
+        _check_f32("grad", grad, (1,) if entry != ENTRY_LOGPROB else (n,), dev, required=n > 0)
+        return
+    k = idx.shape[1]
+    if entry == ENTRY_SUPPORT:
+        _check_f32("lse", lse, (n,), dev, required=n > 0)
+        _check_f32("grad", grad, (n, k), dev)
+    _check_f32("ref_logq", ref_logq, (n, k), dev)
+    _check_f32("saved_lp", saved_lp, (n, k), dev)
+    _check_f32("grad_kl", grad_kl, (n,), dev)
 
 
 def _check_row_temperature(rt, n: int):
@@ -266,6 +305,22 @@ def _check_row_temperature(rt, n: int):
         raise ValueError("row_temperature must be a tensor on a GPU device")
     if rt.dtype != torch.float32 or not rt.is_contiguous() or tuple(rt.shape) != (n,):
         raise ValueError("row_temperature must be a contiguous float32 tensor of shape [n]")
+
+
+def _on_device_of(arg: int):
+    """Run a helper with the device of its positional argument `arg` (H)
+    current, so that the library's device check, its launches and the
+    current-stream lookup all refer to the tensors' GPU."""
+    def wrap(fn):
+        @functools.wraps(fn)
+        def call(*args, **kwargs):
+            t = args[arg] if len(args) > arg else None
+            if isinstance(t, torch.Tensor) and t.device.type == "cuda":
+                with torch.cuda.device(t.device):
+                    return fn(*args, **kwargs)
+            return fn(*args, **kwargs)
+        return call
+    return wrap
 
 
 def workspace(p: lmhead_problem, entry: int, with_backward: bool, device) -> torch.Tensor:
@@ -280,6 +335,7 @@ def _ok(status: int, where: str):
         raise LMHeadError(status, where)
 
 
+@_on_device_of(0)
 def ce_loss_forward(H, W, targets, chunk: int, reduction: str = "mean", num_valid: int = -1,
                     ws: Optional[torch.Tensor] = None, temperature: float = 0.0,
                     row_temperature=None):
@@ -298,6 +354,7 @@ def ce_loss_forward(H, W, targets, chunk: int, reduction: str = "mean", num_vali
     return loss[0], lse, ws
 
 
+@_on_device_of(0)
 def logprob_forward(H, W, targets, chunk: int, ws: Optional[torch.Tensor] = None,
                     temperature: float = 0.0, row_temperature=None):
     """Returns (logp fp32 [n], lse fp32 [n], workspace); lse is of the tempered logits."""
@@ -313,15 +370,17 @@ def logprob_forward(H, W, targets, chunk: int, ws: Optional[torch.Tensor] = None
     return logp, lse, ws
 
 
+@_on_device_of(0)
 def support_forward(H, W, ids, ref_logq, chunk: int, ws: Optional[torch.Tensor] = None,
                     temperature: float = 0.0, row_temperature=None, padded: bool = False):
     """Returns (lp fp32 [n, k], kl fp32 [n] or None, lse fp32 [n], workspace).
     padded: a negative id is a padding slot (LMHEAD_FLAG_PADDED_IDS)."""
-    _check_inputs(H, W, ids)
+    _check_inputs(H, W, ids, support=True)
     n, k = ids.shape
     _check_row_temperature(row_temperature, n)
     p = problem(n, H.shape[1], W.shape[0], chunk, -1, k, FLAG_PADDED_IDS if padded else 0,
                 temperature=temperature, row_temperature=row_temperature)
+    _check_f32("ref_logq", ref_logq, (n, k), H.device)
     if ws is None:
         ws = workspace(p, ENTRY_SUPPORT, False, H.device)
     lp = torch.empty(n, k, dtype=torch.float32, device=H.device)
@@ -332,10 +391,11 @@ def support_forward(H, W, ids, ref_logq, chunk: int, ws: Optional[torch.Tensor] 
     return lp, kl, lse, ws
 
 
+@_on_device_of(0)
 def support_logprob_forward(H, W, ids, chunk: int, ws: Optional[torch.Tensor] = None,
                             temperature: float = 0.0, row_temperature=None, padded: bool = False):
     """Support-set log-probabilities only. Returns (lp fp32 [n, k], lse fp32 [n], workspace)."""
-    _check_inputs(H, W, ids)
+    _check_inputs(H, W, ids, support=True)
     n, k = ids.shape
     _check_row_temperature(row_temperature, n)
     p = problem(n, H.shape[1], W.shape[0], chunk, -1, k, FLAG_PADDED_IDS if padded else 0,
@@ -348,15 +408,17 @@ def support_logprob_forward(H, W, ids, chunk: int, ws: Optional[torch.Tensor] = 
     return lp, lse, ws
 
 
+@_on_device_of(0)
 def support_kl_forward(H, W, ids, ref_logq, ws: Optional[torch.Tensor] = None,
                        temperature: float = 0.0, row_temperature=None, padded: bool = False):
     """KL-only support entry (no vocabulary-wide pass). Returns (kl fp32 [n],
     log p_hat fp32 [n, k], workspace)."""
-    _check_inputs(H, W, ids)
+    _check_inputs(H, W, ids, support=True)
     n, k = ids.shape
     _check_row_temperature(row_temperature, n)
     p = problem(n, H.shape[1], W.shape[0], 256, -1, k, FLAG_PADDED_IDS if padded else 0,
                 temperature=temperature, row_temperature=row_temperature)
+    _check_f32("ref_logq", ref_logq, (n, k), H.device, required=n > 0)
     if ws is None:
         ws = workspace(p, ENTRY_SUPPORT_KL, False, H.device)
     kl = torch.empty(n, dtype=torch.float32, device=H.device)
@@ -365,6 +427,7 @@ def support_kl_forward(H, W, ids, ref_logq, ws: Optional[torch.Tensor] = None,
     return kl, logp_hat, ws
 
 
+@_on_device_of(1)
 def backward(entry: int, H, W, idx, lse, grad, chunk: int, *, ref_logq=None, saved_lp=None,
              grad_kl=None, num_valid: int = -1, need_dH: bool = True, need_dW: bool = True,
              ws: Optional[torch.Tensor] = None, dH=None, dW=None, temperature: float = 0.0,
@@ -372,9 +435,11 @@ def backward(entry: int, H, W, idx, lse, grad, chunk: int, *, ref_logq=None, sav
     """Returns (dH bf16 [n, hidden] or None, dW bf16 [vocab, hidden] or None).
     temperature / row_temperature must be those of the forward that produced lse.
     ENTRY_SUPPORT_KL: saved_lp is the forward's log p_hat; lse and grad are unused."""
-    _check_inputs(H, W, idx)
+    support = entry in (ENTRY_SUPPORT, ENTRY_SUPPORT_KL)
+    _check_inputs(H, W, idx, support=support)
     _check_row_temperature(row_temperature, H.shape[0])
-    k = idx.shape[1] if entry in (ENTRY_SUPPORT, ENTRY_SUPPORT_KL) else 1
+    _check_side(entry, H, idx, lse, grad, ref_logq, saved_lp, grad_kl)
+    k = idx.shape[1] if support else 1
     p = problem(H.shape[0], H.shape[1], W.shape[0], chunk, num_valid, k,
                 FLAG_PADDED_IDS if padded else 0, temperature=temperature,
                 row_temperature=row_temperature)
@@ -399,6 +464,7 @@ def _check_acc(name, t, shape, device):
         raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)}")
 
 
+@_on_device_of(1)
 def backward_accumulate(entry: int, H, W, idx, lse, grad, chunk: int, *, dH_acc=None, dW_acc=None,
                         ref_logq=None, saved_lp=None, grad_kl=None, num_valid: int = -1,
                         out_bf16: bool = False, ws: Optional[torch.Tensor] = None,
@@ -406,11 +472,13 @@ def backward_accumulate(entry: int, H, W, idx, lse, grad, chunk: int, *, dH_acc=
     """dH_acc += dL/dH and dW_acc += dL/dW in fp32 (either may be None).
     Returns (dH, dW): the bf16 casts of the updated accumulators when out_bf16,
     else (None, None)."""
-    _check_inputs(H, W, idx)
+    support = entry in (ENTRY_SUPPORT, ENTRY_SUPPORT_KL)
+    _check_inputs(H, W, idx, support=support)
     _check_row_temperature(row_temperature, H.shape[0])
+    _check_side(entry, H, idx, lse, grad, ref_logq, saved_lp, grad_kl)
     _check_acc("dH_acc", dH_acc, H.shape, H.device)
     _check_acc("dW_acc", dW_acc, W.shape, H.device)
-    k = idx.shape[1] if entry in (ENTRY_SUPPORT, ENTRY_SUPPORT_KL) else 1
+    k = idx.shape[1] if support else 1
     p = problem(H.shape[0], H.shape[1], W.shape[0], chunk, num_valid, k,
                 FLAG_PADDED_IDS if padded else 0, temperature=temperature,
                 row_temperature=row_temperature)

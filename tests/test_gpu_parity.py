@@ -269,3 +269,22 @@ def test_planned_chunk_against_oracle():
     rel_check("loss", [loss.item()], [ref["loss"]])
     grad_check("dH", bf16_to_np(H.grad), ref["dH"])
     grad_check("dW", bf16_to_np(W.grad), ref["dW"])
+
+
+def test_binding_rejects_mismatched_shapes():
+    """The torch helpers refuse targets / ids whose rows do not match H and
+    side inputs of the wrong shape, before anything is launched."""
+    inp = _ragged(0)
+    d = Dev(inp)
+    n = d.H.shape[0]
+    with pytest.raises(ValueError, match="targets"):
+        lm.ce_loss_forward(d.H, d.W, d.t[: n - 1], 512)
+    with pytest.raises(ValueError, match="candidate ids"):
+        lm.support_forward(d.H, d.W, d.t, None, 512)
+    loss, lse, _ = lm.ce_loss_forward(d.H, d.W, d.t, 512)
+    with pytest.raises(ValueError, match="grad"):
+        lm.backward(lm.ENTRY_CE_MEAN, d.H, d.W, d.t, lse, torch.ones(2, device=d.H.device), 512)
+    with pytest.raises(ValueError, match="lse"):
+        lm.backward(lm.ENTRY_CE_MEAN, d.H, d.W, d.t, lse.double(), torch.ones(1, device=d.H.device),
+                    512)
+    torch.cuda.synchronize()
