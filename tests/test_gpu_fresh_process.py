@@ -1,6 +1,6 @@
 """Bitwise determinism across processes: a forward + backward computed in a
 child Python process gives the same bytes (SHA-256 over every output) as the
-same call in this process, for the CE mean and the support entries."""
+same call in this process, for the CE mean, log-prob and support entries."""
 import os
 import subprocess
 import sys
@@ -40,7 +40,7 @@ def _source():
     return _DIGEST.format(root=ROOT, tests=os.path.join(ROOT, "tests"))
 
 
-@pytest.mark.parametrize("entry", [0, 3])
+@pytest.mark.parametrize("entry", [0, 2, 3])
 def test_child_process_gives_the_same_bits(entry):
     ns = {}
     exec(_source(), ns)

@@ -20,7 +20,7 @@ CHUNK = 512
 def _inputs(entry):
     d = dict(n=300, hidden=512, vocab=1000, chunk=CHUNK, seed=900 + entry, ignore_frac=0.1,
              entry=entry)
-    if entry == wlmod.ENTRY_SUPPORT:
+    if entry in (wlmod.ENTRY_SUPPORT, wlmod.ENTRY_SUPPORT_KL):
         d.update(k=16, ignore_frac=0.0)
     return Dev(wlmod.make_inputs(wlmod.custom(**d)))
 
@@ -28,12 +28,17 @@ def _inputs(entry):
 def _step_fn(d, entry):
     n, hidden = d.H.shape
     vocab = d.W.shape[0]
-    k = d.ids.shape[1] if entry == lm.ENTRY_SUPPORT else 1
+    k = d.ids.shape[1] if entry in (lm.ENTRY_SUPPORT, lm.ENTRY_SUPPORT_KL) else 1
     p = lm.problem(n, hidden, vocab, CHUNK, -1, k)
     ws = lm.workspace(p, entry, True, d.H.device)
-    out = dict(lse=torch.empty(n, dtype=torch.float32, device="cuda"),
-               dH=torch.empty_like(d.H), dW=torch.empty_like(d.W))
-    if entry == lm.ENTRY_CE_MEAN:
+    out = dict(dH=torch.empty_like(d.H), dW=torch.empty_like(d.W))
+    if entry != lm.ENTRY_SUPPORT_KL:
+        out["lse"] = torch.empty(n, dtype=torch.float32, device="cuda")
+    if entry == lm.ENTRY_SUPPORT_KL:
+        # the KL-only entry: candidate gathers, integer counting sort in the backward
+        out["kl"] = torch.empty(n, dtype=torch.float32, device="cuda")
+        out["log_phat"] = torch.empty(n, k, dtype=torch.float32, device="cuda")
+    elif entry == lm.ENTRY_CE_MEAN:
         out["loss"] = torch.empty(1, dtype=torch.float32, device="cuda")
     elif entry == lm.ENTRY_LOGPROB:
         out["logp"] = torch.empty(n, dtype=torch.float32, device="cuda")
@@ -42,6 +47,14 @@ def _step_fn(d, entry):
         out["kl"] = torch.empty(n, dtype=torch.float32, device="cuda")
 
     def step():
+        if entry == lm.ENTRY_SUPPORT_KL:
+            st = lm.lmhead_support_kl(p, d.H, d.W, d.ids, d.ref_logq, out["kl"], out["log_phat"], ws,
+                                      ws.numel())
+            assert st == lm.LMHEAD_OK, lm.lmhead_status_string(st)
+            st = lm.lmhead_loss_bwd(p, entry, d.H, d.W, d.ids, d.ref_logq, None, out["log_phat"],
+                                    None, d.grad_kl, out["dH"], out["dW"], ws, ws.numel())
+            assert st == lm.LMHEAD_OK, lm.lmhead_status_string(st)
+            return
         if entry == lm.ENTRY_CE_MEAN:
             st = lm.lmhead_loss_fwd(p, entry, d.H, d.W, d.t, out["loss"], out["lse"], ws, ws.numel())
             idx, ref, saved, gkl = d.t, None, None, None
@@ -60,7 +73,8 @@ def _step_fn(d, entry):
     return step, out, ws
 
 
-@pytest.mark.parametrize("entry", [lm.ENTRY_CE_MEAN, lm.ENTRY_LOGPROB, lm.ENTRY_SUPPORT])
+@pytest.mark.parametrize("entry", [lm.ENTRY_CE_MEAN, lm.ENTRY_LOGPROB, lm.ENTRY_SUPPORT,
+                                   lm.ENTRY_SUPPORT_KL])
 def test_graph_replays_match_eager(entry):
     d = _inputs(entry)
     step, out, ws = _step_fn(d, entry)
