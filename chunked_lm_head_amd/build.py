@@ -48,28 +48,5 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     return LIB
 
 
-C_EXAMPLE_SRC = os.path.join(ROOT, "tests", "c_abi", "ce_roundtrip.cpp")
-C_EXAMPLE = os.path.join(ROOT, "tests", "c_abi", "ce_roundtrip")
-
-
-def build_c_example() -> str:
-    """The C ABI round-trip program the tests run: plain host C++ (g++, the
-    HIP runtime and liblmhead.so), no Python or torch between it and the
-    library."""
-    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
-    cmd = ["g++", "-O2", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE,
-           "-I", os.path.join(rocm, "include"), C_EXAMPLE_SRC, "-L", PKG, "-llmhead",
-           "-L", os.path.join(rocm, "lib"), "-lamdhip64",
-           "-Wl,-rpath,$ORIGIN/../../chunked_lm_head_amd", "-Wl,-rpath," + os.path.join(rocm, "lib"),
-           "-o", C_EXAMPLE + ".tmp"]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("g++ failed to build the C ABI round-trip program")
-    os.replace(C_EXAMPLE + ".tmp", C_EXAMPLE)
-    return C_EXAMPLE
-
-
 if __name__ == "__main__":
     print(build(verbose=True))
-    print(build_c_example())
