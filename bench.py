@@ -247,7 +247,23 @@ def main():
                       "and loss reduction add <1% next to the tiles kernel)",
         },
     }
+    # the backward's three contractions per chunk (recompute, dW, dH: 3 x 2NVHd
+    # flops) as one figure over the whole lmhead_loss_bwd call, which also
+    # holds the row-coefficient pass and every chunk's epilogues
+    bwd_avg_ms = float(np.mean(bwd_ms))
+    bwd_achieved = 3.0 * fwd_flops / (bwd_avg_ms * 1e-3) / 1e12
+    out["roofline_backward"] = {
+        "kernels": "bwd_logit_grad_kernel + bwd_dw_kernel + bwd_dh_kernel, one of each per vocabulary "
+                   "chunk, with the coefficient pass",
+        "bound": "mfma",
+        "achieved": round(bwd_achieved, 2),
+        "peak": BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(bwd_achieved / BF16_PEAK_TFLOPS, 4),
+        "timing": "HIP events around lmhead_loss_bwd on its stream",
+    }
     if entry == workloads.ENTRY_SUPPORT_KL:
+        out.pop("roofline_backward")
         # the KL-only entry gathers rows instead of contracting over V: its
         # forward kernel reads one W row per (row, candidate) and H once
         gather_bytes = 2.0 * wl.n * k * wl.hidden + 2.0 * wl.n * wl.hidden + 12.0 * wl.n * k + 4.0 * wl.n
