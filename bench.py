@@ -234,6 +234,9 @@ def main():
         "pct_bf16_peak": round(100 * tflops / BF16_PEAK_TFLOPS, 2),
         "fwd_ms": round(fwd_avg_ms, 4),
         "bwd_ms": round(float(np.mean(bwd_ms)), 4),
+        "step_ms_events": {"median": round(float(np.median(step_ms)), 4),
+                           "min": round(float(np.min(step_ms)), 4),
+                           "max": round(float(np.max(step_ms)), 4)},
         "deterministic_repeat": deterministic,
         "roofline": {
             "kernel": "fwd_tiles_kernel (logits GEMM + online max/sum-exp epilogue, one launch over all of V)",
