@@ -7,6 +7,9 @@
 #include <string.h>
 
 #include <atomic>
+#include <functional>
+#include <queue>
+#include <vector>
 
 #include <hip/hip_runtime.h>
 
@@ -130,6 +133,45 @@ int check_device() {
 }
 
 int launched() { return hipGetLastError() == hipSuccess ? LMHEAD_OK : LMHEAD_ERR_HIP; }
+
+// The dW and dH contractions of a chunk run as two launches, or as one when
+// that finishes sooner: a launch whose last round of 256 x 256 tiles leaves
+// compute units idle can lend them to the other kind. Estimated in units of
+// one K step of one tile, with one workgroup per compute unit and workgroups
+// starting in launch order on the first free unit (the MI355X has 256; the
+// choice changes only the schedule, never a result).
+constexpr int kComputeUnits = 256;
+
+int64_t rounds_time(int64_t tiles, int64_t steps) { return cdiv(tiles, kComputeUnits) * steps; }
+
+int64_t list_time(int64_t n1, int64_t s1, int64_t n2, int64_t s2) {
+    // finish times of the units, kept sorted: n1 tiles of s1 steps, then n2 of s2
+    std::vector<int64_t> free_at((size_t)kComputeUnits, 0);
+    std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> q(free_at.begin(), free_at.end());
+    int64_t end = 0;
+    auto run = [&](int64_t n, int64_t steps) {
+        for (int64_t i = 0; i < n; ++i) {
+            const int64_t t = q.top() + steps;
+            q.pop();
+            q.push(t);
+            end = t > end ? t : end;
+        }
+    };
+    run(n1, s1);
+    run(n2, s2);
+    return end;
+}
+
+// 1: one launch with the dH tiles first, 0: one launch with the dW tiles
+// first, -1: two launches. One launch only when it saves at least 5 %.
+int dwdh_plan(int64_t n_dw, int64_t k_dw, int64_t n_dh, int64_t k_dh) {
+    // with many rounds the last one's idle units matter little: keep two launches
+    if (n_dw == 0 || n_dh == 0 || n_dw + n_dh > 16 * kComputeUnits) return -1;
+    const int64_t apart = rounds_time(n_dw, k_dw) + rounds_time(n_dh, k_dh);
+    const bool dh_first = k_dh >= k_dw;   // longer tiles first
+    const int64_t together = dh_first ? list_time(n_dh, k_dh, n_dw, k_dw) : list_time(n_dw, k_dw, n_dh, k_dh);
+    return together * 20 <= apart * 19 ? (dh_first ? 1 : 0) : -1;
+}
 
 int grid_1d(int64_t items, int per_block, int cap) {
     int64_t g = cdiv(items, per_block);
@@ -354,8 +396,9 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
         ga.G = G;
         bwd_logit_grad_kernel<<<(unsigned)(ga.tiles_m * ga.tiles_n), kThreads, 0, s>>>(ga);
 
+        DwArgs da{};
+        DhArgs ha{};
         if (want_dw) {
-            DwArgs da;
             da.G = G;
             da.H = (const bf16_bits*)H;
             da.n = L.n;
@@ -368,10 +411,8 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
             da.tiles_n = tiles_hidden;
             da.dW = (bf16_bits*)dW;
             da.dw_acc = dW_acc;
-            bwd_dw_kernel<<<(unsigned)(da.tiles_m * da.tiles_n), kThreads, 0, s>>>(da);
         }
         if (want_dh) {
-            DhArgs ha;
             ha.G = G;
             ha.Wc = Wc;
             ha.width = width;
@@ -386,7 +427,15 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
             ha.keep_acc = dH_acc != nullptr;
             ha.dh_acc = dH_acc != nullptr ? dH_acc : (float*)(w + L.dh_acc);
             ha.dH = (bf16_bits*)dH;
-            bwd_dh_kernel<<<(unsigned)(ha.tiles_m * ha.tiles_n), kThreads, 0, s>>>(ha);
+        }
+        const int64_t n_dw = want_dw ? da.tiles_m * da.tiles_n : 0;
+        const int64_t n_dh = want_dh ? ha.tiles_m * ha.tiles_n : 0;
+        const int plan_one = dwdh_plan(n_dw, L.n_pad / kTileK, n_dh, w_pad / kTileK);
+        if (plan_one >= 0) {
+            bwd_dwdh_kernel<<<(unsigned)(n_dw + n_dh), kThreads, 0, s>>>(da, ha, plan_one);
+        } else {
+            if (want_dw) bwd_dw_kernel<<<(unsigned)n_dw, kThreads, 0, s>>>(da);
+            if (want_dh) bwd_dh_kernel<<<(unsigned)n_dh, kThreads, 0, s>>>(ha);
         }
     }
     return launched();

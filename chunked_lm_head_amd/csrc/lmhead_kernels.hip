@@ -534,10 +534,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
 // K-loop over every row n in ascending order; bf16 store of the fp32 sum.
 // With a caller accumulator the fp32 sum is first added to it (dw_acc +=),
 // and the bf16 output, if any, is the cast of the updated accumulator.
-__global__ __launch_bounds__(kThreads, 1) void bwd_dw_kernel(DwArgs a) {
-    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+__device__ __forceinline__ void dw_tile(const DwArgs& a, int64_t bid, char* smem) {
     int64_t tm, tn;
-    map_tile(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    map_tile(bid, a.tiles_m, a.tiles_n, tm, tn);
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
     AccTile acc;
     // both operands MN-major: G [n_pad, w_pad] and H [n, hidden], k = n
@@ -598,10 +597,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dw_kernel(DwArgs a) {
 // chunk's columns; the fp32 running sum over chunks (chunk order) lives in
 // dh_acc and the last chunk writes the bf16 result. A caller accumulator is
 // dh_acc itself: read from chunk 0 on and stored after the last chunk too.
-__global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(DhArgs a) {
-    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+__device__ __forceinline__ void dh_tile(const DhArgs& a, int64_t bid, char* smem) {
     int64_t tm, tn;
-    map_tile(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    map_tile(bid, a.tiles_m, a.tiles_n, tm, tn);
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
     AccTile acc;
     // B = the chunk of W, MN-major [width, hidden], k = chunk column
@@ -656,6 +654,31 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(DhArgs a) {
         }
         __syncthreads();
     }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void bwd_dw_kernel(DwArgs a) {
+    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+    dw_tile(a, blockIdx.x, smem);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(DhArgs a) {
+    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+    dh_tile(a, blockIdx.x, smem);
+}
+
+// The dW and dH tiles of one chunk in one launch: the first `first_count`
+// workgroups take the kind named by dh_first, the rest the other kind. Each
+// tile is computed exactly as in its own kernel (same code, same K order), so
+// the results do not depend on which launch runs it; the host picks this form
+// when one launch leaves compute units idle that the other kind can fill.
+__global__ __launch_bounds__(kThreads, 1) void bwd_dwdh_kernel(DwArgs dw, DhArgs dh, int dh_first) {
+    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+    const int64_t bid = blockIdx.x;
+    const int64_t n_first = dh_first ? dh.tiles_m * dh.tiles_n : dw.tiles_m * dw.tiles_n;
+    const bool take_dh = dh_first ? bid < n_first : bid >= n_first;
+    const int64_t local = bid < n_first ? bid : bid - n_first;
+    if (take_dh) dh_tile(dh, local, smem);
+    else dw_tile(dw, local, smem);
 }
 
 // out[i] = bf16 (round to nearest even) of in[i]; count is a multiple of 2.

@@ -288,3 +288,20 @@ def test_binding_rejects_mismatched_shapes():
         lm.backward(lm.ENTRY_CE_MEAN, d.H, d.W, d.t, lse.double(), torch.ones(1, device=d.H.device),
                     512)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("entry", [0, 3])
+def test_joint_dw_dh_launch_matches_separate_launches_bitwise(entry):
+    """Small problems run a chunk's dW and dH tiles in one launch (the units
+    one kind leaves idle take tiles of the other); a backward that wants only
+    dH or only dW runs that kind's own kernel. Each tile is the same
+    computation either way, so the results agree bit for bit."""
+    inp = _ragged(entry)
+    d = Dev(inp)
+    both = run_entry(d, entry, 512)
+    only_dh = run_entry(d, entry, 512, need_dW=False)
+    only_dw = run_entry(d, entry, 512, need_dH=False)
+    torch.cuda.synchronize()
+    assert only_dh["dW"] is None and only_dw["dH"] is None
+    assert torch.equal(both["dH"], only_dh["dH"])
+    assert torch.equal(both["dW"], only_dw["dW"])
