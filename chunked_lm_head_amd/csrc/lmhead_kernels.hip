@@ -225,13 +225,17 @@ __global__ void finalize_rows_kernel(FinalizeArgs a) {
     const int sub = (int)(gid % kFinLanes);
     const bool live = row < a.n;                 // whole groups share `live`
     const float2* p = a.part + (live ? row : 0);
+    // unrolled so that eight loads are in flight at once (the loop is
+    // latency-bound otherwise); the per-lane order of the additions is unchanged
     float M = neg_inf();
     if (live)
+#pragma unroll 8
         for (int64_t t = sub; t < a.tiles_n; t += kFinLanes) M = fmaxf(M, p[t * a.n].x);
     M = group_max8(M);
     const float Mb = M * kLog2e;
     float S = 0.0f;
     if (live)
+#pragma unroll 8
         for (int64_t t = sub; t < a.tiles_n; t += kFinLanes) {
             const float2 v = p[t * a.n];
             S += v.y * exp2_fast(__builtin_fmaf(v.x, kLog2e, -Mb));
