@@ -27,8 +27,15 @@ constexpr int64_t kMaxHidden = 65536;
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
+// Per-tile candidate buckets of the dense support entry (hit_count_kernel):
+// one set in the forward's regions and one in the backward's.
+struct HitRegions {
+    size_t counts, cursor, offsets, tsum, tprefix, list;
+};
+
 struct Layout {
     int64_t n, n_pad, hidden, vocab, chunk, w_pad, tiles_v, k;
+    HitRegions hit_fwd, hit_bwd;
     // forward regions
     size_t hdr, lse, part, zg, rows;
     // backward regions
@@ -92,16 +99,28 @@ Layout plan(const lmhead_problem& p, int entry) {
         L.bwd_total = off;
         return L;
     }
+    const bool buckets = entry == LMHEAD_ENTRY_SUPPORT;
+    const int64_t nb = (L.n_pad / kTile) * L.tiles_v;
+    auto take_hits = [&](HitRegions& R) {
+        R.counts = take(4 * nb);
+        R.cursor = take(4 * nb);
+        R.offsets = take(4 * (nb + 1));
+        R.tsum = take(4 * cdiv(nb, kScanTile));
+        R.tprefix = take(4 * (cdiv(nb, kScanTile) + 1));
+        R.list = take(4 * L.n * L.k);
+    };
     L.lse = take(4 * L.n);
     L.part = take(8 * L.tiles_v * L.n);
     L.zg = take(4 * L.n * L.k);
     L.rows = take(4 * L.n);
+    if (buckets) take_hits(L.hit_fwd);
     L.fwd_total = off;
     off = after_hdr;
     L.coef_a = take(4 * L.n_pad);
     L.coef_c = take(4 * L.n * L.k);
     L.G = take(2 * L.n_pad * L.w_pad);
     L.dh_acc = take(4 * L.n * L.hidden);
+    if (buckets) take_hits(L.hit_bwd);
     L.bwd_total = off > L.fwd_total ? off : L.fwd_total;
     return L;
 }
@@ -184,6 +203,35 @@ void fill_u32(void* p, int64_t count, uint32_t value, hipStream_t s) {
     fill_u32_kernel<<<grid_1d(count, kThreads, 4096), kThreads, 0, s>>>((uint32_t*)p, count, value);
 }
 
+// The dense support entry's per-tile candidate buckets: bucket (row tile,
+// vocabulary tile) lists its (row, column, slot) hits in ascending order.
+// Counting uses integer atomics only; the scan and the per-bucket sort make
+// the result independent of their order.
+void build_hits(const Layout& L, const HitRegions& R, char* w, const int32_t* ids, hipStream_t s,
+                const int32_t** offsets_out, const int32_t** list_out) {
+    const int64_t nb = (L.n_pad / kTile) * L.tiles_v;
+    int32_t* counts = (int32_t*)(w + R.counts);
+    int32_t* cursor = (int32_t*)(w + R.cursor);
+    int32_t* offsets = (int32_t*)(w + R.offsets);
+    int32_t* tsum = (int32_t*)(w + R.tsum);
+    int32_t* tprefix = (int32_t*)(w + R.tprefix);
+    int32_t* list = (int32_t*)(w + R.list);
+    fill_u32(counts, nb, 0u, s);
+    fill_u32(cursor, nb, 0u, s);
+    const int64_t nk = L.n * L.k;
+    hit_count_kernel<<<grid_1d(nk, kThreads, 4096), kThreads, 0, s>>>(ids, L.n, (int)L.k, L.vocab, L.tiles_v,
+                                                                      counts);
+    const int64_t tiles = cdiv(nb, kScanTile);
+    tile_sums_kernel<<<(unsigned)tiles, 256, 0, s>>>(counts, nb, tsum);
+    exclusive_scan_kernel<<<1, 1024, 0, s>>>(tsum, tiles, tprefix);
+    scan_tiles_kernel<<<(unsigned)tiles, 256, 0, s>>>(counts, nb, tprefix, tiles, offsets);
+    hit_fill_kernel<<<grid_1d(nk, kThreads, 4096), kThreads, 0, s>>>(ids, L.n, (int)L.k, L.vocab, L.tiles_v,
+                                                                     offsets, cursor, list);
+    bucket_sort_kernel<<<grid_1d(nb, kThreads, 4096), kThreads, 0, s>>>(offsets, nb, list);
+    *offsets_out = offsets;
+    *list_out = list;
+}
+
 // Validation shared by the three forward entries.
 int forward(const lmhead_problem* p, int entry, const void* H, const void* W, const int32_t* ids,
             const float* ref_logq, float* row_out, float* kl, float* lse_out, float* loss,
@@ -231,6 +279,9 @@ int forward(const lmhead_problem* p, int entry, const void* H, const void* W, co
     fa.k = (int)L.k;
     fa.part = (float2*)(w + L.part);
     fa.zg = (float*)(w + L.zg);
+    fa.hit_offsets = nullptr;
+    fa.hit_list = nullptr;
+    if (entry == LMHEAD_ENTRY_SUPPORT) build_hits(L, L.hit_fwd, w, ids, s, &fa.hit_offsets, &fa.hit_list);
     fwd_tiles_kernel<<<(unsigned)(fa.tiles_m * fa.tiles_n), kThreads, 0, s>>>(fa);
 
     FinalizeArgs fin;
@@ -367,6 +418,9 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
     }
 
     bf16_bits* G = (bf16_bits*)(w + L.G);
+    const int32_t* hit_offsets = nullptr;
+    const int32_t* hit_list = nullptr;
+    if (entry == LMHEAD_ENTRY_SUPPORT) build_hits(L, L.hit_bwd, w, ids, s, &hit_offsets, &hit_list);
     const int64_t nchunks = cdiv(L.vocab, L.chunk);
     const int64_t tiles_rows = L.n_pad / kTile;
     const int64_t tiles_hidden = cdiv(L.hidden, kTile);
@@ -394,6 +448,9 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
         ga.k = (int)L.k;
         ga.lse = lse;
         ga.G = G;
+        ga.tiles_v = L.tiles_v;
+        ga.hit_offsets = hit_offsets;
+        ga.hit_list = hit_list;
         bwd_logit_grad_kernel<<<(unsigned)(ga.tiles_m * ga.tiles_n), kThreads, 0, s>>>(ga);
 
         DwArgs da{};

@@ -292,6 +292,34 @@ __global__ void bucket_sort_kernel(const int32_t* offsets, int64_t vocab, int32_
     }
 }
 
+// Hit lists for the tile epilogues of the support entries: count, then fill
+// (positions within a bucket come from an atomic cursor, so the order is
+// arbitrary until bucket_sort_kernel sorts each bucket's packed values).
+__global__ void hit_count_kernel(const int32_t* ids, int64_t n, int k, int64_t vocab, int64_t tiles_v,
+                                 int32_t* counts) {
+    const int64_t nk = n * k;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nk;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t id = ids[i];
+        if (id >= 0 && id < vocab) atomicAdd(counts + (i / k >> 8) * tiles_v + (id >> 8), 1);
+    }
+}
+
+__global__ void hit_fill_kernel(const int32_t* ids, int64_t n, int k, int64_t vocab, int64_t tiles_v,
+                                const int32_t* offsets, int32_t* cursor, int32_t* list) {
+    const int64_t nk = n * k;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nk;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t id = ids[i];
+        if (id < 0 || id >= vocab) continue;
+        const int64_t row = i / k;
+        const int kk = (int)(i - row * k);
+        const int64_t b = (row >> 8) * tiles_v + (id >> 8);
+        list[offsets[b] + atomicAdd(cursor + b, 1)] =
+            (int32_t)(((row & 255) << kHitRowShift) | ((id & 255) << kHitColShift) | kk);
+    }
+}
+
 // dW[v] = sum over the entries (n, k) with id_nk = v, in ascending (n, k)
 // order, of c_nk H[n]; rows no candidate lists get 0. One wave per row v.
 __global__ __launch_bounds__(kThreads) void cand_dw_kernel(CandBwdArgs a) {

@@ -49,6 +49,11 @@ struct FwdTilesArgs {
     float2* part;         // [tiles_n, n] (max, sum) per (tile, row)
     float* zg;            // [n, k] logits at the ids
     Temperature T;
+    // k > 1: the candidate ids bucketed by (row tile, vocabulary tile), see
+    // hit_count_kernel; bucket b's entries are hit_list[hit_offsets[b] ..
+    // hit_offsets[b + 1])
+    const int32_t* hit_offsets;
+    const int32_t* hit_list;
 };
 
 struct FinalizeArgs {
@@ -96,6 +101,9 @@ struct LogitGradArgs {
     const float* lse;
     bf16_bits* G;          // [n_pad, w_pad]
     Temperature T;
+    int64_t tiles_v;       // vocabulary tiles of the whole vocabulary (bucket index)
+    const int32_t* hit_offsets;   // k > 1: as in FwdTilesArgs
+    const int32_t* hit_list;
 };
 
 struct DwArgs {
@@ -173,6 +181,17 @@ __global__ void scan_tiles_kernel(const int32_t* counts, int64_t vocab, const in
 __global__ void cand_fill_kernel(const int32_t* ids, int64_t nk, int64_t vocab, const int32_t* offsets,
                                  int32_t* cursor, int32_t* list);
 __global__ void bucket_sort_kernel(const int32_t* offsets, int64_t vocab, int32_t* list);
+
+// Per-tile hit lists of the support entries. Entry (n, kk) with a valid id
+// goes to bucket (n / 256) * tiles_v + id / 256 as the packed value
+// (n % 256) << 18 | (id % 256) << 10 | kk, so a bucket sorted ascending lists
+// its hits by row, then column, then slot.
+constexpr int kHitRowShift = 18;
+constexpr int kHitColShift = 10;
+__global__ void hit_count_kernel(const int32_t* ids, int64_t n, int k, int64_t vocab, int64_t tiles_v,
+                                 int32_t* counts);
+__global__ void hit_fill_kernel(const int32_t* ids, int64_t n, int k, int64_t vocab, int64_t tiles_v,
+                                const int32_t* offsets, int32_t* cursor, int32_t* list);
 __global__ void cand_dw_kernel(CandBwdArgs a);
 __global__ void f32_to_bf16_kernel(const float* in, int64_t count, bf16_bits* out);
 

@@ -80,52 +80,17 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t count, uint32_t value) {
         p[i] = value;
 }
 
-// Scans of the rows' candidate ids against a tile's columns [col0, col0 +
-// ncol). The differences are taken modulo 2^32: with 0 <= col0 < 2^30 an id
-// lands in [0, ncol) exactly when id - col0 does over the integers. A row has
-// about k * 256 / V hits per tile, so the per-id cost is what matters.
-//
-// k = 1: each thread checks its own row's id.
+// A row's label against a tile's columns [col0, col0 + ncol) (k = 1: each
+// thread checks its own row's id). The difference is taken modulo 2^32: with
+// 0 <= col0 < 2^30 an id lands in [0, ncol) exactly when id - col0 does over
+// the integers. For k > 1 the tiles read their hits from per-tile buckets
+// built before the launch (hit_count_kernel, hit_fill_kernel): a row has about
+// k * 256 / V hits per tile, so scanning every id in every tile cost more
+// than the hits themselves.
 __device__ __forceinline__ bool id_in_tile(const int32_t* idr, uint32_t col0, int ncol, int& j) {
     const uint32_t d = (uint32_t)idr[0] - col0;
     j = (int)d;
     return d < (uint32_t)ncol;
-}
-
-// k > 1: the wave walks its 64 rows (row0 + 0..63), 16 at a time. The lanes
-// load a row's ids at slots k0 + lane, so each load instruction reads one
-// row's contiguous ids instead of one id from each of 64 rows; the hits of
-// a row (a ballot) are visited in ascending slot order by the row's own lane
-// (lane r holds row row0 + r), as visit(slot, column within the tile). Every
-// lane of the wave must call it.
-template <class Visit>
-__device__ __forceinline__ void scan_ids_wave(const int32_t* ids, int64_t row0, int64_t n, int k,
-                                              uint32_t col0, int ncol, int lane, Visit visit) {
-#pragma unroll 1
-    for (int r0 = 0; r0 < 64; r0 += 16) {
-        if (row0 + r0 >= n) break;
-#pragma unroll 1
-        for (int k0 = 0; k0 < k; k0 += 64) {
-            const bool slot_ok = k0 + lane < k;
-            const int kk = slot_ok ? k0 + lane : k - 1;
-            uint32_t d[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int64_t row = row0 + r0 + i < n ? row0 + r0 + i : n - 1;
-                d[i] = (uint32_t)ids[row * k + kk] - col0;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                uint64_t hits = __ballot(slot_ok && row0 + r0 + i < n && d[i] < (uint32_t)ncol);
-                while (hits != 0u) {
-                    const int b = __builtin_ctzll(hits);
-                    hits &= hits - 1u;
-                    const int j = __builtin_amdgcn_readlane((int)d[i], b);
-                    if (lane == r0 + i) visit(k0 + b, j);
-                }
-            }
-        }
-    }
 }
 
 // ------------------------------------------------------------- forward tiles
@@ -186,12 +151,23 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTilesArgs a) 
             run_s = run_s * exp2_fast((run_m - M) * kLog2e) + s * exp2_fast((m - M) * kLog2e);
             run_m = M;
         }
-        auto gather = [&](int kk, int j) { a.zg[row * a.k + kk] = Sr[j * kEpiStride] * inv_tau; };
         if (a.k == 1) {
             int j;
-            if (row_ok && id_in_tile(a.ids + row, (uint32_t)col0, ncol, j)) gather(0, j);
+            if (row_ok && id_in_tile(a.ids + row, (uint32_t)col0, ncol, j))
+                a.zg[row] = Sr[j * kEpiStride] * inv_tau;
         } else {
-            scan_ids_wave(a.ids, m0 + wave * 64, a.n, a.k, (uint32_t)col0, ncol, lane, gather);
+            // the tile's hits from its bucket, one thread per entry: every
+            // (row, slot) has one entry, so each zg element has one writer
+            const int64_t b = tm * a.tiles_n + tn;
+            const int32_t e1 = a.hit_offsets[b + 1];
+            for (int32_t i = a.hit_offsets[b] + tid; i < e1; i += kThreads) {
+                const int32_t e = a.hit_list[i];
+                const int c = (e >> kHitColShift) & 255;
+                if ((c >> 7) != half) continue;
+                const int r = e >> kHitRowShift;
+                const int64_t rw = m0 + r;
+                a.zg[rw * a.k + (e & 1023)] = S[(c & 127) * kEpiStride + r] * (1.0f / row_tau(a.T, rw));
+            }
         }
         __syncthreads();
     }
@@ -257,16 +233,19 @@ __global__ void finalize_rows_kernel(FinalizeArgs a) {
         return;
     }
     // support entry; in padded lists a negative id is a padding slot (lp = 0,
-    // no part in p_hat or the KL)
+    // no part in p_hat or the KL). The loops over the row's k candidates are
+    // unrolled so that their loads overlap; each sum keeps ascending k order.
     const int k = a.k;
     const int32_t* idr = a.ids + row * k;
     const float* zc = a.zg + row * k;
     bool bad = bad_tau;
+#pragma unroll 8
     for (int kk = 0; kk < k; ++kk) {
         const int64_t id = idr[kk];
         bad = bad || id >= a.vocab || (id < 0 && !a.padded);
     }
     float* lp = a.row_out + row * k;
+#pragma unroll 8
     for (int kk = 0; kk < k; ++kk) lp[kk] = bad ? quiet_nan() : (idr[kk] < 0 ? 0.0f : zc[kk] - lse);
     if (a.kl != nullptr) {
         if (bad) {
@@ -275,14 +254,17 @@ __global__ void finalize_rows_kernel(FinalizeArgs a) {
         }
         // log p_hat_k = z_k - log sum_j exp z_j over the listed candidates
         float mx = neg_inf();
+#pragma unroll 8
         for (int kk = 0; kk < k; ++kk)
             if (idr[kk] >= 0) mx = fmaxf(mx, zc[kk]);
         float se = 0.0f;
+#pragma unroll 8
         for (int kk = 0; kk < k; ++kk)
             if (idr[kk] >= 0) se += expf(zc[kk] - mx);
         const float ls = mx + logf(se);
         const float* r = a.ref_logq + row * k;
         float kl = 0.0f;
+#pragma unroll 8
         for (int kk = 0; kk < k; ++kk) {
             const float q = expf(r[kk]);
             if (idr[kk] >= 0 && q > 0.0f) kl += q * (r[kk] - (zc[kk] - ls));
@@ -495,12 +477,31 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
         const int64_t rem = a.width - col0;
         const int ncol = rem <= 0 ? 0 : (rem >= 128 ? 128 : (int)rem);
         // c_nk at the row's ids in the tile, in ascending k
-        auto add_c = [&](int kk, int j) { Sr[j * kEpiStride] += a.coef_c[row * a.k + kk]; };
         if (a.k == 1) {
             int j;
-            if (row_ok && id_in_tile(a.ids + row, (uint32_t)(a.v0 + col0), ncol, j)) add_c(0, j);
+            if (row_ok && id_in_tile(a.ids + row, (uint32_t)(a.v0 + col0), ncol, j))
+                Sr[j * kEpiStride] += a.coef_c[row];
         } else {
-            scan_ids_wave(a.ids, m0 + wave * 64, a.n, a.k, (uint32_t)(a.v0 + col0), ncol, lane, add_c);
+            // the tile's bucket lists its hits by row, column, slot: the first
+            // entry of each (row, column) run adds the run's c_nk in ascending
+            // slot order, so every element has one writer and a fixed order
+            const int64_t b = tm * a.tiles_v + (a.v0 >> 8) + tn;
+            const int32_t e0 = a.hit_offsets[b], e1 = a.hit_offsets[b + 1];
+            for (int32_t i = e0 + tid; i < e1; i += kThreads) {
+                const int32_t key = a.hit_list[i] >> kHitColShift;   // row << 8 | column
+                if (i > e0 && (a.hit_list[i - 1] >> kHitColShift) == key) continue;
+                const int c = key & 255;
+                if ((c >> 7) != half) continue;
+                const int r = key >> 8;
+                float* dst = S + (c & 127) * kEpiStride + r;
+                float v = *dst;
+                for (int32_t i2 = i; i2 < e1; ++i2) {
+                    const int32_t e = a.hit_list[i2];
+                    if ((e >> kHitColShift) != key) break;
+                    v += a.coef_c[(m0 + r) * a.k + (e & 1023)];
+                }
+                *dst = v;
+            }
         }
         __syncthreads();
         if (a.G != nullptr) {
