@@ -275,11 +275,31 @@ __global__ void cand_fill_kernel(const int32_t* ids, int64_t nk, int64_t vocab, 
     }
 }
 
-// Sort each bucket ascending (insertion sort; buckets hold few entries).
-__global__ void bucket_sort_kernel(const int32_t* offsets, int64_t vocab, int32_t* list) {
-    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < vocab;
-         v += (int64_t)gridDim.x * blockDim.x) {
-        const int32_t b = offsets[v], e = offsets[v + 1];
+// Sort each bucket ascending. One wave per bucket: a bucket of up to 64
+// entries is sorted across the lanes by a bitonic network (lanes past the
+// bucket hold INT_MAX, above every entry); a larger one, which a skewed id
+// distribution can produce, by an insertion sort in lane 0. Entries are
+// distinct, so the result is the unique ascending order either way.
+__global__ __launch_bounds__(256) void bucket_sort_kernel(const int32_t* offsets, int64_t buckets, int32_t* list) {
+    const int lane = threadIdx.x & 63;
+    const int64_t v = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+    if (v >= buckets) return;   // the whole wave
+    const int32_t b = offsets[v], e = offsets[v + 1];
+    const int32_t cnt = e - b;
+    if (cnt <= 1) return;
+    if (cnt <= 64) {
+        int32_t x = lane < cnt ? list[b + lane] : INT_MAX;
+#pragma unroll
+        for (int k = 2; k <= 64; k <<= 1)
+#pragma unroll
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                const int32_t y = __shfl_xor(x, j);
+                const bool up = (lane & k) == 0;      // this pair's sequence sorts ascending
+                const bool lower = (lane & j) == 0;   // the pair's lower lane
+                x = (lower == up) ? (x < y ? x : y) : (x < y ? y : x);
+            }
+        if (lane < cnt) list[b + lane] = x;
+    } else if (lane == 0) {
         for (int32_t i = b + 1; i < e; ++i) {
             const int32_t x = list[i];
             int32_t j = i - 1;

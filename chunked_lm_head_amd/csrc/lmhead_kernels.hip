@@ -217,11 +217,12 @@ __global__ void finalize_rows_kernel(FinalizeArgs a) {
             S += v.y * exp2_fast(__builtin_fmaf(v.x, kLog2e, -Mb));
         }
     S = group_sum8(S);
-    if (!live || sub != 0) return;
-    const float lse = M + logf(S);
-    a.lse[row] = lse;
+    if (!live) return;
+    const float lse = M + logf(S);   // every lane of the group holds the same M and S
     const bool bad_tau = a.T.row != nullptr && !tau_ok(row_tau(a.T, row));
     if (a.entry == kEntryCeMean || a.entry == kEntryCeSum || a.entry == kEntryLogprob) {
+        if (sub != 0) return;
+        a.lse[row] = lse;
         const int64_t t = a.ids[row];
         const bool bad = t >= a.vocab || bad_tau;
         const bool valid = t >= 0 && !bad;
@@ -233,43 +234,45 @@ __global__ void finalize_rows_kernel(FinalizeArgs a) {
         return;
     }
     // support entry; in padded lists a negative id is a padding slot (lp = 0,
-    // no part in p_hat or the KL). The loops over the row's k candidates are
-    // unrolled so that their loads overlap; each sum keeps ascending k order.
+    // no part in p_hat or the KL). The group's eight lanes share the row's k
+    // slots (lane sub takes kk = sub, sub + 8, ... in ascending order) and
+    // combine their partial max / sums with the fixed xor pairing above.
+    if (sub == 0) a.lse[row] = lse;
     const int k = a.k;
     const int32_t* idr = a.ids + row * k;
     const float* zc = a.zg + row * k;
-    bool bad = bad_tau;
-#pragma unroll 8
-    for (int kk = 0; kk < k; ++kk) {
+    bool bad_own = false;
+    for (int kk = sub; kk < k; kk += kFinLanes) {
         const int64_t id = idr[kk];
-        bad = bad || id >= a.vocab || (id < 0 && !a.padded);
+        bad_own = bad_own || id >= a.vocab || (id < 0 && !a.padded);
     }
+    const bool bad = bad_tau || group_max8(bad_own ? 1.0f : 0.0f) != 0.0f;
     float* lp = a.row_out + row * k;
-#pragma unroll 8
-    for (int kk = 0; kk < k; ++kk) lp[kk] = bad ? quiet_nan() : (idr[kk] < 0 ? 0.0f : zc[kk] - lse);
+    for (int kk = sub; kk < k; kk += kFinLanes)
+        lp[kk] = bad ? quiet_nan() : (idr[kk] < 0 ? 0.0f : zc[kk] - lse);
     if (a.kl != nullptr) {
         if (bad) {
-            a.kl[row] = quiet_nan();
+            if (sub == 0) a.kl[row] = quiet_nan();
             return;
         }
         // log p_hat_k = z_k - log sum_j exp z_j over the listed candidates
         float mx = neg_inf();
-#pragma unroll 8
-        for (int kk = 0; kk < k; ++kk)
+        for (int kk = sub; kk < k; kk += kFinLanes)
             if (idr[kk] >= 0) mx = fmaxf(mx, zc[kk]);
+        mx = group_max8(mx);
         float se = 0.0f;
-#pragma unroll 8
-        for (int kk = 0; kk < k; ++kk)
+        for (int kk = sub; kk < k; kk += kFinLanes)
             if (idr[kk] >= 0) se += expf(zc[kk] - mx);
+        se = group_sum8(se);
         const float ls = mx + logf(se);
         const float* r = a.ref_logq + row * k;
         float kl = 0.0f;
-#pragma unroll 8
-        for (int kk = 0; kk < k; ++kk) {
+        for (int kk = sub; kk < k; kk += kFinLanes) {
             const float q = expf(r[kk]);
             if (idr[kk] >= 0 && q > 0.0f) kl += q * (r[kk] - (zc[kk] - ls));
         }
-        a.kl[row] = kl;
+        kl = group_sum8(kl);
+        if (sub == 0) a.kl[row] = kl;
     }
 }
 
