@@ -227,7 +227,7 @@ void build_hits(const Layout& L, const HitRegions& R, char* w, const int32_t* id
     scan_tiles_kernel<<<(unsigned)tiles, 256, 0, s>>>(counts, nb, tprefix, tiles, offsets);
     hit_fill_kernel<<<grid_1d(nk, kThreads, 4096), kThreads, 0, s>>>(ids, L.n, (int)L.k, L.vocab, L.tiles_v,
                                                                      offsets, cursor, list);
-    bucket_sort_kernel<<<(unsigned)cdiv(nb, kThreads / 64), kThreads, 0, s>>>(offsets, nb, list);
+    bucket_sort_wave_kernel<<<(unsigned)cdiv(nb, kThreads / 64), kThreads, 0, s>>>(offsets, nb, list);
     *offsets_out = offsets;
     *list_out = list;
 }
@@ -410,8 +410,8 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
             scan_tiles_kernel<<<(unsigned)tiles, 256, 0, s>>>(counts, L.vocab, tprefix, tiles, offsets);
             cand_fill_kernel<<<grid_1d(nk, kThreads, 4096), kThreads, 0, s>>>(ids, nk, L.vocab, offsets,
                                                                               cursor, list);
-            bucket_sort_kernel<<<(unsigned)cdiv(L.vocab, kThreads / 64), kThreads, 0, s>>>(offsets, L.vocab,
-                                                                                          list);
+            bucket_sort_kernel<<<grid_1d(L.vocab, kThreads, 4096), kThreads, 0, s>>>(offsets, L.vocab,
+                                                                                     list);
             cand_dw_kernel<<<(unsigned)cdiv(L.vocab, kThreads / 64), kThreads, 0, s>>>(cb);
         }
         return launched();

@@ -275,12 +275,33 @@ __global__ void cand_fill_kernel(const int32_t* ids, int64_t nk, int64_t vocab, 
     }
 }
 
-// Sort each bucket ascending. One wave per bucket: a bucket of up to 64
-// entries is sorted across the lanes by a bitonic network (lanes past the
-// bucket hold INT_MAX, above every entry); a larger one, which a skewed id
-// distribution can produce, by an insertion sort in lane 0. Entries are
-// distinct, so the result is the unique ascending order either way.
-__global__ __launch_bounds__(256) void bucket_sort_kernel(const int32_t* offsets, int64_t buckets, int32_t* list) {
+// Sort each bucket ascending, one thread per bucket (insertion sort): for
+// the vocabulary buckets of the KL-only entry, which hold N·K / V entries
+// (a few) on average.
+__global__ void bucket_sort_kernel(const int32_t* offsets, int64_t buckets, int32_t* list) {
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < buckets;
+         v += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t b = offsets[v], e = offsets[v + 1];
+        for (int32_t i = b + 1; i < e; ++i) {
+            const int32_t x = list[i];
+            int32_t j = i - 1;
+            while (j >= b && list[j] > x) {
+                list[j + 1] = list[j];
+                --j;
+            }
+            list[j + 1] = x;
+        }
+    }
+}
+
+// The same, one wave per bucket: a bucket of up to 64 entries is sorted
+// across the lanes by a bitonic network (lanes past the bucket hold INT_MAX,
+// above every entry); a larger one, which a skewed id distribution can
+// produce, by an insertion sort in lane 0. For the per-tile hit buckets,
+// which hold tens of entries. Entries are distinct, so the result is the
+// unique ascending order either way.
+__global__ __launch_bounds__(256) void bucket_sort_wave_kernel(const int32_t* offsets, int64_t buckets,
+                                                               int32_t* list) {
     const int lane = threadIdx.x & 63;
     const int64_t v = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
     if (v >= buckets) return;   // the whole wave

@@ -181,6 +181,7 @@ __global__ void scan_tiles_kernel(const int32_t* counts, int64_t vocab, const in
 __global__ void cand_fill_kernel(const int32_t* ids, int64_t nk, int64_t vocab, const int32_t* offsets,
                                  int32_t* cursor, int32_t* list);
 __global__ void bucket_sort_kernel(const int32_t* offsets, int64_t buckets, int32_t* list);
+__global__ void bucket_sort_wave_kernel(const int32_t* offsets, int64_t buckets, int32_t* list);
 
 // Per-tile hit lists of the support entries. Entry (n, kk) with a valid id
 // goes to bucket (n / 256) * tiles_v + id / 256 as the packed value
