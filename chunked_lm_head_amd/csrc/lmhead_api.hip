@@ -30,7 +30,7 @@ int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 // Per-tile candidate buckets of the dense support entry (hit_count_kernel):
 // one set in the forward's regions and one in the backward's.
 struct HitRegions {
-    size_t counts, cursor, offsets, tsum, tprefix, list;
+    size_t counts, cursor, offsets, tsum, tprefix, list, large, n_large;
 };
 
 struct Layout {
@@ -41,7 +41,7 @@ struct Layout {
     // backward regions
     size_t coef_a, coef_c, G, dh_acc;
     // backward of the KL-only entry: inverse index of the candidate ids
-    size_t counts, offsets, cursor, list, tsum, tprefix;
+    size_t counts, offsets, cursor, list, tsum, tprefix, large, n_large, pieces, piece_off, partial;
     size_t fwd_total, bwd_total;
 };
 
@@ -96,6 +96,12 @@ Layout plan(const lmhead_problem& p, int entry) {
         L.list = take(4 * L.n * L.k);
         L.tsum = take(4 * cdiv(L.vocab, kScanTile));
         L.tprefix = take(4 * (cdiv(L.vocab, kScanTile) + 1));
+        L.large = take(4 * L.vocab);
+        L.n_large = take(4);
+        // split pieces of large dW buckets: at most 2 N k / kDwSplitEntries of them
+        L.pieces = take(4 * L.vocab);
+        L.piece_off = take(4 * (L.vocab + 1));
+        L.partial = take(4 * (2 * L.n * L.k / kDwSplitEntries + 1) * L.hidden);
         L.bwd_total = off;
         return L;
     }
@@ -108,6 +114,8 @@ Layout plan(const lmhead_problem& p, int entry) {
         R.tsum = take(4 * cdiv(nb, kScanTile));
         R.tprefix = take(4 * (cdiv(nb, kScanTile) + 1));
         R.list = take(4 * L.n * L.k);
+        R.large = take(4 * nb);
+        R.n_large = take(4);
     };
     L.lse = take(4 * L.n);
     L.part = take(8 * L.tiles_v * L.n);
@@ -160,6 +168,10 @@ int launched() { return hipGetLastError() == hipSuccess ? LMHEAD_OK : LMHEAD_ERR
 // starting in launch order on the first free unit (the MI355X has 256; the
 // choice changes only the schedule, never a result).
 constexpr int kComputeUnits = 256;
+// workgroups of bucket_sort_block_kernel (each loops over the listed large buckets)
+constexpr int kSortBlocks = 512;
+// workgroups of the split dW kernels (each loops over its share of the pieces / buckets)
+constexpr int kSplitBlocks = 1024;
 
 int64_t rounds_time(int64_t tiles, int64_t steps) { return cdiv(tiles, kComputeUnits) * steps; }
 
@@ -227,7 +239,12 @@ void build_hits(const Layout& L, const HitRegions& R, char* w, const int32_t* id
     scan_tiles_kernel<<<(unsigned)tiles, 256, 0, s>>>(counts, nb, tprefix, tiles, offsets);
     hit_fill_kernel<<<grid_1d(nk, kThreads, 4096), kThreads, 0, s>>>(ids, L.n, (int)L.k, L.vocab, L.tiles_v,
                                                                      offsets, cursor, list);
-    bucket_sort_wave_kernel<<<(unsigned)cdiv(nb, kThreads / 64), kThreads, 0, s>>>(offsets, nb, list);
+    int32_t* large = (int32_t*)(w + R.large);
+    int32_t* n_large = (int32_t*)(w + R.n_large);
+    fill_u32(n_large, 1, 0u, s);
+    bucket_sort_wave_kernel<<<(unsigned)cdiv(nb, kThreads / 64), kThreads, 0, s>>>(offsets, nb, list, large,
+                                                                                  n_large);
+    bucket_sort_block_kernel<<<kSortBlocks, 1024, 0, s>>>(offsets, list, large, n_large);
     *offsets_out = offsets;
     *list_out = list;
 }
@@ -410,9 +427,24 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
             scan_tiles_kernel<<<(unsigned)tiles, 256, 0, s>>>(counts, L.vocab, tprefix, tiles, offsets);
             cand_fill_kernel<<<grid_1d(nk, kThreads, 4096), kThreads, 0, s>>>(ids, nk, L.vocab, offsets,
                                                                               cursor, list);
-            bucket_sort_kernel<<<grid_1d(L.vocab, kThreads, 4096), kThreads, 0, s>>>(offsets, L.vocab,
-                                                                                     list);
+            int32_t* large = (int32_t*)(w + L.large);
+            int32_t* n_large = (int32_t*)(w + L.n_large);
+            fill_u32(n_large, 1, 0u, s);
+            bucket_sort_kernel<<<grid_1d(L.vocab, kThreads, 4096), kThreads, 0, s>>>(offsets, L.vocab, list,
+                                                                                     large, n_large);
+            bucket_sort_block_kernel<<<kSortBlocks, 1024, 0, s>>>(offsets, list, large, n_large);
             cand_dw_kernel<<<(unsigned)cdiv(L.vocab, kThreads / 64), kThreads, 0, s>>>(cb);
+            // buckets above kDwSplitEntries entries: pieces, their offsets, partial rows, join
+            int32_t* pieces = (int32_t*)(w + L.pieces);
+            int32_t* piece_off = (int32_t*)(w + L.piece_off);
+            float* partial = (float*)(w + L.partial);
+            cand_split_counts_kernel<<<grid_1d(L.vocab, kThreads, 4096), kThreads, 0, s>>>(offsets, large, n_large,
+                                                                                           L.vocab, pieces);
+            tile_sums_kernel<<<(unsigned)tiles, 256, 0, s>>>(pieces, L.vocab, tsum);
+            exclusive_scan_kernel<<<1, 1024, 0, s>>>(tsum, tiles, tprefix);
+            scan_tiles_kernel<<<(unsigned)tiles, 256, 0, s>>>(pieces, L.vocab, tprefix, tiles, piece_off);
+            cand_dw_split_kernel<<<kSplitBlocks, kThreads, 0, s>>>(cb, large, n_large, piece_off, partial);
+            cand_dw_join_kernel<<<kSplitBlocks, kThreads, 0, s>>>(cb, large, n_large, piece_off, partial);
         }
         return launched();
     }

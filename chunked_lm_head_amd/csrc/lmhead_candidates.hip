@@ -275,13 +275,24 @@ __global__ void cand_fill_kernel(const int32_t* ids, int64_t nk, int64_t vocab, 
     }
 }
 
-// Sort each bucket ascending, one thread per bucket (insertion sort): for
-// the vocabulary buckets of the KL-only entry, which hold N·K / V entries
-// (a few) on average.
-__global__ void bucket_sort_kernel(const int32_t* offsets, int64_t buckets, int32_t* list) {
+// Sorting the buckets ascending (entries are distinct, so the ascending order
+// is unique and the result does not depend on how it is reached). Small
+// buckets are sorted where they are found; larger ones are appended to a list
+// (an integer atomic fixes only the list's order, not the result) and sorted
+// by bucket_sort_block_kernel, one workgroup per bucket.
+constexpr int kSortLdsMax = 32768;   // entries a workgroup sorts in LDS (128 KB)
+
+// One thread per bucket: insertion sort for up to 16 entries, the vocabulary
+// buckets of the KL-only entry holding N·K / V (a few) on average.
+__global__ void bucket_sort_kernel(const int32_t* offsets, int64_t buckets, int32_t* list, int32_t* large,
+                                   int32_t* n_large) {
     for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < buckets;
          v += (int64_t)gridDim.x * blockDim.x) {
         const int32_t b = offsets[v], e = offsets[v + 1];
+        if (e - b > 16) {
+            large[atomicAdd(n_large, 1)] = (int32_t)v;
+            continue;
+        }
         for (int32_t i = b + 1; i < e; ++i) {
             const int32_t x = list[i];
             int32_t j = i - 1;
@@ -294,42 +305,83 @@ __global__ void bucket_sort_kernel(const int32_t* offsets, int64_t buckets, int3
     }
 }
 
-// The same, one wave per bucket: a bucket of up to 64 entries is sorted
-// across the lanes by a bitonic network (lanes past the bucket hold INT_MAX,
-// above every entry); a larger one, which a skewed id distribution can
-// produce, by an insertion sort in lane 0. For the per-tile hit buckets,
-// which hold tens of entries. Entries are distinct, so the result is the
-// unique ascending order either way.
+// One wave per bucket: up to 64 entries sorted across the lanes by a bitonic
+// network (lanes past the bucket hold INT_MAX, above every entry): the
+// per-tile hit buckets, which hold tens of entries.
 __global__ __launch_bounds__(256) void bucket_sort_wave_kernel(const int32_t* offsets, int64_t buckets,
-                                                               int32_t* list) {
+                                                               int32_t* list, int32_t* large,
+                                                               int32_t* n_large) {
     const int lane = threadIdx.x & 63;
     const int64_t v = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
     if (v >= buckets) return;   // the whole wave
     const int32_t b = offsets[v], e = offsets[v + 1];
     const int32_t cnt = e - b;
     if (cnt <= 1) return;
-    if (cnt <= 64) {
-        int32_t x = lane < cnt ? list[b + lane] : INT_MAX;
+    if (cnt > 64) {
+        if (lane == 0) large[atomicAdd(n_large, 1)] = (int32_t)v;
+        return;
+    }
+    int32_t x = lane < cnt ? list[b + lane] : INT_MAX;
 #pragma unroll
-        for (int k = 2; k <= 64; k <<= 1)
+    for (int k = 2; k <= 64; k <<= 1)
 #pragma unroll
-            for (int j = k >> 1; j > 0; j >>= 1) {
-                const int32_t y = __shfl_xor(x, j);
-                const bool up = (lane & k) == 0;      // this pair's sequence sorts ascending
-                const bool lower = (lane & j) == 0;   // the pair's lower lane
-                x = (lower == up) ? (x < y ? x : y) : (x < y ? y : x);
-            }
-        if (lane < cnt) list[b + lane] = x;
-    } else if (lane == 0) {
-        for (int32_t i = b + 1; i < e; ++i) {
-            const int32_t x = list[i];
-            int32_t j = i - 1;
-            while (j >= b && list[j] > x) {
-                list[j + 1] = list[j];
-                --j;
-            }
-            list[j + 1] = x;
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const int32_t y = __shfl_xor(x, j);
+            const bool up = (lane & k) == 0;      // this pair's sequence sorts ascending
+            const bool lower = (lane & j) == 0;   // the pair's lower lane
+            x = (lower == up) ? (x < y ? x : y) : (x < y ? y : x);
         }
+    if (lane < cnt) list[b + lane] = x;
+}
+
+// The listed large buckets, one workgroup of 1024 threads per bucket: a
+// bitonic sort in LDS over the bucket padded with INT_MAX to a power of two.
+// A bucket beyond kSortLdsMax entries (only a degenerate candidate list
+// makes one) falls back to an insertion sort by one thread.
+__global__ __launch_bounds__(1024) void bucket_sort_block_kernel(const int32_t* offsets, int32_t* list,
+                                                                 const int32_t* large, const int32_t* n_large) {
+    __shared__ int32_t sh[kSortLdsMax];
+    const int t = threadIdx.x;
+    const int32_t count = *n_large;
+    for (int32_t q = blockIdx.x; q < count; q += gridDim.x) {
+        const int32_t v = large[q];
+        const int32_t b = offsets[v], e = offsets[v + 1];
+        const int32_t m = e - b;
+        if (m > kSortLdsMax) {
+            if (t == 0)
+                for (int32_t i = b + 1; i < e; ++i) {
+                    const int32_t x = list[i];
+                    int32_t j = i - 1;
+                    while (j >= b && list[j] > x) {
+                        list[j + 1] = list[j];
+                        --j;
+                    }
+                    list[j + 1] = x;
+                }
+            __syncthreads();
+            continue;
+        }
+        int32_t P = 64;
+        while (P < m) P <<= 1;
+        for (int32_t i = t; i < P; i += 1024) sh[i] = i < m ? list[b + i] : INT_MAX;
+        __syncthreads();
+        for (int32_t k = 2; k <= P; k <<= 1)
+            for (int32_t j = k >> 1; j > 0; j >>= 1) {
+                for (int32_t i = t; i < P; i += 1024) {
+                    const int32_t l = i ^ j;
+                    if (l > i) {
+                        const int32_t x = sh[i], y = sh[l];
+                        const bool up = (i & k) == 0;
+                        if ((x > y) == up) {
+                            sh[i] = y;
+                            sh[l] = x;
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        for (int32_t i = t; i < m; i += 1024) list[b + i] = sh[i];
+        __syncthreads();
     }
 }
 
@@ -362,23 +414,159 @@ __global__ void hit_fill_kernel(const int32_t* ids, int64_t n, int k, int64_t vo
 }
 
 // dW[v] = sum over the entries (n, k) with id_nk = v, in ascending (n, k)
-// order, of c_nk H[n]; rows no candidate lists get 0. One wave per row v.
+// order, of c_nk H[n]; rows no candidate lists get 0.
+//
+// dw_sum adds the entries [j0, j1) of a bucket into acc for the hidden
+// positions h0 + 512 s + 8 lane (s < kDwPass): four entries' list, coefficient
+// and H loads are issued together, and every element still takes its products
+// in ascending entry order.
+constexpr int kDwPass = 4;      // 512-wide hidden segments per pass over the entries
+constexpr int kDwSplit = kDwSplitEntries;   // a bucket with more entries is summed by several waves
+
+__device__ __forceinline__ void dw_sum(const CandBwdArgs& a, int32_t j0, int32_t j1, int64_t h0, int lane,
+                                       float (&acc)[kDwPass][8]) {
+#pragma unroll
+    for (int s = 0; s < kDwPass; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[s][e] = 0.0f;
+    int32_t j = j0;
+    for (; j + 4 <= j1; j += 4) {
+        int32_t ii[4];
+        float cc[4];
+        uint4 hv[4][kDwPass];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ii[u] = a.list[j + u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            cc[u] = a.coef_c[ii[u]];
+            const bf16_bits* hr = a.H + (int64_t)(ii[u] / a.k) * a.hidden;
+#pragma unroll
+            for (int s = 0; s < kDwPass; ++s) {
+                const int64_t h = h0 + s * kSeg + lane * 8;
+                hv[u][s] = h < a.hidden ? *reinterpret_cast<const uint4*>(hr + h) : make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (cc[u] != 0.0f)
+#pragma unroll
+                for (int s = 0; s < kDwPass; ++s) fma8(acc[s], cc[u], hv[u][s]);
+    }
+    for (; j < j1; ++j) {
+        const int32_t i = a.list[j];
+        const float c = a.coef_c[i];
+        if (c == 0.0f) continue;
+        const bf16_bits* hr = a.H + (int64_t)(i / a.k) * a.hidden;
+#pragma unroll
+        for (int s = 0; s < kDwPass; ++s) {
+            const int64_t h = h0 + s * kSeg + lane * 8;
+            if (h < a.hidden) fma8(acc[s], c, *reinterpret_cast<const uint4*>(hr + h));
+        }
+    }
+}
+
+// One wave per vocabulary row; rows whose bucket holds more than kDwSplit
+// entries are left to cand_dw_split_kernel and cand_dw_join_kernel.
 __global__ __launch_bounds__(kThreads) void cand_dw_kernel(CandBwdArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t v = (int64_t)blockIdx.x * kWaves + wave;
     if (v >= a.vocab) return;
     const int32_t b = a.offsets[v], e = a.offsets[v + 1];
-    for (int64_t h = lane * 8; h < a.hidden; h += kSeg) {
-        float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-        for (int32_t j = b; j < e; ++j) {
-            const int32_t i = a.list[j];
-            const float c = a.coef_c[i];
-            if (c == 0.0f) continue;
-            const int64_t n = i / a.k;
-            fma8(acc, c, *reinterpret_cast<const uint4*>(a.H + n * a.hidden + h));
+    if (e - b > kDwSplit) return;
+    for (int64_t h0 = 0; h0 < a.hidden; h0 += kDwPass * kSeg) {
+        float acc[kDwPass][8];
+        dw_sum(a, b, e, h0, lane, acc);
+#pragma unroll
+        for (int s = 0; s < kDwPass; ++s) {
+            const int64_t h = h0 + s * kSeg + lane * 8;
+            if (h < a.hidden)
+                store_row8(acc[s], a.dW_acc != nullptr ? a.dW_acc + v * a.hidden + h : nullptr,
+                           a.dW != nullptr ? a.dW + v * a.hidden + h : nullptr);
         }
-        store_row8(acc, a.dW_acc != nullptr ? a.dW_acc + v * a.hidden + h : nullptr,
-                   a.dW != nullptr ? a.dW + v * a.hidden + h : nullptr);
+    }
+}
+
+// Large buckets (a common id listed by many rows) are split into pieces of
+// kDwSplit entries so that no single wave sums thousands of rows: piece
+// counts per listed large bucket (zero for the listed ones not above
+// kDwSplit), their exclusive scan (the multi-block scan), one wave per piece
+// writing its fp32 partial row, and one wave per bucket adding the partials
+// in piece order. The split depends only on the bucket sizes, so the result
+// is deterministic; a split bucket's sum is associated piece by piece.
+__global__ void cand_split_counts_kernel(const int32_t* offsets, const int32_t* large, const int32_t* n_large,
+                                         int64_t cap, int32_t* pieces) {
+    const int32_t count = *n_large;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < cap;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        int32_t p = 0;
+        if (q < count) {
+            const int32_t v = large[q];
+            const int32_t m = offsets[v + 1] - offsets[v];
+            p = m > kDwSplit ? (m + kDwSplit - 1) / kDwSplit : 0;
+        }
+        pieces[q] = p;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void cand_dw_split_kernel(CandBwdArgs a, const int32_t* large,
+                                                                 const int32_t* n_large, const int32_t* piece_off,
+                                                                 float* partial) {
+    const int lane = threadIdx.x & 63;
+    const int32_t count = *n_large;
+    if (count == 0) return;
+    const int32_t total = piece_off[count];
+    for (int64_t g = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); g < total;
+         g += (int64_t)gridDim.x * kWaves) {
+        // the listed bucket q with piece_off[q] <= g < piece_off[q + 1]
+        int32_t lo = 0, hi = count - 1;
+        while (lo < hi) {
+            const int32_t mid = (lo + hi + 1) >> 1;
+            if (piece_off[mid] <= g) lo = mid;
+            else hi = mid - 1;
+        }
+        const int32_t v = large[lo];
+        const int32_t b = a.offsets[v], e = a.offsets[v + 1];
+        const int32_t j0 = b + (int32_t)(g - piece_off[lo]) * kDwSplit;
+        const int32_t j1 = j0 + kDwSplit < e ? j0 + kDwSplit : e;
+        for (int64_t h0 = 0; h0 < a.hidden; h0 += kDwPass * kSeg) {
+            float acc[kDwPass][8];
+            dw_sum(a, j0, j1, h0, lane, acc);
+#pragma unroll
+            for (int s = 0; s < kDwPass; ++s) {
+                const int64_t h = h0 + s * kSeg + lane * 8;
+                if (h < a.hidden) {
+                    float4* o = reinterpret_cast<float4*>(partial + g * a.hidden + h);
+                    o[0] = make_float4(acc[s][0], acc[s][1], acc[s][2], acc[s][3]);
+                    o[1] = make_float4(acc[s][4], acc[s][5], acc[s][6], acc[s][7]);
+                }
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void cand_dw_join_kernel(CandBwdArgs a, const int32_t* large,
+                                                                const int32_t* n_large, const int32_t* piece_off,
+                                                                const float* partial) {
+    const int lane = threadIdx.x & 63;
+    const int32_t count = *n_large;
+    for (int64_t q = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); q < count;
+         q += (int64_t)gridDim.x * kWaves) {
+        const int32_t p0 = piece_off[q], p1 = piece_off[q + 1];
+        if (p1 == p0) continue;   // not split: cand_dw_kernel wrote it
+        const int64_t v = large[q];
+        for (int64_t h = lane * 8; h < a.hidden; h += kSeg) {
+            float acc[8];
+            const float4* f = reinterpret_cast<const float4*>(partial + (int64_t)p0 * a.hidden + h);
+            acc[0] = f[0].x; acc[1] = f[0].y; acc[2] = f[0].z; acc[3] = f[0].w;
+            acc[4] = f[1].x; acc[5] = f[1].y; acc[6] = f[1].z; acc[7] = f[1].w;
+            for (int32_t g = p0 + 1; g < p1; ++g) {
+                const float4* x = reinterpret_cast<const float4*>(partial + (int64_t)g * a.hidden + h);
+                acc[0] += x[0].x; acc[1] += x[0].y; acc[2] += x[0].z; acc[3] += x[0].w;
+                acc[4] += x[1].x; acc[5] += x[1].y; acc[6] += x[1].z; acc[7] += x[1].w;
+            }
+            store_row8(acc, a.dW_acc != nullptr ? a.dW_acc + v * a.hidden + h : nullptr,
+                       a.dW != nullptr ? a.dW + v * a.hidden + h : nullptr);
+        }
     }
 }
 

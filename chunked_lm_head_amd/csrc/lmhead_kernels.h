@@ -180,8 +180,19 @@ __global__ void scan_tiles_kernel(const int32_t* counts, int64_t vocab, const in
                                   int32_t* offsets);
 __global__ void cand_fill_kernel(const int32_t* ids, int64_t nk, int64_t vocab, const int32_t* offsets,
                                  int32_t* cursor, int32_t* list);
-__global__ void bucket_sort_kernel(const int32_t* offsets, int64_t buckets, int32_t* list);
-__global__ void bucket_sort_wave_kernel(const int32_t* offsets, int64_t buckets, int32_t* list);
+__global__ void bucket_sort_kernel(const int32_t* offsets, int64_t buckets, int32_t* list, int32_t* large,
+                                   int32_t* n_large);
+__global__ void bucket_sort_wave_kernel(const int32_t* offsets, int64_t buckets, int32_t* list, int32_t* large,
+                                        int32_t* n_large);
+__global__ void bucket_sort_block_kernel(const int32_t* offsets, int32_t* list, const int32_t* large,
+                                         const int32_t* n_large);
+__global__ void cand_split_counts_kernel(const int32_t* offsets, const int32_t* large, const int32_t* n_large,
+                                         int64_t cap, int32_t* pieces);
+__global__ void cand_dw_split_kernel(CandBwdArgs a, const int32_t* large, const int32_t* n_large,
+                                     const int32_t* piece_off, float* partial);
+__global__ void cand_dw_join_kernel(CandBwdArgs a, const int32_t* large, const int32_t* n_large,
+                                    const int32_t* piece_off, const float* partial);
+constexpr int kDwSplitEntries = 256;   // bucket entries per split piece (must match the kernels)
 
 // Per-tile hit lists of the support entries. Entry (n, kk) with a valid id
 // goes to bucket (n / 256) * tiles_v + id / 256 as the packed value

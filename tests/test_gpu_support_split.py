@@ -264,3 +264,40 @@ def test_maximum_candidate_count(pad):
     rel_check("kl-only kl", to_np(ko["kl"]), ref_kl["kl"])
     grad_check("kl-only dH", bf16_to_np(ko["dH"]), ref_kl["dH"])
     grad_check("kl-only dW", bf16_to_np(ko["dW"]), ref_kl["dW"])
+
+
+def test_skewed_candidate_lists():
+    """Candidate ids drawn from a Zipf law (every row lists the most common
+    ids): vocabulary buckets of the KL-only entry with hundreds of entries and
+    per-tile hit buckets with thousands, sorted by the workgroup sort, for the
+    dense support entry and the KL-only one, against the oracle, plus a
+    bitwise repeat."""
+    inp = _inputs(n=600, vocab=3000, k=64, seed=800)
+    rng = np.random.default_rng(801)
+    w = np.arange(1, 3001, dtype=np.float64) ** -1.1
+    w /= w.sum()
+    for i in range(inp.ids.shape[0]):
+        inp.ids[i] = rng.choice(3000, size=64, replace=False, p=w)
+    d = Dev(inp)
+    lp, kl, lse, _ = lm.support_forward(d.H, d.W, d.ids, d.ref_logq, 512)
+    dH, dW = lm.backward(lm.ENTRY_SUPPORT, d.H, d.W, d.ids, lse, d.grad, 512, ref_logq=d.ref_logq,
+                         saved_lp=lp, grad_kl=d.grad_kl)
+    ko = _kl_only(d)
+    torch.cuda.synchronize()
+    ref = oracle.run(3, inp.H, inp.W, ids=inp.ids, ref_logq=inp.ref_logq, grad=inp.grad,
+                     grad_kl=inp.grad_kl)
+    rel_check("lp", to_np(lp), ref["lp"])
+    rel_check("kl", to_np(kl), ref["kl"])
+    grad_check("dH", bf16_to_np(dH), ref["dH"])
+    grad_check("dW", bf16_to_np(dW), ref["dW"])
+    ref_kl = oracle.run(oracle.ENTRY_SUPPORT_KL, inp.H, inp.W, ids=inp.ids, ref_logq=inp.ref_logq,
+                        grad_kl=inp.grad_kl)
+    rel_check("kl-only kl", to_np(ko["kl"]), ref_kl["kl"])
+    grad_check("kl-only dH", bf16_to_np(ko["dH"]), ref_kl["dH"])
+    grad_check("kl-only dW", bf16_to_np(ko["dW"]), ref_kl["dW"])
+    ko2 = _kl_only(d)
+    dH2, dW2 = lm.backward(lm.ENTRY_SUPPORT, d.H, d.W, d.ids, lse, d.grad, 512, ref_logq=d.ref_logq,
+                           saved_lp=lp, grad_kl=d.grad_kl)
+    torch.cuda.synchronize()
+    assert torch.equal(ko["dW"], ko2["dW"]) and torch.equal(ko["dH"], ko2["dH"])
+    assert torch.equal(dW, dW2) and torch.equal(dH, dH2)
