@@ -434,6 +434,7 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
                                                                                      large, n_large);
             bucket_sort_block_kernel<<<kSortBlocks, 1024, 0, s>>>(offsets, list, large, n_large);
             cand_dw_kernel<<<(unsigned)cdiv(L.vocab, kThreads / 64), kThreads, 0, s>>>(cb);
+            cand_dw_mid_kernel<<<kSplitBlocks, kThreads, 0, s>>>(cb, large, n_large);
             // buckets above kDwSplitEntries entries: pieces, their offsets, partial rows, join
             int32_t* pieces = (int32_t*)(w + L.pieces);
             int32_t* piece_off = (int32_t*)(w + L.piece_off);

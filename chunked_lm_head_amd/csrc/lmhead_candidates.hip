@@ -281,15 +281,18 @@ __global__ void cand_fill_kernel(const int32_t* ids, int64_t nk, int64_t vocab, 
 // (an integer atomic fixes only the list's order, not the result) and sorted
 // by bucket_sort_block_kernel, one workgroup per bucket.
 constexpr int kSortLdsMax = 32768;   // entries a workgroup sorts in LDS (128 KB)
+// A vocabulary bucket above this many entries is listed as large: sorted by
+// the workgroup sort and, in the KL-only dW, summed by the mid / split kernels.
+constexpr int kSmallBucket = 16;
 
-// One thread per bucket: insertion sort for up to 16 entries, the vocabulary
+// One thread per bucket: insertion sort for up to kSmallBucket entries, the vocabulary
 // buckets of the KL-only entry holding N·K / V (a few) on average.
 __global__ void bucket_sort_kernel(const int32_t* offsets, int64_t buckets, int32_t* list, int32_t* large,
                                    int32_t* n_large) {
     for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < buckets;
          v += (int64_t)gridDim.x * blockDim.x) {
         const int32_t b = offsets[v], e = offsets[v + 1];
-        if (e - b > 16) {
+        if (e - b > kSmallBucket) {
             large[atomicAdd(n_large, 1)] = (int32_t)v;
             continue;
         }
@@ -465,23 +468,51 @@ __device__ __forceinline__ void dw_sum(const CandBwdArgs& a, int32_t j0, int32_t
     }
 }
 
-// One wave per vocabulary row; rows whose bucket holds more than kDwSplit
-// entries are left to cand_dw_split_kernel and cand_dw_join_kernel.
+// One wave per vocabulary row whose bucket holds at most kSmallBucket entries (the
+// common case: N·K / V entries per row on average), with few registers so that
+// many waves hide the gather latency. Larger buckets are in the sort's list
+// of large buckets and are summed by cand_dw_mid_kernel (up to kDwSplit
+// entries) or split (above it).
 __global__ __launch_bounds__(kThreads) void cand_dw_kernel(CandBwdArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t v = (int64_t)blockIdx.x * kWaves + wave;
     if (v >= a.vocab) return;
     const int32_t b = a.offsets[v], e = a.offsets[v + 1];
-    if (e - b > kDwSplit) return;
-    for (int64_t h0 = 0; h0 < a.hidden; h0 += kDwPass * kSeg) {
-        float acc[kDwPass][8];
-        dw_sum(a, b, e, h0, lane, acc);
+    if (e - b > kSmallBucket) return;
+    for (int64_t h = lane * 8; h < a.hidden; h += kSeg) {
+        float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        for (int32_t j = b; j < e; ++j) {
+            const int32_t i = a.list[j];
+            const float c = a.coef_c[i];
+            if (c == 0.0f) continue;
+            const int64_t n = i / a.k;
+            fma8(acc, c, *reinterpret_cast<const uint4*>(a.H + n * a.hidden + h));
+        }
+        store_row8(acc, a.dW_acc != nullptr ? a.dW_acc + v * a.hidden + h : nullptr,
+                   a.dW != nullptr ? a.dW + v * a.hidden + h : nullptr);
+    }
+}
+
+// One wave per listed large bucket of kSmallBucket + 1 .. kDwSplit entries.
+__global__ __launch_bounds__(kThreads) void cand_dw_mid_kernel(CandBwdArgs a, const int32_t* large,
+                                                               const int32_t* n_large) {
+    const int lane = threadIdx.x & 63;
+    const int32_t count = *n_large;
+    for (int64_t q = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); q < count;
+         q += (int64_t)gridDim.x * kWaves) {
+        const int64_t v = large[q];
+        const int32_t b = a.offsets[v], e = a.offsets[v + 1];
+        if (e - b > kDwSplit) continue;
+        for (int64_t h0 = 0; h0 < a.hidden; h0 += kDwPass * kSeg) {
+            float acc[kDwPass][8];
+            dw_sum(a, b, e, h0, lane, acc);
 #pragma unroll
-        for (int s = 0; s < kDwPass; ++s) {
-            const int64_t h = h0 + s * kSeg + lane * 8;
-            if (h < a.hidden)
-                store_row8(acc[s], a.dW_acc != nullptr ? a.dW_acc + v * a.hidden + h : nullptr,
-                           a.dW != nullptr ? a.dW + v * a.hidden + h : nullptr);
+            for (int s = 0; s < kDwPass; ++s) {
+                const int64_t h = h0 + s * kSeg + lane * 8;
+                if (h < a.hidden)
+                    store_row8(acc[s], a.dW_acc != nullptr ? a.dW_acc + v * a.hidden + h : nullptr,
+                               a.dW != nullptr ? a.dW + v * a.hidden + h : nullptr);
+            }
         }
     }
 }

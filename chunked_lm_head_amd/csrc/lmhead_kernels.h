@@ -186,6 +186,7 @@ __global__ void bucket_sort_wave_kernel(const int32_t* offsets, int64_t buckets,
                                         int32_t* n_large);
 __global__ void bucket_sort_block_kernel(const int32_t* offsets, int32_t* list, const int32_t* large,
                                          const int32_t* n_large);
+__global__ void cand_dw_mid_kernel(CandBwdArgs a, const int32_t* large, const int32_t* n_large);
 __global__ void cand_split_counts_kernel(const int32_t* offsets, const int32_t* large, const int32_t* n_large,
                                          int64_t cap, int32_t* pieces);
 __global__ void cand_dw_split_kernel(CandBwdArgs a, const int32_t* large, const int32_t* n_large,
