@@ -40,6 +40,7 @@ struct Layout {
     size_t hdr, lse, part, zg, rows;
     // backward regions
     size_t coef_a, coef_c, G, dh_acc;
+    size_t dh_part;   // fp32 partial dH tiles of the K-split (few row tiles only)
     // backward of the KL-only entry: inverse index of the candidate ids
     size_t counts, offsets, cursor, list, tsum, tprefix, large, n_large, pieces, piece_off, partial;
     size_t fwd_total, bwd_total;
@@ -66,6 +67,9 @@ int validate_problem(const lmhead_problem* p, int entry) {
     if (cdiv(p->n, kTile) * cdiv(p->vocab, kTile) > INT_MAX) return LMHEAD_ERR_SHAPE;
     return LMHEAD_OK;
 }
+
+constexpr int kComputeUnits = 256;
+int dh_slices(int64_t n, int64_t n_pad, int64_t hidden, int64_t w_pad);
 
 Layout plan(const lmhead_problem& p, int entry) {
     Layout L{};
@@ -128,6 +132,14 @@ Layout plan(const lmhead_problem& p, int entry) {
     L.coef_c = take(4 * L.n * L.k);
     L.G = take(2 * L.n_pad * L.w_pad);
     L.dh_acc = take(4 * L.n * L.hidden);
+    {
+        // the first chunk is the widest; the last one may split further
+        const int64_t last = L.vocab - (cdiv(L.vocab, L.chunk) - 1) * L.chunk;
+        const int s0 = dh_slices(L.n, L.n_pad, L.hidden, L.w_pad);
+        const int s1 = dh_slices(L.n, L.n_pad, L.hidden, round_up(last, kTile));
+        const int smax = s0 > s1 ? s0 : s1;
+        L.dh_part = take(smax > 1 ? 4 * smax * L.n * L.hidden : 0);
+    }
     if (buckets) take_hits(L.hit_bwd);
     L.bwd_total = off > L.fwd_total ? off : L.fwd_total;
     return L;
@@ -165,9 +177,8 @@ int launched() { return hipGetLastError() == hipSuccess ? LMHEAD_OK : LMHEAD_ERR
 // that finishes sooner: a launch whose last round of 256 x 256 tiles leaves
 // compute units idle can lend them to the other kind. Estimated in units of
 // one K step of one tile, with one workgroup per compute unit and workgroups
-// starting in launch order on the first free unit (the MI355X has 256; the
-// choice changes only the schedule, never a result).
-constexpr int kComputeUnits = 256;
+// starting in launch order on the first free unit (the MI355X has 256
+// compute units; the choice changes only the schedule, never a result).
 // workgroups of bucket_sort_block_kernel (each loops over the listed large buckets)
 constexpr int kSortBlocks = 512;
 // workgroups of the split dW kernels (each loops over its share of the pieces / buckets)
@@ -202,6 +213,36 @@ int dwdh_plan(int64_t n_dw, int64_t k_dw, int64_t n_dh, int64_t k_dh) {
     const bool dh_first = k_dh >= k_dw;   // longer tiles first
     const int64_t together = dh_first ? list_time(n_dh, k_dh, n_dw, k_dw) : list_time(n_dw, k_dw, n_dh, k_dh);
     return together * 20 <= apart * 19 ? (dh_first ? 1 : 0) : -1;
+}
+
+// K slices of a chunk's dH contraction (1: no split). With few dH tiles
+// (small batches) each one runs all of the chunk's K steps while most compute
+// units idle; cutting the chunk's columns into S equal slices (S a power of
+// two dividing the K steps, at least 8 steps each) gives S times the tiles,
+// whose fp32 partials dh_join_kernel adds in slice order. Chosen from the
+// same estimate as dwdh_plan, plus two steps per tile for the prologue and
+// the partial's store and the join's HBM traffic at 8 MB per step (one K step
+// of one tile is about 1.7 us), only where it saves at least 5 %. It depends
+// on the shape alone (dW wanted or not), so one shape always sums in one order.
+int dh_slices(int64_t n, int64_t n_pad, int64_t hidden, int64_t w_pad) {
+    const int64_t n_dh = (n_pad / kTile) * cdiv(hidden, kTile);
+    if (n <= 0 || 2 * n_dh > kComputeUnits) return 1;
+    const int64_t n_dw = (w_pad / kTile) * cdiv(hidden, kTile), k_dw = n_pad / kTileK;
+    const int64_t kt = w_pad / kTileK;
+    const int one = dwdh_plan(n_dw, k_dw, n_dh, kt);
+    const int64_t base = one < 0 ? rounds_time(n_dw, k_dw) + rounds_time(n_dh, kt)
+                                 : (one == 1 ? list_time(n_dh, kt, n_dw, k_dw) : list_time(n_dw, k_dw, n_dh, kt));
+    int best = 1;
+    int64_t best_t = base;
+    for (int64_t sl = 2; kt % sl == 0 && kt / sl >= 8; sl *= 2) {
+        const int64_t join = cdiv((sl + 2) * n * hidden * 4, (int64_t)8 << 20);
+        const int64_t t = rounds_time(n_dw, k_dw) + rounds_time(n_dh * sl, kt / sl + 2) + join;
+        if (t * 20 <= base * 19 && t < best_t) {
+            best = (int)sl;
+            best_t = t;
+        }
+    }
+    return best;
 }
 
 int grid_1d(int64_t items, int per_block, int cap) {
@@ -520,6 +561,14 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
         }
         const int64_t n_dw = want_dw ? da.tiles_m * da.tiles_n : 0;
         const int64_t n_dh = want_dh ? ha.tiles_m * ha.tiles_n : 0;
+        const int slices = dh_slices(L.n, L.n_pad, L.hidden, w_pad);
+        if (want_dh && slices > 1) {
+            float* part = (float*)(w + L.dh_part);
+            if (want_dw) bwd_dw_kernel<<<(unsigned)n_dw, kThreads, 0, s>>>(da);
+            bwd_dh_split_kernel<<<(unsigned)(n_dh * slices), kThreads, 0, s>>>(ha, slices, part);
+            dh_join_kernel<<<grid_1d(L.n * L.hidden / 4, kThreads, 4096), kThreads, 0, s>>>(ha, slices, part);
+            continue;
+        }
         const int plan_one = dwdh_plan(n_dw, L.n_pad / kTileK, n_dh, w_pad / kTileK);
         if (plan_one >= 0) {
             bwd_dwdh_kernel<<<(unsigned)(n_dw + n_dh), kThreads, 0, s>>>(da, ha, plan_one);

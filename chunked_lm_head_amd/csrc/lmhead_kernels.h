@@ -170,6 +170,8 @@ __global__ void bwd_logit_grad_kernel(LogitGradArgs a);
 __global__ void bwd_dw_kernel(DwArgs a);
 __global__ void bwd_dh_kernel(DhArgs a);
 __global__ void bwd_dwdh_kernel(DwArgs dw, DhArgs dh, int dh_first);
+__global__ void bwd_dh_split_kernel(DhArgs a, int slices, float* partial);
+__global__ void dh_join_kernel(DhArgs a, int slices, const float* partial);
 __global__ void cand_kl_fwd_kernel(CandFwdArgs a);
 __global__ void cand_dh_kernel(CandBwdArgs a);
 __global__ void cand_count_kernel(const int32_t* ids, int64_t nk, int64_t vocab, int32_t* counts);

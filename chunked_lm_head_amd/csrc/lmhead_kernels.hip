@@ -689,6 +689,78 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dwdh_kernel(DwArgs dw, DhArgs
     else dw_tile(dw, local, smem);
 }
 
+// Few row tiles (small batches): a chunk's dH tiles are split along the
+// chunk's columns into `slices` equal K ranges (multiples of 64), one
+// workgroup per (slice, tile), each writing its fp32 partial tile to
+// partial[slice, n, hidden]; dh_join_kernel then adds the partials in slice
+// order to the running sum. The split depends only on the problem's shape.
+__global__ __launch_bounds__(kThreads, 1) void bwd_dh_split_kernel(DhArgs a, int slices, float* partial) {
+    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+    const int64_t tiles = a.tiles_m * a.tiles_n;
+    const int64_t sl = blockIdx.x / tiles;
+    int64_t tm, tn;
+    map_tile(blockIdx.x - sl * tiles, a.tiles_m, a.tiles_n, tm, tn);
+    const int64_t m0 = tm * kTile, n0 = tn * kTile;
+    const int64_t ks = a.w_pad / slices, k0 = sl * ks;
+    const int64_t krows = a.width - k0;   // rows of W_c from k0 on (<= 0: the slice is all padding)
+    AccTile acc;
+    gemm_mainloop<false, true>(Operand{a.G + k0, a.w_pad, a.n_pad}, m0,
+                               Operand{a.Wc + (krows > 0 ? k0 : 0) * a.hidden, a.hidden, krows > 0 ? krows : 0},
+                               n0, ks, smem, acc);
+    float* S = reinterpret_cast<float*>(smem);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+    float* out = partial + sl * a.n * a.hidden;
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+        if (wc == half) stage_half_rows(S, acc, wr, lane);
+        __syncthreads();
+        const int c = 4 * (lane & 31);
+        const int64_t h = n0 + half * 128 + c;
+        if (h < a.hidden) {
+#pragma unroll 4
+            for (int u = 0; u < 32; ++u) {
+                const int r = wave * 64 + u * 2 + (lane >> 5);
+                const int64_t row = m0 + r;
+                if (row < a.n)
+                    *reinterpret_cast<float4*>(out + row * a.hidden + h) =
+                        *reinterpret_cast<const float4*>(S + r * kRowStride + c);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// dh_acc (+)= partial[0] + partial[1] + ... in slice order, four elements per
+// thread; the last chunk writes the bf16 dH and, for a caller accumulator,
+// the fp32 sum, exactly as bwd_dh_kernel's epilogue does.
+__global__ void dh_join_kernel(DhArgs a, int slices, const float* partial) {
+    const int64_t count = a.n * a.hidden / 4;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < count;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t o = q * 4;
+        float4 p = *reinterpret_cast<const float4*>(partial + o);
+        for (int sl = 1; sl < slices; ++sl) {
+            const float4 x = *reinterpret_cast<const float4*>(partial + sl * a.n * a.hidden + o);
+            p.x += x.x;
+            p.y += x.y;
+            p.z += x.z;
+            p.w += x.w;
+        }
+        float4 v = p;
+        if (!a.first) {
+            const float4 d = *reinterpret_cast<const float4*>(a.dh_acc + o);
+            v.x = d.x + p.x;
+            v.y = d.y + p.y;
+            v.z = d.z + p.z;
+            v.w = d.w + p.w;
+        }
+        if (a.last && a.dH != nullptr)
+            *reinterpret_cast<uint2*>(a.dH + o) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+        if (!a.last || a.keep_acc) *reinterpret_cast<float4*>(a.dh_acc + o) = v;
+    }
+}
+
 // out[i] = bf16 (round to nearest even) of in[i]; count is a multiple of 2.
 __global__ void f32_to_bf16_kernel(const float* in, int64_t count, bf16_bits* out) {
     for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 2; i < count;
