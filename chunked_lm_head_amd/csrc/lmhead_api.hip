@@ -631,7 +631,8 @@ int lmhead_plan_chunk(const lmhead_problem* p, int entry, size_t budget_bytes, i
         return plan(q, entry).bwd_total <= budget_bytes;
     };
     if (!fits(256)) return LMHEAD_ERR_WORKSPACE;
-    // largest fitting chunk (the workspace grows with the chunk), by bisection over multiples of 256
+    // largest fitting chunk by bisection over multiples of 256 (the workspace
+    // grows with the chunk, up to the dip noted below)
     int64_t lo = 1, hi = cdiv(q.vocab, 256);
     while (lo < hi) {
         const int64_t mid = lo + (hi - lo + 1) / 2;
@@ -639,7 +640,11 @@ int lmhead_plan_chunk(const lmhead_problem* p, int entry, size_t budget_bytes, i
         else hi = mid - 1;
     }
     const int64_t passes = cdiv(q.vocab, lo * 256);
-    *chunk = round_up(cdiv(q.vocab, passes), 256);
+    const int64_t even = round_up(cdiv(q.vocab, passes), 256);
+    // the dH K-split's partials make the workspace dip where a wider chunk
+    // takes fewer slices (small batches); the even split of the same passes
+    // is taken only if it fits too, else the bisection's own chunk
+    *chunk = fits(even) ? even : lo * 256;
     return LMHEAD_OK;
 }
 

@@ -177,7 +177,11 @@ int lmhead_memory_report(const lmhead_problem* p, int entry, int with_backward,
  * `budget_bytes` with the fewest vocabulary chunks (the fewest passes) and,
  * among those, the smallest chunk (a multiple of 256), which spreads the
  * vocabulary evenly over the passes. Writes it to *chunk. Returns
- * LMHEAD_ERR_WORKSPACE if even a 256-wide chunk does not fit.
+ * LMHEAD_ERR_WORKSPACE if even a 256-wide chunk does not fit. The chunk
+ * returned always fits. With few row tiles (small batches) the workspace
+ * holds the fp32 partials of the dH K-split, whose slice count follows the
+ * chunk's width and can fall as the chunk grows; there the choice is the
+ * bisection's (a fitting chunk, not always the one with the fewest passes).
  */
 int lmhead_plan_chunk(const lmhead_problem* p, int entry, size_t budget_bytes, int64_t* chunk);
 

@@ -66,3 +66,20 @@ def test_plan_examples_and_errors():
     # the support entry's candidates add to the workspace, never to fewer bytes
     assert lm.plan_chunk(8192, 4096, 151936, 600 << 20, entry=3, k=64) <= \
         lm.plan_chunk(8192, 4096, 151936, 600 << 20)
+
+
+@pytest.mark.parametrize("shape", [dict(n=256, hidden=4096, vocab=151936),
+                                   dict(n=200, hidden=512, vocab=5000),
+                                   dict(n=1024, hidden=2048, vocab=151936)])
+def test_plan_always_fits_with_dh_split_partials(shape):
+    """Small batches hold the dH K-split's fp32 partials, whose slice count
+    follows the chunk's K steps and can fall as the chunk widens, so the
+    workspace is not monotone in the chunk there. Whatever the budget, the
+    planned chunk's workspace fits it."""
+    ws = [_ws(c, **shape) for c in range(256, 256 * math.ceil(shape["vocab"] / 256) + 1, 256)]
+    assert all(w > 0 for w in ws)
+    lo, hi = min(ws), max(ws)
+    for i in range(41):
+        budget = lo + (hi - lo) * i // 40
+        c = lm.plan_chunk(shape["n"], shape["hidden"], shape["vocab"], budget)
+        assert c % 256 == 0 and _ws(c, **shape) <= budget, (budget, c)
