@@ -17,19 +17,20 @@ pytestmark = pytest.mark.gpu
 CHUNK = 512
 
 
-def _inputs(entry):
+def _inputs(entry, **shape):
     d = dict(n=300, hidden=512, vocab=1000, chunk=CHUNK, seed=900 + entry, ignore_frac=0.1,
              entry=entry)
+    d.update(shape)
     if entry in (wlmod.ENTRY_SUPPORT, wlmod.ENTRY_SUPPORT_KL):
         d.update(k=16, ignore_frac=0.0)
     return Dev(wlmod.make_inputs(wlmod.custom(**d)))
 
 
-def _step_fn(d, entry):
+def _step_fn(d, entry, chunk=CHUNK):
     n, hidden = d.H.shape
     vocab = d.W.shape[0]
     k = d.ids.shape[1] if entry in (lm.ENTRY_SUPPORT, lm.ENTRY_SUPPORT_KL) else 1
-    p = lm.problem(n, hidden, vocab, CHUNK, -1, k)
+    p = lm.problem(n, hidden, vocab, chunk, -1, k)
     ws = lm.workspace(p, entry, True, d.H.device)
     out = dict(dH=torch.empty_like(d.H), dW=torch.empty_like(d.W))
     if entry != lm.ENTRY_SUPPORT_KL:
@@ -73,11 +74,16 @@ def _step_fn(d, entry):
     return step, out, ws
 
 
-@pytest.mark.parametrize("entry", [lm.ENTRY_CE_MEAN, lm.ENTRY_LOGPROB, lm.ENTRY_SUPPORT,
-                                   lm.ENTRY_SUPPORT_KL])
-def test_graph_replays_match_eager(entry):
-    d = _inputs(entry)
-    step, out, ws = _step_fn(d, entry)
+# the last two: n = 200 rows with chunk 2048 split each chunk's dH contraction
+# into K slices (partials, then an ordered join kernel)
+@pytest.mark.parametrize("entry,shape", [
+    (lm.ENTRY_CE_MEAN, {}), (lm.ENTRY_LOGPROB, {}), (lm.ENTRY_SUPPORT, {}), (lm.ENTRY_SUPPORT_KL, {}),
+    (lm.ENTRY_CE_MEAN, dict(n=200, vocab=5000, chunk=2048)),
+    (lm.ENTRY_SUPPORT, dict(n=200, vocab=5000, chunk=2048)),
+])
+def test_graph_replays_match_eager(entry, shape):
+    d = _inputs(entry, **shape)
+    step, out, ws = _step_fn(d, entry, shape.get("chunk", CHUNK))
     step()
     torch.cuda.synchronize()
     ref = {name: t.clone() for name, t in out.items()}
