@@ -88,6 +88,7 @@ class lmhead_memory_figures(ctypes.Structure):
         ("dz_chunk_bytes", ctypes.c_size_t),
         ("dh_acc_bytes", ctypes.c_size_t),
         ("caller_output_bytes", ctypes.c_size_t),
+        ("dh_split_bytes", ctypes.c_size_t),
     ]
 
 

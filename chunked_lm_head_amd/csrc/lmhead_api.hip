@@ -41,6 +41,7 @@ struct Layout {
     // backward regions
     size_t coef_a, coef_c, G, dh_acc;
     size_t dh_part;   // fp32 partial dH tiles of the K-split (few row tiles only)
+    int64_t dh_part_bytes;
     // backward of the KL-only entry: inverse index of the candidate ids
     size_t counts, offsets, cursor, list, tsum, tprefix, large, n_large, pieces, piece_off, partial;
     size_t fwd_total, bwd_total;
@@ -138,7 +139,8 @@ Layout plan(const lmhead_problem& p, int entry) {
         const int s0 = dh_slices(L.n, L.n_pad, L.hidden, L.w_pad);
         const int s1 = dh_slices(L.n, L.n_pad, L.hidden, round_up(last, kTile));
         const int smax = s0 > s1 ? s0 : s1;
-        L.dh_part = take(smax > 1 ? 4 * smax * L.n * L.hidden : 0);
+        L.dh_part_bytes = smax > 1 ? 4 * smax * L.n * L.hidden : 0;
+        L.dh_part = take(L.dh_part_bytes);
     }
     if (buckets) take_hits(L.hit_bwd);
     L.bwd_total = off > L.fwd_total ? off : L.fwd_total;
@@ -607,6 +609,7 @@ int lmhead_memory_report(const lmhead_problem* p, int entry, int with_backward,
     if (with_backward && !kl_only) {
         r.dz_chunk_bytes = (size_t)(2 * L.n_pad * L.w_pad);
         r.dh_acc_bytes = (size_t)(4 * L.n * L.hidden);
+        r.dh_split_bytes = (size_t)L.dh_part_bytes;
     }
     // fp32 outputs: lse [n] plus loss [1] / logp [n] / lp [n, k] and kl [n]
     size_t outs = (size_t)(4 * L.n);

@@ -164,6 +164,9 @@ typedef struct lmhead_memory_figures {
     size_t caller_output_bytes;  /* buffers the caller allocates: the entry's fp32 outputs
                                     (loss / logp / lp, kl, lse), plus bf16 dH and dW
                                     with the backward */
+    size_t dh_split_bytes;       /* backward, few row tiles only (else 0): fp32 partial
+                                    dH of the K slices a chunk's dH contraction is cut
+                                    into, joined in slice order */
 } lmhead_memory_figures;
 
 /* Fills *out. Returns LMHEAD_ERR_ARG / LMHEAD_ERR_SHAPE for an invalid

@@ -83,3 +83,17 @@ def test_plan_always_fits_with_dh_split_partials(shape):
         budget = lo + (hi - lo) * i // 40
         c = lm.plan_chunk(shape["n"], shape["hidden"], shape["vocab"], budget)
         assert c % 256 == 0 and _ws(c, **shape) <= budget, (budget, c)
+
+
+def test_report_lists_dh_split_partials():
+    """Small batches: the fp32 partials of the dH K-split are listed, S slices
+    of [n, hidden] (n = 256, Hd = 4096, chunk 8192: 16 slices; the 4480-wide
+    tail chunk takes fewer); none at the headline or without the backward."""
+    r = lm.memory_report(256, 4096, 151936, 8192, 0, True, 1)
+    assert r["dh_split_bytes"] == 16 * 4 * 256 * 4096
+    parts = r["dz_chunk_bytes"] + r["dh_acc_bytes"] + r["dh_split_bytes"]
+    assert parts <= r["workspace_bytes"] <= parts + (1 << 20)
+    assert lm.memory_report(256, 4096, 151936, 8192, 0, False, 1)["dh_split_bytes"] == 0
+    assert lm.memory_report(8192, 4096, 151936, 8192, 0, True, 1)["dh_split_bytes"] == 0
+    # chunk 512 has 8 K steps: too few to split
+    assert lm.memory_report(256, 4096, 151936, 512, 0, True, 1)["dh_split_bytes"] == 0
