@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="headline",
-                    choices=["headline", "mid", "logprob", "support", "tiny"])
+                    choices=["headline", "mid", "logprob", "support", "tiny", "small"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle sample")

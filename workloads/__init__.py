@@ -80,6 +80,9 @@ WORKLOADS = {
                         seed=1004, entry=ENTRY_LOGPROB),
     "support": Workload("support", n=8192, hidden=4096, vocab=151936, chunk=8192,
                         seed=1005, entry=ENTRY_SUPPORT, k=64),
+    # the headline's H, W and chunk at a small batch (256 rows: one row tile),
+    # where the backward's dH contraction takes the K-split
+    "small": Workload("small", n=256, hidden=4096, vocab=151936, chunk=8192, seed=1006),
 }
 
 
