@@ -41,7 +41,9 @@ def _sample_rows(n, seed, valid=None):
     return np.sort(rng.choice(pool, size=min(N_SAMPLE_ROWS, pool.size), replace=False))
 
 
-@pytest.mark.parametrize("name", ["mid", "headline", "logprob", "support"])
+# "small" (N = 256) is the headline's W and chunk at one row tile: its
+# backward takes the dH K-split
+@pytest.mark.parametrize("name", ["mid", "headline", "logprob", "support", "small"])
 def test_fullsize_rows_against_oracle(name):
     wl = wlmod.WORKLOADS[name]
     inp = _inputs(name)
