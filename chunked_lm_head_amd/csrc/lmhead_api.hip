@@ -23,6 +23,12 @@ using namespace lmhead;
 constexpr int64_t kMaxRows = int64_t(1) << 30;
 constexpr int64_t kMaxVocab = int64_t(1) << 30;
 constexpr int64_t kMaxHidden = 65536;
+// Widest padded chunk, round_up(min(chunk, vocab), 256): dL/dz is the K-major
+// operand of the dH contraction with a row pitch of that width, and a tile's
+// buffer range (256 rows of it, in bytes) must stay below 2^31.
+constexpr int64_t kMaxChunkPad = (int64_t(1) << 22) - 256;
+// Most K slices of a chunk's dH contraction (bounds the fp32 partials)
+constexpr int kMaxDhSlices = 16;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
@@ -62,8 +68,14 @@ int validate_problem(const lmhead_problem* p, int entry) {
     if (p->chunk < 256 || p->chunk % 256 != 0 || p->chunk > kMaxVocab + 256) return LMHEAD_ERR_SHAPE;
     if (p->num_valid < -1) return LMHEAD_ERR_SHAPE;
     if (is_support(entry) && (p->k < 1 || p->k > kMaxCandidates)) return LMHEAD_ERR_SHAPE;
-    // the KL-only entry indexes (row, candidate) entries with int32
-    if (entry == LMHEAD_ENTRY_SUPPORT_KL && p->n * (int64_t)p->k > INT_MAX) return LMHEAD_ERR_SHAPE;
+    // both support entries index (row, candidate) entries with int32: the
+    // KL-only entry's inverse index, the dense entry's per-tile buckets and
+    // their offset scans
+    if (is_support(entry) && p->n * (int64_t)p->k > INT_MAX) return LMHEAD_ERR_SHAPE;
+    // every entry with a vocabulary-wide pass: the backward's chunk width
+    if (entry != LMHEAD_ENTRY_SUPPORT_KL &&
+        round_up(p->chunk < p->vocab ? p->chunk : p->vocab, kTile) > kMaxChunkPad)
+        return LMHEAD_ERR_SHAPE;
     // one workgroup per 256 x 256 tile: keep every grid within 2^31 - 1
     if (cdiv(p->n, kTile) * cdiv(p->vocab, kTile) > INT_MAX) return LMHEAD_ERR_SHAPE;
     return LMHEAD_OK;
@@ -220,7 +232,7 @@ int dwdh_plan(int64_t n_dw, int64_t k_dw, int64_t n_dh, int64_t k_dh) {
 // K slices of a chunk's dH contraction (1: no split). With few dH tiles
 // (small batches) each one runs all of the chunk's K steps while most compute
 // units idle; cutting the chunk's columns into S equal slices (S a power of
-// two dividing the K steps, at least 8 steps each) gives S times the tiles,
+// two dividing the K steps, at least 8 steps each, S <= 16) gives S times the tiles,
 // whose fp32 partials dh_join_kernel adds in slice order. Chosen from the
 // same estimate as dwdh_plan, plus two steps per tile for the prologue and
 // the partial's store and the join's HBM traffic at 8 MB per step (one K step
@@ -236,7 +248,7 @@ int dh_slices(int64_t n, int64_t n_pad, int64_t hidden, int64_t w_pad) {
                                  : (one == 1 ? list_time(n_dh, kt, n_dw, k_dw) : list_time(n_dw, k_dw, n_dh, kt));
     int best = 1;
     int64_t best_t = base;
-    for (int64_t sl = 2; kt % sl == 0 && kt / sl >= 8; sl *= 2) {
+    for (int64_t sl = 2; sl <= kMaxDhSlices && kt % sl == 0 && kt / sl >= 8; sl *= 2) {
         const int64_t join = cdiv((sl + 2) * n * hidden * 4, (int64_t)8 << 20);
         const int64_t t = rounds_time(n_dw, k_dw) + rounds_time(n_dh * sl, kt / sl + 2) + join;
         if (t * 20 <= base * 19 && t < best_t) {
@@ -637,6 +649,7 @@ int lmhead_plan_chunk(const lmhead_problem* p, int entry, size_t budget_bytes, i
     // largest fitting chunk by bisection over multiples of 256 (the workspace
     // grows with the chunk, up to the dip noted below)
     int64_t lo = 1, hi = cdiv(q.vocab, 256);
+    if (entry != LMHEAD_ENTRY_SUPPORT_KL && hi > kMaxChunkPad / 256) hi = kMaxChunkPad / 256;
     while (lo < hi) {
         const int64_t mid = lo + (hi - lo + 1) / 2;
         if (fits(mid * 256)) lo = mid;

@@ -109,12 +109,17 @@ enum lmhead_device_error {
  *   chunk      vocabulary chunk of the backward pass: a multiple of 256,
  *              >= 256. The backward materialises dL/dz for one chunk
  *              ([n x chunk] bf16) at a time; the forward's result does not
- *              depend on it.
+ *              depend on it. Every entry but the KL-only one also needs
+ *              round_up(min(chunk, vocab), 256) <= 4,194,048 (2^22 - 256:
+ *              dL/dz is read with that row pitch, 256 rows per buffer
+ *              range of at most 2^31 - 1 bytes); vocabularies above that
+ *              take a smaller chunk.
  *   num_valid  -1: count valid rows (0 <= label < vocab) on the device,
  *              with no host synchronisation; >= 0: use this value verbatim as
  *              the CE mean's denominator ("given counts", [PR14-tests]).
- *   k          candidates per row for the support entries (1..1024; the
- *              KL-only entry also needs n * k < 2^31); ignored by the others.
+ *   k          candidates per row for the support entries (1..1024, and
+ *              n * k <= 2^31 - 1: both support entries index their (row,
+ *              candidate) entries with int32); ignored by the others.
  *   flags      0, or LMHEAD_FLAG_PADDED_IDS with a support entry.
  *   temperature     scalar temperature t applied to every row; 0 = off
  *                   (t = 1). Must be finite and >= 0.

@@ -6,6 +6,7 @@ returned before anything touches a device. Calls here use fake addresses
 and always fail validation first, so nothing is ever launched.
 """
 import ctypes
+import math
 import os
 import re
 
@@ -198,3 +199,59 @@ def test_support_split_and_padding_host_checks():
     r = lm.memory_report(64, 256, 1024, 256, lm.ENTRY_SUPPORT_KL, True, 8)
     assert r["partials_bytes"] == r["dz_chunk_bytes"] == 0
     assert r["caller_output_bytes"] == 4 * 64 * 8 + 4 * 64 + 2 * 64 * 256 + 2 * 1024 * 256
+
+
+def test_support_entries_reject_int32_entry_counts():
+    """Both support entries index their (row, candidate) entries with int32
+    (the dense entry's per-tile buckets and offset scans, the KL-only entry's
+    inverse index), so n * k above 2^31 - 1 is a shape error before anything
+    is enqueued; n * k = 2^31 - 1024 is accepted."""
+    over = dict(n=1 << 21, k=1024, hidden=64, vocab=4096, chunk=4096)   # n k = 2^31
+    under = dict(over, n=(1 << 21) - 1)
+    ws = lm.lmhead_workspace_size
+    for entry in (lm.ENTRY_SUPPORT, lm.ENTRY_SUPPORT_KL):
+        for bwd in (0, 1):
+            assert ws(_p(**over), entry, bwd) == 0, (entry, bwd)
+            assert ws(_p(**under), entry, bwd) > 0, (entry, bwd)
+    # the single-id entries ignore k
+    assert ws(_p(**over), lm.ENTRY_CE_MEAN, 1) > 0
+    p = _p(**over)
+    S = lm.LMHEAD_ERR_SHAPE
+    assert lm.lmhead_support_logprob_kl(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, BIG, 0) == S
+    assert lm.lmhead_support_logprob(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, BIG, 0) == S
+    assert lm.lmhead_support_kl(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, BIG, 0) == S
+    for entry in (lm.ENTRY_SUPPORT, lm.ENTRY_SUPPORT_KL):
+        grad = FAKE if entry == lm.ENTRY_SUPPORT else None
+        assert lm.lmhead_loss_bwd(p, entry, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, grad, FAKE, FAKE, FAKE,
+                                  FAKE, BIG, 0) == S
+        assert lm.lmhead_loss_bwd_accumulate(p, entry, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, grad, FAKE,
+                                             FAKE, FAKE, None, None, FAKE, BIG, 0) == S
+    with pytest.raises(lm.LMHeadError) as e:
+        lm.memory_report(over["n"], 64, 4096, 4096, lm.ENTRY_SUPPORT, True, 1024)
+    assert e.value.status == S
+
+
+def test_chunk_width_is_capped():
+    """dL/dz of one chunk is read with a row pitch of the padded chunk width,
+    256 rows per buffer range below 2^31 bytes: round_up(min(chunk, vocab),
+    256) above 2^22 - 256 is a shape error for every entry with a
+    vocabulary-wide pass (the KL-only entry has none and ignores the chunk)."""
+    cap = (1 << 22) - 256
+    ws = lm.lmhead_workspace_size
+    big_v = 1 << 23
+    assert ws(_p(hidden=64, vocab=big_v, chunk=cap), lm.ENTRY_CE_MEAN, 1) > 0
+    assert ws(_p(hidden=64, vocab=big_v, chunk=cap + 256), lm.ENTRY_CE_MEAN, 1) == 0
+    assert ws(_p(hidden=64, vocab=big_v, chunk=cap + 256), lm.ENTRY_CE_MEAN, 0) == 0
+    # a chunk wider than the vocabulary counts as the vocabulary's width
+    assert ws(_p(hidden=64, vocab=cap, chunk=1 << 30), lm.ENTRY_LOGPROB, 1) > 0
+    assert ws(_p(hidden=64, vocab=cap + 1, chunk=1 << 30), lm.ENTRY_LOGPROB, 1) == 0
+    assert ws(_p(hidden=64, vocab=big_v, chunk=1 << 23, k=4), lm.ENTRY_SUPPORT, 1) == 0
+    assert ws(_p(hidden=64, vocab=big_v, chunk=1 << 23, k=4), lm.ENTRY_SUPPORT_KL, 1) > 0
+    p = _p(hidden=64, vocab=big_v, chunk=1 << 23)
+    assert lm.lmhead_loss_fwd(p, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, BIG, 0) == lm.LMHEAD_ERR_SHAPE
+    assert lm.lmhead_loss_bwd(p, 0, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, FAKE,
+                              BIG, 0) == lm.LMHEAD_ERR_SHAPE
+    # the planner never goes past the cap, whatever the budget
+    c = lm.plan_chunk(64, 64, big_v, 1 << 45)
+    assert c <= cap and c % 256 == 0 and ws(_p(hidden=64, vocab=big_v, chunk=c), 0, 1) > 0
+    assert c == 256 * -(-big_v // 3 // 256) + (256 if big_v % 3 else 0) or math.ceil(big_v / c) == 3

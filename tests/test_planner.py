@@ -97,3 +97,13 @@ def test_report_lists_dh_split_partials():
     assert lm.memory_report(8192, 4096, 151936, 8192, 0, True, 1)["dh_split_bytes"] == 0
     # chunk 512 has 8 K steps: too few to split
     assert lm.memory_report(256, 4096, 151936, 512, 0, True, 1)["dh_split_bytes"] == 0
+
+
+def test_dh_split_slices_are_capped():
+    """The dH K-split takes at most 16 slices, so its fp32 partials stay within
+    16 x [n, hidden] even where the chunk has many more K steps (n = 256,
+    hidden = 256, chunk 32768: 512 K steps, one dH tile)."""
+    for chunk in (8192, 32768, 65536):
+        r = lm.memory_report(256, 256, 151936, chunk, 0, True, 1)
+        assert 0 < r["dh_split_bytes"] <= 16 * 4 * 256 * 256, (chunk, r["dh_split_bytes"])
+    assert lm.memory_report(256, 256, 151936, 32768, 0, True, 1)["dh_split_bytes"] == 16 * 4 * 256 * 256
