@@ -383,6 +383,65 @@ def test_row_sample_matches_full():
     np.testing.assert_array_equal(dw, full["dW"][cols])
 
 
+_ROW_CASES = [
+    # (entry, padded, with KL grads, temperature, per-row temperature)
+    (oracle.ENTRY_CE_MEAN, False, False, 0.0, True),
+    (oracle.ENTRY_CE_SUM, False, False, 1.3, False),
+    (oracle.ENTRY_LOGPROB, False, False, 0.0, False),
+    (oracle.ENTRY_LOGPROB, False, False, 1.3, True),
+    (oracle.ENTRY_SUPPORT, False, True, 0.0, True),
+    (oracle.ENTRY_SUPPORT, False, False, 0.7, True),
+    (oracle.ENTRY_SUPPORT, True, True, 0.0, True),
+    (oracle.ENTRY_SUPPORT, True, False, 0.0, False),
+    (oracle.ENTRY_SUPPORT_KL, False, True, 0.0, True),
+    (oracle.ENTRY_SUPPORT_KL, True, True, 1.3, True),
+]
+
+
+@pytest.mark.parametrize("entry,padded,with_kl,temp,per_row", _ROW_CASES)
+def test_row_sample_matches_full_every_entry(entry, padded, with_kl, temp, per_row):
+    """The sampled-row path that the full-size GPU parity tests use equals the
+    pinned full path (oracle.run) on the same rows for every entry: CE mean and
+    sum, log-prob, support with and without the KL term, KL-only, padded
+    candidate lists, scalar and per-row temperatures. The rows are not a prefix
+    and every row has its own upstream gradient and temperature, so a per-row
+    input not indexed by the sampled rows changes the result."""
+    support = entry in (oracle.ENTRY_SUPPORT, oracle.ENTRY_SUPPORT_KL)
+    kw = dict(n=40, hidden=64, vocab=333, ignore_frac=0.1 if not support else 0.0, seed=31 + entry,
+              entry=entry if entry != oracle.ENTRY_SUPPORT_KL else oracle.ENTRY_SUPPORT,
+              k=6 if support else 1, pad_frac=0.3 if padded else 0.0)
+    wl, inp = _tiny_inputs(**kw)
+    rng = np.random.default_rng(5 + entry)
+    rt = rng.uniform(0.5, 2.0, size=40) if per_row else None
+    grad = inp.grad
+    if entry in (oracle.ENTRY_CE_MEAN, oracle.ENTRY_CE_SUM):
+        grad = np.array([0.75])
+    grad_kl = inp.grad_kl if with_kl else None
+    common = dict(targets=inp.targets, ids=inp.ids, ref_logq=inp.ref_logq,
+                  grad=None if entry == oracle.ENTRY_SUPPORT_KL else grad, grad_kl=grad_kl,
+                  temperature=temp, row_temperature=rt, padded=padded)
+    if entry == oracle.ENTRY_SUPPORT_KL:
+        common["grad_kl"] = inp.grad_kl
+    full = oracle.run(entry, inp.H, inp.W, **common)
+    rows = np.array([1, 7, 22, 39])
+    count = full.get("count")
+    s = oracle.rows_forward_backward(entry, inp.H, inp.W, rows, count=count, **common)
+    for key in ("lse", "loss_rows", "logp", "lp", "kl", "log_phat"):
+        if key in full and key in s:
+            np.testing.assert_allclose(s[key], full[key][rows], rtol=1e-13, atol=1e-15, err_msg=key)
+    expect = {oracle.ENTRY_CE_MEAN: ("lse", "loss_rows"), oracle.ENTRY_CE_SUM: ("lse", "loss_rows"),
+              oracle.ENTRY_LOGPROB: ("lse", "logp"), oracle.ENTRY_SUPPORT: ("lse", "lp"),
+              oracle.ENTRY_SUPPORT_KL: ("kl", "log_phat")}[entry]
+    for key in expect:
+        assert key in s, key
+    if entry == oracle.ENTRY_SUPPORT and inp.ref_logq is not None:
+        assert "kl" in s
+    np.testing.assert_allclose(s["dz"], full["dz"][rows], rtol=1e-13, atol=1e-16)
+    np.testing.assert_allclose(s["dH"], full["dH"][rows], rtol=1e-12, atol=1e-16)
+    # the sampled rows' gradient is not trivially zero
+    assert np.abs(s["dH"]).max() > 0
+
+
 # ------------------------------------------------------------------ mutations
 
 def test_mutations_are_caught(monkeypatch):
