@@ -181,7 +181,7 @@ def test_support_split_and_padding_host_checks():
     assert ws(_p(k=8, chunk=512), lm.ENTRY_SUPPORT_KL, 1) == kl_b
     assert ws(_p(k=0), lm.ENTRY_SUPPORT_KL, 0) == 0
     assert ws(_p(n=1 << 22, k=1024), lm.ENTRY_SUPPORT_KL, 0) == 0      # n * k >= 2^31
-    assert ws(_p(n=1 << 22, k=1024), lm.ENTRY_SUPPORT, 0) > 0
+    assert ws(_p(n=1 << 22, k=1024), lm.ENTRY_SUPPORT, 0) == 0         # int32 buckets too
     pk = _p(k=8)
     f = lm.lmhead_support_kl
     assert f(pk, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, BIG, 0) == lm.LMHEAD_ERR_ARG   # ref_logq
