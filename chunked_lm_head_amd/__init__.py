@@ -8,7 +8,7 @@ every entry raises.
 
 Two layers:
 
-* ``lmhead_workspace_size``, ``lmhead_loss_fwd``, ``lmhead_logprob``,
+* ``lmhead_workspace_size``, ``lmhead_loss_fwd``, ``lmhead_loss_fwd_noalloc``, ``lmhead_logprob``,
   ``lmhead_support_logprob_kl``, ``lmhead_support_logprob``,
   ``lmhead_support_kl``, ``lmhead_loss_bwd``,
   ``lmhead_loss_bwd_accumulate``, ``lmhead_memory_report``,
@@ -40,6 +40,8 @@ LMHEAD_ERR_ALIGN = 3
 LMHEAD_ERR_WORKSPACE = 4
 LMHEAD_ERR_DEVICE = 5
 LMHEAD_ERR_HIP = 6
+LMHEAD_ERR_SCRATCH = 7
+STATIC_SCRATCH_BYTES = 64 << 20
 
 ENTRY_CE_MEAN = 0
 ENTRY_CE_SUM = 1
@@ -115,6 +117,7 @@ def lib() -> ctypes.CDLL:
         L.lmhead_workspace_size.argtypes = [P, i32, i32]
         L.lmhead_workspace_size.restype = sz
         L.lmhead_loss_fwd.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.lmhead_loss_fwd_noalloc.argtypes = [P, i32, vp, vp, vp, vp, vp, vp]
         L.lmhead_logprob.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
         L.lmhead_support_logprob_kl.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.lmhead_support_logprob.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -128,7 +131,7 @@ def lib() -> ctypes.CDLL:
         L.lmhead_status_string.restype = ctypes.c_char_p
         L.lmhead_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32),
                                                ctypes.POINTER(ctypes.c_int64)]
-        for f in (L.lmhead_loss_fwd, L.lmhead_logprob, L.lmhead_support_logprob_kl,
+        for f in (L.lmhead_loss_fwd, L.lmhead_loss_fwd_noalloc, L.lmhead_logprob, L.lmhead_support_logprob_kl,
                   L.lmhead_support_logprob, L.lmhead_support_kl,
                   L.lmhead_loss_bwd, L.lmhead_loss_bwd_accumulate, L.lmhead_read_device_error,
                   L.lmhead_memory_report, L.lmhead_plan_chunk):
@@ -190,6 +193,11 @@ def plan_chunk(n: int, hidden: int, vocab: int, budget_bytes: int, entry: int = 
 def lmhead_loss_fwd(p, entry, H, W, targets, loss, lse, workspace, workspace_bytes, stream=None) -> int:
     return lib().lmhead_loss_fwd(ctypes.byref(p), entry, _p(H), _p(W), _p(targets), _p(loss),
                                  _p(lse), _p(workspace), workspace_bytes, _stream(stream))
+
+
+def lmhead_loss_fwd_noalloc(p, entry, H, W, targets, loss, lse, stream=None) -> int:
+    return lib().lmhead_loss_fwd_noalloc(ctypes.byref(p), entry, _p(H), _p(W), _p(targets), _p(loss),
+                                         _p(lse), _stream(stream))
 
 
 def lmhead_logprob(p, H, W, targets, logp, lse, workspace, workspace_bytes, stream=None) -> int:

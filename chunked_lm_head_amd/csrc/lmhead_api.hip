@@ -8,6 +8,7 @@
 
 #include <atomic>
 #include <functional>
+#include <mutex>
 #include <queue>
 #include <vector>
 
@@ -595,9 +596,54 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
 }
 
 
+// The allocation-free forward's workspace: a file-scope device array, one
+// copy per device, held until the process ends. Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol); it uses the device address hipGetSymbolAddress returns, fetched
+// once per device with that device current.
+constexpr size_t kScratchBytes = LMHEAD_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[256];
+
+int scratch_base(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return LMHEAD_ERR_DEVICE;
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (ptr == nullptr) {
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+                return LMHEAD_ERR_HIP;
+            g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return LMHEAD_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int lmhead_loss_fwd_noalloc(const lmhead_problem* p, int entry, const void* H, const void* W,
+                            const int32_t* targets, float* loss, float* lse, void* stream) {
+    if (entry != LMHEAD_ENTRY_CE_MEAN && entry != LMHEAD_ENTRY_CE_SUM) return LMHEAD_ERR_ARG;
+    int st = validate_problem(p, entry);
+    if (st != LMHEAD_OK) return st;
+    if (plan(*p, entry).fwd_total > kScratchBytes) return LMHEAD_ERR_SCRATCH;
+    st = check_device();
+    if (st != LMHEAD_OK) return st;
+    void* ws = nullptr;
+    st = scratch_base(&ws);
+    if (st != LMHEAD_OK) return st;
+    // the header words that must start at zero are cleared by the forward's
+    // first kernel; every other region is written before it is read
+    return forward(p, entry, H, W, targets, nullptr, nullptr, nullptr, lse, loss, ws, kScratchBytes,
+                   stream);
+}
 
 size_t lmhead_workspace_size(const lmhead_problem* p, int entry, int with_backward) {
     if (validate_problem(p, entry) != LMHEAD_OK) return 0;
@@ -763,6 +809,8 @@ const char* lmhead_status_string(int status) {
         case LMHEAD_ERR_WORKSPACE: return "workspace too small";
         case LMHEAD_ERR_DEVICE: return "no gfx950 (MI355X) device is current";
         case LMHEAD_ERR_HIP: return "HIP runtime error";
+        case LMHEAD_ERR_SCRATCH:
+            return "forward workspace larger than the static scratch buffer (LMHEAD_STATIC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

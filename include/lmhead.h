@@ -70,7 +70,9 @@ enum lmhead_status {
     LMHEAD_ERR_ALIGN = 3,      /* a device pointer not 16-byte aligned (workspace: 256) */
     LMHEAD_ERR_WORKSPACE = 4,  /* workspace_bytes < lmhead_workspace_size(...) */
     LMHEAD_ERR_DEVICE = 5,     /* current device is not gfx950 or no device */
-    LMHEAD_ERR_HIP = 6         /* a HIP launch or runtime call failed */
+    LMHEAD_ERR_HIP = 6,        /* a HIP launch or runtime call failed */
+    LMHEAD_ERR_SCRATCH = 7     /* lmhead_loss_fwd_noalloc: the problem's forward workspace
+                                  exceeds LMHEAD_STATIC_SCRATCH_BYTES */
 };
 
 /* Loss entries ([PR8059]: CE loss, log-probability entry, support-set entries). */
@@ -211,6 +213,27 @@ int lmhead_loss_fwd(const lmhead_problem* p, int entry,
                     const void* H, const void* W, const int32_t* targets,
                     float* loss, float* lse,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free variant of lmhead_loss_fwd, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Same arguments (minus the workspace),
+ * results and bits as lmhead_loss_fwd. Its workspace is a static device
+ * buffer inside this library, LMHEAD_STATIC_SCRATCH_BYTES (64 MiB) per
+ * device, held until the process ends; the call allocates nothing.
+ *   Returns LMHEAD_ERR_SCRATCH, before anything is enqueued, when the
+ *   problem's forward workspace (lmhead_workspace_size(p, entry, 0)) is
+ *   larger than that buffer; host errors as lmhead_loss_fwd otherwise.
+ *   Every call on one device shares that device's buffer, which keeps the
+ *   last call's contents: calls that overlap on one device (two streams or
+ *   two host threads without ordering between them) race, so serialise them.
+ *   The device error word lives in that buffer and cannot be read with
+ *   lmhead_read_device_error; a label >= vocab shows as a NaN loss.
+ */
+#define LMHEAD_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int lmhead_loss_fwd_noalloc(const lmhead_problem* p, int entry,
+                            const void* H, const void* W, const int32_t* targets,
+                            float* loss, float* lse, void* stream);
 
 /*
  * Per-token log-probability ([PR8059] "the log-probability entry"; the RL

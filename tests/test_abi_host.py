@@ -31,7 +31,8 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
     assert names == sorted([
-        "lmhead_loss_bwd", "lmhead_loss_bwd_accumulate", "lmhead_loss_fwd", "lmhead_logprob",
+        "lmhead_loss_bwd", "lmhead_loss_bwd_accumulate", "lmhead_loss_fwd", "lmhead_loss_fwd_noalloc",
+        "lmhead_logprob",
         "lmhead_memory_report", "lmhead_plan_chunk", "lmhead_read_device_error",
         "lmhead_support_kl", "lmhead_support_logprob",
         "lmhead_status_string", "lmhead_support_logprob_kl", "lmhead_workspace_size"])
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in range(7):
+    for st in range(8):
         assert lm.lmhead_status_string(st)
     assert lm.lmhead_status_string(99) == "unknown status"
 
@@ -255,3 +256,15 @@ def test_chunk_width_is_capped():
     c = lm.plan_chunk(64, 64, big_v, 1 << 45)
     assert c <= cap and c % 256 == 0 and ws(_p(hidden=64, vocab=big_v, chunk=c), 0, 1) > 0
     assert c == 256 * -(-big_v // 3 // 256) + (256 if big_v % 3 else 0) or math.ceil(big_v / c) == 3
+
+
+def test_noalloc_forward_host_checks():
+    """The allocation-free forward refuses, before touching a device, a problem
+    whose forward workspace exceeds its static buffer, and a non-CE entry."""
+    big = lm.problem(1 << 16, 256, 1 << 17, 1024, -1, 1)
+    assert lm.lmhead_workspace_size(big, 0, 0) > lm.STATIC_SCRATCH_BYTES
+    f = lm.lmhead_loss_fwd_noalloc
+    assert f(big, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == lm.LMHEAD_ERR_SCRATCH
+    assert f(_p(), lm.ENTRY_LOGPROB, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == lm.LMHEAD_ERR_ARG
+    assert f(_p(hidden=96), 0, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == lm.LMHEAD_ERR_SHAPE
+    assert "static scratch" in lm.lmhead_status_string(lm.LMHEAD_ERR_SCRATCH)
