@@ -91,6 +91,7 @@ class lmhead_memory_figures(ctypes.Structure):
         ("dh_acc_bytes", ctypes.c_size_t),
         ("caller_output_bytes", ctypes.c_size_t),
         ("dh_split_bytes", ctypes.c_size_t),
+        ("operand_copy_bytes", ctypes.c_size_t),
     ]
 
 

@@ -375,6 +375,185 @@ __device__ __forceinline__ void gemm_mainloop(const Operand& A, int64_t m0, cons
     __syncthreads();
 }
 
+// ------------------------------------------------------------------------
+// The direct-A K loop (logits contractions: A = H, B = W or a chunk of it,
+// both contraction-contiguous). A is read from a copy of H in MFMA fragment
+// order and goes from memory straight into the fragment registers; only B is
+// staged in LDS, and it gets there without registers, by buffer loads that
+// write LDS directly. Against the staged core above this halves the LDS
+// traffic per K step (B only: 32 KB written and 64 KB read per workgroup
+// instead of 64 and 128) and drops every LDS store instruction from the loop.
+//
+// Fragment order: 16-row x 32-k blocks of 1 KB, block (m / 16, k / 32) at
+// ((m / 16) * (K / 32) + k / 32) * 1 KB, lane l's 16 bytes (row l % 16, k
+// 8 (l / 16) .. + 8: exactly the lane's A operand of one
+// v_mfma_f32_16x16x32_bf16) at byte 16 l of the block. One fragment load is
+// one fully used 1 KB block (eight 128-byte lines); reading the same
+// fragments from the row-major H touches 16 rows per 16 lanes and ran at
+// 0.40 MFMA busy, limited by the vector cache's line rate. Rows past n are
+// stored as zeros, so a tile never reads past its operand.
+//
+// Register ring: fragments of K steps kt and kt + 1 (2 x 2 substeps x 8
+// blocks x 4 registers = 128 VGPRs); the fragment of step kt is reloaded with
+// step kt + 2's right after its last MFMA, so each load has two K steps to
+// land. LDS ring: four B stages of 32 KB (K-major tile rows of 128 bytes,
+// 16-byte chunk q of row r at q ^ ((r >> 1) & 7), the layout of the staged
+// core); during step kt each wave issues eight 1 KB loads of step kt + 3 into
+// the stage step kt - 1 released. The stage barrier (mid-step, between the
+// passes of the second substep) waits only for this wave's loads of step
+// kt + 1: 48 loads were issued after them (the rest of step kt - 2, all of
+// step kt - 1 and step kt up to the barrier, 24 per step), so vmcnt(48)
+// leaves the later ones in flight; the compiler's own barrier fence would
+// wait for every load, since it counts the LDS-writing loads as LDS stores.
+constexpr int kDaStage = kTile * kTileK * 2;   // one K-major B tile: 32 KB
+constexpr int kDaStages = 4;
+static_assert(kDaStages * kDaStage <= kLdsBytes, "B ring must fit the LDS");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+struct DaCtx {
+    __amdgpu_buffer_rsrc_t ra;   // A: the tile's 256 rows of the fragment-order copy
+    uint32_t va;                 // lane offset in A: the wave's row half, lane's 16 bytes
+    uint32_t kblk;               // bytes per 16-row block of A (K / 32 KB)
+    __amdgpu_buffer_rsrc_t rb;   // B: the tile's rows, range ending at the operand's last row
+    uint32_t vb[2];              // lane offset in B for even / odd chunk u (swizzle parity)
+    uint32_t brow8;              // bytes per 8 rows of B
+    int64_t KT;
+    char* smem;
+    int wave, lane;
+};
+
+// Fragment (substep s, block i) of K step kt (clamped to the last step).
+__device__ __forceinline__ bf16x8 da_a(const DaCtx& c, int64_t kt, int s, int i) {
+    const int64_t ktc = kt < c.KT ? kt : c.KT - 1;
+    const uint32_t soff = (uint32_t)i * c.kblk + (uint32_t)(ktc * 2048 + s * 1024);
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(c.ra, c.va, soff, 0));
+}
+
+// Load u (0..7) of a wave for B step kt into stage ST: LDS rows
+// 64 w + 8 u .. + 8 of the stage, 1 KB written in lane order; lane p loads
+// the global chunk that belongs at its position ((p % 8) ^ swizzle of its row).
+template <int ST>
+__device__ __forceinline__ void da_b(const DaCtx& c, int64_t kt, int u) {
+    const int64_t ktc = kt < c.KT ? kt : c.KT - 1;
+    char* dst = c.smem + ST * kDaStage + (c.wave * 64 + u * 8) * 128;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rb, (lds_void_t*)dst, 16, c.vb[u & 1],
+                                             (uint32_t)u * c.brow8 + (uint32_t)(ktc * 128), 0, 0);
+}
+
+// K step kt, reading B stage ST = kt % 4; same MFMA order and fragment reads
+// as pg_step. B loads of step kt + 3 go out every 12 MFMAs from the first.
+template <int ST>
+__device__ __forceinline__ void da_step(const DaCtx& c, int64_t kt, AccTile& acc, bf16x8 (&fa)[2][2][8],
+                                        bf16x8 (&fb)[8]) {
+    constexpr int P = ST & 1;
+    const char* cur = c.smem + ST * kDaStage;
+    const char* nxt = c.smem + ((ST + 1) & 3) * kDaStage;
+    const int br = (c.wave & 1) * 128;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int t = 0; t < 32; ++t) {
+            const int bi = t >> 2, bj = t & 3;
+            mma16(acc[bi][bj], fa[P][s][bi], fb[bj]);
+            if ((t & 1) && t < 8) fb[4 + (t >> 1)] = frag16(cur, br + 16 * (4 + (t >> 1)), s, c.lane);
+            const int pos = s * 64 + t;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (u * 12 == pos) da_b<(ST + 3) & 3>(c, kt + 3, u);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (s == 1) {
+            asm volatile("s_waitcnt vmcnt(48) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const char* src = s == 0 ? cur : nxt;
+        const int s2 = s == 0 ? 1 : 0;
+#pragma unroll
+        for (int t = 0; t < 32; ++t) {
+            const int bi = t >> 2, bj = 4 + (t & 3);
+            mma16(acc[bi][bj], fa[P][s][bi], fb[bj]);
+            if ((t & 3) == 3) fa[P][s][bi] = da_a(c, kt + 2, s, bi);
+            if ((t & 1) && t < 8) fb[t >> 1] = frag16(src, br + 16 * (t >> 1), s2, c.lane);
+            const int pos = s * 64 + 32 + t;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (u * 12 == pos) da_b<(ST + 3) & 3>(c, kt + 3, u);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// C[m0.., n0..] = sum_k A(m, k) B(n, k) for one 256 x 256 tile. Af: the
+// fragment-order copy of A (row count a multiple of 256, rows past the
+// operand zero); B K-major (rows at or past B.rows read as zero). K: a
+// multiple of 64. Every accumulator gets the same products in the same MFMA
+// slots as gemm_mainloop<false, false>, so the two give identical bits.
+__device__ __forceinline__ void gemm_mainloop_da(const bf16_bits* Af, int64_t m0, const Operand& B, int64_t n0,
+                                                 int64_t K, char* smem, AccTile& acc) {
+    const int tid = threadIdx.x;
+    DaCtx c;
+    c.KT = K / kTileK;
+    c.smem = smem;
+    c.lane = tid & 63;
+    c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    c.ra = __builtin_amdgcn_make_buffer_rsrc((void*)(Af + m0 * K), 0, (int)(kTile * K * 2), 0x00020000);
+    c.kblk = (uint32_t)(K / 32 * 1024);
+    c.va = (uint32_t)((c.wave >> 1) * 8 * c.kblk + c.lane * 16);
+    {
+        const int64_t rows = B.rows - n0 < kTile ? B.rows - n0 : kTile;
+        c.rb = __builtin_amdgcn_make_buffer_rsrc((void*)(B.ptr + n0 * B.ld), 0, (int)(rows * B.ld * 2),
+                                                 0x00020000);
+        // row r + 8 u has swizzle(r) ^ 4 for odd u
+        const int r = c.wave * 64 + (c.lane >> 3);
+        const int q = (c.lane & 7) ^ swizzle(r);
+        c.vb[0] = (uint32_t)((r * B.ld + q * 8) * 2);
+        c.vb[1] = (uint32_t)((r * B.ld + (q ^ 4) * 8) * 2);
+        c.brow8 = (uint32_t)(8 * B.ld * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
+    bf16x8 fa[2][2][8];
+    // prologue: B steps 0, 1, 2 into stages 0, 1, 2; A steps 0 and 1 into the ring
+#pragma unroll
+    for (int u = 0; u < 8; ++u) da_b<0>(c, 0, u);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) fa[0][s][i] = da_a(c, 0, s, i);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) da_b<1>(c, 1, u);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) fa[1][s][i] = da_a(c, 1, s, i);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) da_b<2>(c, 2, u);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    bf16x8 fb[8];
+    const int br = (c.wave & 1) * 128;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = frag16(smem, br + 16 * j, 0, c.lane);
+    int64_t kt = 0;
+    for (; kt + 3 < c.KT; kt += 4) {
+        da_step<0>(c, kt, acc, fa, fb);
+        da_step<1>(c, kt + 1, acc, fa, fb);
+        da_step<2>(c, kt + 2, acc, fa, fb);
+        da_step<3>(c, kt + 3, acc, fa, fb);
+    }
+    if (kt < c.KT) da_step<0>(c, kt, acc, fa, fb);
+    if (kt + 1 < c.KT) da_step<1>(c, kt + 1, acc, fa, fb);
+    if (kt + 2 < c.KT) da_step<2>(c, kt + 2, acc, fa, fb);
+    mma_drain();
+    // every load (the clamped ones past the last step included) has landed
+    // before the epilogue reuses the LDS
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Write the accumulators of the waves whose column half is `half` into the
 // fp32 staging area S laid out [column 0..127][row 0..255] (stride kEpiStride):
 // afterwards thread t can walk row t of that half with conflict-free reads.

@@ -43,8 +43,10 @@ struct HitRegions {
 struct Layout {
     int64_t n, n_pad, hidden, vocab, chunk, w_pad, tiles_v, k;
     HitRegions hit_fwd, hit_bwd;
-    // forward regions
-    size_t hdr, lse, part, zg, rows;
+    // forward regions (hfrag_fwd: H in MFMA fragment order, n_pad rows)
+    size_t hdr, lse, part, zg, rows, hfrag_fwd;
+    size_t hfrag_bwd;                 // the backward's own copy (workspace contents do not survive calls)
+    int64_t hfrag_bytes;
     // backward regions
     size_t coef_a, coef_c, G, dh_acc;
     size_t dh_part;   // fp32 partial dH tiles of the K-split (few row tiles only)
@@ -135,6 +137,8 @@ Layout plan(const lmhead_problem& p, int entry) {
         R.large = take(4 * nb);
         R.n_large = take(4);
     };
+    L.hfrag_bytes = 2 * L.n_pad * L.hidden;
+    L.hfrag_fwd = take(L.hfrag_bytes);
     L.lse = take(4 * L.n);
     L.part = take(8 * L.tiles_v * L.n);
     L.zg = take(4 * L.n * L.k);
@@ -142,6 +146,7 @@ Layout plan(const lmhead_problem& p, int entry) {
     if (buckets) take_hits(L.hit_fwd);
     L.fwd_total = off;
     off = after_hdr;
+    L.hfrag_bwd = take(L.hfrag_bytes);
     L.coef_a = take(4 * L.n_pad);
     L.coef_c = take(4 * L.n * L.k);
     L.G = take(2 * L.n_pad * L.w_pad);
@@ -339,9 +344,11 @@ int forward(const lmhead_problem* p, int entry, const void* H, const void* W, co
     const int mode = entry == LMHEAD_ENTRY_SUPPORT ? 1 + padded : 0;
     scan_labels_kernel<<<grid_1d(L.n, kThreads, 1024), kThreads, 0, s>>>(ids, L.n, (int)L.k, L.vocab,
                                                                           mode, T, hdr);
+    frag_pack_kernel<<<grid_1d(L.n_pad * L.hidden / 8, kThreads, 8192), kThreads, 0, s>>>(
+        (const bf16_bits*)H, L.n, L.hidden, L.n_pad, (bf16_bits*)(w + L.hfrag_fwd));
     FwdTilesArgs fa;
     fa.T = T;
-    fa.H = (const bf16_bits*)H;
+    fa.Hf = (const bf16_bits*)(w + L.hfrag_fwd);
     fa.W = (const bf16_bits*)W;
     fa.n = L.n;
     fa.hidden = L.hidden;
@@ -507,6 +514,9 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
     }
 
     bf16_bits* G = (bf16_bits*)(w + L.G);
+    const bf16_bits* Hf = (const bf16_bits*)(w + L.hfrag_bwd);
+    frag_pack_kernel<<<grid_1d(L.n_pad * L.hidden / 8, kThreads, 8192), kThreads, 0, s>>>(
+        (const bf16_bits*)H, L.n, L.hidden, L.n_pad, (bf16_bits*)Hf);
     const int32_t* hit_offsets = nullptr;
     const int32_t* hit_list = nullptr;
     if (entry == LMHEAD_ENTRY_SUPPORT) build_hits(L, L.hit_bwd, w, ids, s, &hit_offsets, &hit_list);
@@ -521,7 +531,7 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
 
         LogitGradArgs ga;
         ga.T = T;
-        ga.H = (const bf16_bits*)H;
+        ga.Hf = Hf;
         ga.Wc = Wc;
         ga.n = L.n;
         ga.n_pad = L.n_pad;
@@ -664,6 +674,7 @@ int lmhead_memory_report(const lmhead_problem* p, int entry, int with_backward,
     r.forward_bytes = L.fwd_total;
     const bool kl_only = entry == LMHEAD_ENTRY_SUPPORT_KL;
     r.partials_bytes = kl_only ? 0 : (size_t)(8 * L.tiles_v * L.n);
+    if (!kl_only) r.operand_copy_bytes = (size_t)L.hfrag_bytes;
     if (with_backward && !kl_only) {
         r.dz_chunk_bytes = (size_t)(2 * L.n_pad * L.w_pad);
         r.dh_acc_bytes = (size_t)(4 * L.n * L.hidden);

@@ -40,7 +40,7 @@ __device__ __forceinline__ float row_tau(const Temperature& T, int64_t row) {
 __device__ __forceinline__ bool tau_ok(float tau) { return tau > 0.0f && tau <= 3.402823466e38f; }
 
 struct FwdTilesArgs {
-    const bf16_bits* H;
+    const bf16_bits* Hf;   // H in MFMA fragment order (frag_pack_kernel), n_pad rows
     const bf16_bits* W;
     int64_t n, hidden, vocab;
     int64_t tiles_m, tiles_n;
@@ -89,7 +89,7 @@ struct CoeffArgs {
 };
 
 struct LogitGradArgs {
-    const bf16_bits* H;
+    const bf16_bits* Hf;   // H in MFMA fragment order (frag_pack_kernel), n_pad rows
     const bf16_bits* Wc;   // first row of the chunk
     int64_t n, n_pad, hidden;
     int64_t v0, width, w_pad;
@@ -160,6 +160,7 @@ __global__ void init_header_kernel(int32_t* hdr);
 __global__ void scan_labels_kernel(const int32_t* ids, int64_t n, int k, int64_t vocab, int support,
                                    Temperature T, int32_t* hdr);
 __global__ void fill_u32_kernel(uint32_t* p, int64_t count, uint32_t value);
+__global__ void frag_pack_kernel(const bf16_bits* H, int64_t n, int64_t hidden, int64_t n_pad, bf16_bits* Hf);
 __global__ void fwd_tiles_kernel(FwdTilesArgs a);
 __global__ void finalize_rows_kernel(FinalizeArgs a);
 __global__ void ce_reduce_kernel(const float* rows, int64_t n, const int32_t* hdr, int64_t num_valid,

@@ -93,6 +93,29 @@ __device__ __forceinline__ bool id_in_tile(const int32_t* idr, uint32_t col0, in
     return d < (uint32_t)ncol;
 }
 
+// ---------------------------------------------------- H in fragment order
+
+// Hf = H in MFMA fragment order (the A operand of the direct-A K loop):
+// 16-row x 32-column blocks of 1 KB, block (m / 16, k / 32) at
+// ((m / 16) * (hidden / 32) + k / 32) * 512 elements, lane l's 8 elements
+// (row m0 + l % 16, columns k0 + 8 (l / 16) .. + 8) at element 8 l of the
+// block; rows n .. n_pad - 1 are zero. One thread per 16-byte piece, pieces in
+// output order (the stores are contiguous per wave).
+__global__ void frag_pack_kernel(const bf16_bits* H, int64_t n, int64_t hidden, int64_t n_pad, bf16_bits* Hf) {
+    const int64_t pieces = n_pad * hidden / 8;
+    const int64_t kb_count = hidden / 32;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < pieces;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t blk = q >> 6;
+        const int l = (int)(q & 63);
+        const int64_t m = (blk / kb_count) * 16 + (l & 15);
+        const int64_t k = (blk % kb_count) * 32 + 8 * (l >> 4);
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (m < n) v = *reinterpret_cast<const uint4*>(H + m * hidden + k);
+        *reinterpret_cast<uint4*>(Hf + q * 8) = v;
+    }
+}
+
 // ------------------------------------------------------------- forward tiles
 
 // One 256-row x 256-column logits tile: z = H W^T on MFMA, then per row the
@@ -106,8 +129,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTilesArgs a) 
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
 
     AccTile acc;
-    gemm_mainloop<false, false>(Operand{a.H, a.hidden, a.n}, m0, Operand{a.W, a.hidden, a.vocab}, n0, a.hidden,
-                  smem, acc);
+    gemm_mainloop_da(a.Hf, m0, Operand{a.W, a.hidden, a.vocab}, n0, a.hidden, smem, acc);
 
     float* S = reinterpret_cast<float*>(smem);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -430,8 +452,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
 
     AccTile acc;
-    gemm_mainloop<false, false>(Operand{a.H, a.hidden, a.n}, m0, Operand{a.Wc, a.hidden, a.width}, n0, a.hidden,
-                  smem, acc);
+    gemm_mainloop_da(a.Hf, m0, Operand{a.Wc, a.hidden, a.width}, n0, a.hidden, smem, acc);
 
     float* S = reinterpret_cast<float*>(smem);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
