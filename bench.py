@@ -50,6 +50,9 @@ def parse():
                          "path's shapes, outside the timed region, and report them under vendor_gemm")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run one device-to-device copy of BYTES (counter calibration)")
+    ap.add_argument("--other-steps", type=int, default=5,
+                    help="timed steps of each other workload (log-prob, dense support, KL-only "
+                         "support) reported under other_workloads; 0 skips them")
     return ap.parse_args()
 
 
@@ -113,94 +116,15 @@ def main():
     inp = workloads.make_inputs(wl)
     log(f"inputs for {wl.name} drawn in {time.time() - t0:.1f}s")
 
-    def bf16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    H, W = bf16(inp.H), bf16(inp.W)
     entry = workloads.ENTRY_SUPPORT_KL if args.kl_only else wl.entry
-    k = wl.k if entry in (workloads.ENTRY_SUPPORT, workloads.ENTRY_SUPPORT_KL) else 1
-    idx = torch.from_numpy(inp.targets if inp.targets is not None else inp.ids).to(dev)
-    grad = torch.from_numpy(inp.grad).to(dev)
-    ref_logq = torch.from_numpy(inp.ref_logq).to(dev) if inp.ref_logq is not None else None
-    grad_kl = torch.from_numpy(inp.grad_kl).to(dev) if inp.grad_kl is not None else None
-
-    p = lm.problem(wl.n, wl.hidden, wl.vocab, wl.chunk, -1, k)
-    ws_bytes = lm.lmhead_workspace_size(p, entry, 1)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    loss = torch.empty(1, dtype=torch.float32, device=dev)
-    lse = torch.empty(wl.n, dtype=torch.float32, device=dev)
-    row_out = torch.empty((wl.n, k) if k > 1 else (wl.n,), dtype=torch.float32, device=dev)
-    kl = torch.empty(wl.n, dtype=torch.float32, device=dev)
-    dH = torch.empty_like(H)
-    dW = torch.empty_like(W)
-    stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
-    log(f"workspace {ws_bytes / 2**20:.1f} MiB; dtype bf16; chunk {wl.chunk}")
-
-    def fwd():
-        if entry in (workloads.ENTRY_CE_MEAN, workloads.ENTRY_CE_SUM):
-            st = lm.lmhead_loss_fwd(p, entry, H, W, idx, loss, lse, ws, ws_bytes, sp)
-        elif entry == workloads.ENTRY_LOGPROB:
-            st = lm.lmhead_logprob(p, H, W, idx, row_out, lse, ws, ws_bytes, sp)
-        elif entry == workloads.ENTRY_SUPPORT:
-            st = lm.lmhead_support_logprob_kl(p, H, W, idx, ref_logq, row_out, kl, lse, ws,
-                                              ws_bytes, sp)
-        else:   # KL-only: row_out holds log p_hat
-            st = lm.lmhead_support_kl(p, H, W, idx, ref_logq, kl, row_out, ws, ws_bytes, sp)
-        if st:
-            raise lm.LMHeadError(st, "forward")
-
-    def bwd():
-        if entry == workloads.ENTRY_SUPPORT_KL:
-            st = lm.lmhead_loss_bwd(p, entry, H, W, idx, ref_logq, None, row_out, None, grad_kl,
-                                    dH, dW, ws, ws_bytes, sp)
-        else:
-            saved = row_out if entry == workloads.ENTRY_SUPPORT else None
-            st = lm.lmhead_loss_bwd(p, entry, H, W, idx, ref_logq, lse, saved, grad, grad_kl, dH,
-                                    dW, ws, ws_bytes, sp)
-        if st:
-            raise lm.LMHeadError(st, "backward")
-
-    for _ in range(args.warmup):
-        fwd()
-        bwd()
-    torch.cuda.synchronize()
-    log(f"{args.warmup} warmup steps done")
-
+    run = Runner(torch, lm, workloads, wl, inp, entry, dev)
+    t = time_steps(torch, run, args.steps, args.warmup)
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record(stream)
-        fwd()
-        ev[i][1].record(stream)
-        bwd()
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    fwd_ms = [a.elapsed_time(b) for a, b, _ in ev]
-    bwd_ms = [b.elapsed_time(c) for _, b, c in ev]
-    step_ms = [a.elapsed_time(c) for a, _, c in ev]
-    ms_per_step = wall * 1e3 / K
-    log(f"timed {K} steps: wall {ms_per_step:.3f} ms/step; events fwd {np.mean(fwd_ms):.3f} "
-        f"bwd {np.mean(bwd_ms):.3f} step {np.mean(step_ms):.3f} ms")
-
-    # determinism: the last timed step's outputs against one more step
-    def digest():
-        torch.cuda.synchronize()
-        h = hashlib.sha256()
-        for t in (loss, lse, row_out, dH, dW):
-            h.update(t.view(torch.uint8).cpu().numpy().tobytes())
-        return h.hexdigest()
-
-    d1 = digest()
-    fwd()
-    bwd()
-    d2 = digest()
-    deterministic = d1 == d2
-    log(f"bitwise repeat: {deterministic} ({d1[:16]})")
+    wall, ms_per_step = t["wall_s"], t["ms_per_step"]
+    fwd_ms, bwd_ms, step_ms = t["fwd_ms"], t["bwd_ms"], t["step_ms"]
+    deterministic = t["deterministic"]
+    k = run.k
+    H, W, stream = run.H, run.W, run.stream
 
     flops = wl.flops_fwd_bwd
     tokens_per_s = wl.n * K / wall
@@ -293,7 +217,162 @@ def main():
         out["vendor_gemm"] = vendor_gemm(torch, H, W, wl, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds, entry)
+    if args.other_steps > 0 and args.workload == "headline" and not args.kl_only:
+        del run, H, W, inp
+        torch.cuda.empty_cache()
+        out["other_workloads"] = other_workloads(torch, lm, workloads, dev, args.other_steps)
     print(json.dumps(out), flush=True)
+
+
+class Runner:
+    """One entry's inputs on the device, its outputs and workspace allocated
+    once, and its forward / backward through the C ABI on the current stream."""
+
+    def __init__(self, torch, lm, workloads, wl, inp, entry, dev):
+        def bf16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        self.torch, self.lm, self.entry = torch, lm, entry
+        E = workloads
+        self.E = E
+        self.H, self.W = bf16(inp.H), bf16(inp.W)
+        k = wl.k if entry in (E.ENTRY_SUPPORT, E.ENTRY_SUPPORT_KL) else 1
+        self.k = k
+        self.idx = torch.from_numpy(inp.targets if inp.targets is not None else inp.ids).to(dev)
+        self.grad = torch.from_numpy(inp.grad).to(dev)
+        self.ref_logq = torch.from_numpy(inp.ref_logq).to(dev) if inp.ref_logq is not None else None
+        self.grad_kl = torch.from_numpy(inp.grad_kl).to(dev) if inp.grad_kl is not None else None
+        self.p = lm.problem(wl.n, wl.hidden, wl.vocab, wl.chunk, -1, k)
+        self.ws_bytes = lm.lmhead_workspace_size(self.p, entry, 1)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.loss = torch.empty(1, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(wl.n, dtype=torch.float32, device=dev)
+        self.row_out = torch.empty((wl.n, k) if k > 1 else (wl.n,), dtype=torch.float32, device=dev)
+        self.kl = torch.empty(wl.n, dtype=torch.float32, device=dev)
+        self.dH = torch.empty_like(self.H)
+        self.dW = torch.empty_like(self.W)
+        self.stream = torch.cuda.current_stream()
+        self.sp = self.stream.cuda_stream
+        log(f"{wl.name}: workspace {self.ws_bytes / 2**20:.1f} MiB; dtype bf16; chunk {wl.chunk}")
+
+    def fwd(self):
+        lm, E, e = self.lm, self.E, self.entry
+        if e in (E.ENTRY_CE_MEAN, E.ENTRY_CE_SUM):
+            st = lm.lmhead_loss_fwd(self.p, e, self.H, self.W, self.idx, self.loss, self.lse, self.ws,
+                                    self.ws_bytes, self.sp)
+        elif e == E.ENTRY_LOGPROB:
+            st = lm.lmhead_logprob(self.p, self.H, self.W, self.idx, self.row_out, self.lse, self.ws,
+                                   self.ws_bytes, self.sp)
+        elif e == E.ENTRY_SUPPORT:
+            st = lm.lmhead_support_logprob_kl(self.p, self.H, self.W, self.idx, self.ref_logq, self.row_out,
+                                              self.kl, self.lse, self.ws, self.ws_bytes, self.sp)
+        else:   # KL-only: row_out holds log p_hat
+            st = lm.lmhead_support_kl(self.p, self.H, self.W, self.idx, self.ref_logq, self.kl, self.row_out,
+                                      self.ws, self.ws_bytes, self.sp)
+        if st:
+            raise lm.LMHeadError(st, "forward")
+
+    def bwd(self):
+        lm, E, e = self.lm, self.E, self.entry
+        if e == E.ENTRY_SUPPORT_KL:
+            st = lm.lmhead_loss_bwd(self.p, e, self.H, self.W, self.idx, self.ref_logq, None, self.row_out,
+                                    None, self.grad_kl, self.dH, self.dW, self.ws, self.ws_bytes, self.sp)
+        else:
+            saved = self.row_out if e == E.ENTRY_SUPPORT else None
+            st = lm.lmhead_loss_bwd(self.p, e, self.H, self.W, self.idx, self.ref_logq, self.lse, saved,
+                                    self.grad, self.grad_kl, self.dH, self.dW, self.ws, self.ws_bytes, self.sp)
+        if st:
+            raise lm.LMHeadError(st, "backward")
+
+    def digest(self):
+        self.torch.cuda.synchronize()
+        h = hashlib.sha256()
+        for t in (self.loss, self.lse, self.row_out, self.kl, self.dH, self.dW):
+            h.update(t.view(self.torch.uint8).cpu().numpy().tobytes())
+        return h.hexdigest()
+
+
+def time_steps(torch, run, steps, warmup):
+    """`warmup` untimed steps, then `steps` timed ones (HIP events on the calls'
+    stream, wall clock between device synchronisations); then one more step
+    must reproduce the last timed step's outputs bit for bit."""
+    for _ in range(warmup):
+        run.fwd()
+        run.bwd()
+    torch.cuda.synchronize()
+    log(f"{warmup} warmup steps done")
+    stream = run.stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        run.fwd()
+        ev[i][1].record(stream)
+        run.bwd()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    fwd_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    bwd_ms = [b.elapsed_time(c) for _, b, c in ev]
+    step_ms = [a.elapsed_time(c) for a, _, c in ev]
+    ms_per_step = wall * 1e3 / steps
+    log(f"timed {steps} steps: wall {ms_per_step:.3f} ms/step; events fwd {np.mean(fwd_ms):.3f} "
+        f"bwd {np.mean(bwd_ms):.3f} step {np.mean(step_ms):.3f} ms")
+    d1 = run.digest()
+    run.fwd()
+    run.bwd()
+    d2 = run.digest()
+    log(f"bitwise repeat: {d1 == d2} ({d1[:16]})")
+    return {"wall_s": wall, "ms_per_step": ms_per_step, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+            "step_ms": step_ms, "deterministic": d1 == d2}
+
+
+def other_workloads(torch, lm, workloads, dev, steps):
+    """The other workloads of the path, timed the same way with a few steps
+    each (inputs drawn by the same seeded recipe): the per-token log-prob
+    entry, the dense support entry (log-probs + KL over K = 64 candidates) and
+    the KL-only support entry on the same inputs."""
+    E = workloads
+    res = {}
+    support_inp = None
+    for key, name, entry in (("logprob", "logprob", E.ENTRY_LOGPROB),
+                             ("support", "support", E.ENTRY_SUPPORT),
+                             ("support_kl_only", "support", E.ENTRY_SUPPORT_KL)):
+        wl = E.WORKLOADS[name]
+        t0 = time.time()
+        if name == "support" and support_inp is not None:
+            inp = support_inp
+        else:
+            inp = E.make_inputs(wl)
+            log(f"inputs for {name} drawn in {time.time() - t0:.1f}s")
+        if name == "support":
+            support_inp = inp
+        run = Runner(torch, lm, workloads, wl, inp, entry, dev)
+        t = time_steps(torch, run, steps, 2)
+        ms = t["ms_per_step"]
+        rec = {
+            "workload": f"{name}: N={wl.n}, Hd={wl.hidden}, V={wl.vocab}, chunk {wl.chunk}"
+                        + (f", K={wl.k}" if run.k > 1 else "") + f", entry "
+                        + {E.ENTRY_LOGPROB: "logprob", E.ENTRY_SUPPORT: "support (lp + KL)",
+                           E.ENTRY_SUPPORT_KL: "support_kl (KL only)"}[entry]
+                        + ", forward + backward (dH, dW)",
+            "tokens_per_s": round(wl.n * steps / t["wall_s"], 1),
+            "ms_per_step": round(ms, 4),
+            "fwd_ms": round(float(np.mean(t["fwd_ms"])), 4),
+            "bwd_ms": round(float(np.mean(t["bwd_ms"])), 4),
+            "steps": steps,
+            "deterministic_repeat": t["deterministic"],
+        }
+        if entry != E.ENTRY_SUPPORT_KL:
+            tf = wl.flops_fwd_bwd / (ms * 1e-3) / 1e12
+            rec["tflops_8nvh"] = round(tf, 2)
+            rec["pct_bf16_peak"] = round(100 * tf / BF16_PEAK_TFLOPS, 2)
+        res[key] = rec
+        del run
+        torch.cuda.empty_cache()
+    return res
 
 
 def vendor_gemm(torch, H, W, wl, stream, reps=5):
@@ -341,6 +420,34 @@ def vendor_gemm(torch, H, W, wl, stream, reps=5):
     return rec
 
 
+def host_cpus():
+    """The host cores this process may run on: its CPU affinity set, bounded by
+    a cgroup CPU quota if one is set; and the CPU model."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count() or 1
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, period = f.read().split()[:2]
+        if q != "max":
+            quota = int(q) / int(period)
+    except (OSError, ValueError):
+        pass
+    threads = avail if quota is None else max(1, min(avail, int(quota)))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"threads": threads, "available": avail, "quota": quota, "model": model}
+
+
 def cpu_baseline(wl, inp, target_s, entry=None):
     """The fp64 oracle, as it stands, on a bounded sample of rows of the same
     workload: for each sampled row the full forward (logits over the whole
@@ -349,7 +456,8 @@ def cpu_baseline(wl, inp, target_s, entry=None):
     import oracle
 
     entry = wl.entry if entry is None else entry
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
+    host = host_cpus()
+    threads = host["threads"]
     rng = np.random.default_rng(wl.seed + 77)
 
     def one(rows):
@@ -379,7 +487,7 @@ def cpu_baseline(wl, inp, target_s, entry=None):
     probe_rows = rng.choice(wl.n, size=4, replace=False)
     t_probe = one(probe_rows)
     per_row = t_probe / 4
-    n_rows = int(max(4, min(256, target_s / max(per_row, 1e-6))))
+    n_rows = int(max(4, min(1024, target_s / max(per_row, 1e-6))))
     n_rows = (n_rows // 4) * 4
     rows = rng.choice(wl.n, size=n_rows, replace=False)
     log(f"cpu baseline: probe {t_probe:.2f}s for 4 rows; timing {n_rows} rows on {threads} threads")
@@ -388,6 +496,9 @@ def cpu_baseline(wl, inp, target_s, entry=None):
         "value": round(n_rows / dt, 4),
         "unit": "tokens/s",
         "cores": threads,
+        "cores_available": host["available"],
+        "cgroup_cpu_quota": host["quota"],
+        "cpu_model": host["model"],
         "kind": "oracle",
         "sample": f"{n_rows} rows of the {wl.name} workload (fp64 C oracle, entry {entry}: logits "
                   f"over all {wl.vocab} ids, the entry's outputs, dL/dz, the rows' dH and their dW "
