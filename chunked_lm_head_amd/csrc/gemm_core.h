@@ -376,91 +376,206 @@ __device__ __forceinline__ void gemm_mainloop(const Operand& A, int64_t m0, cons
 }
 
 // ------------------------------------------------------------------------
-// The direct-A K loop (logits contractions: A = H, B = W or a chunk of it,
-// both contraction-contiguous). A is read from a copy of H in MFMA fragment
-// order and goes from memory straight into the fragment registers; only B is
-// staged in LDS, and it gets there without registers, by buffer loads that
-// write LDS directly. Against the staged core above this halves the LDS
-// traffic per K step (B only: 32 KB written and 64 KB read per workgroup
-// instead of 64 and 128) and drops every LDS store instruction from the loop.
+// The direct-A K loop. A goes from memory straight into the MFMA fragment
+// registers; only B is staged in LDS, and it gets there without registers,
+// by buffer loads that write LDS directly. Against the staged core above this
+// halves the LDS traffic per K step (B only: 32 KB written and 64 KB read per
+// workgroup instead of 64 and 128) and drops every LDS store instruction
+// from the loop.
 //
-// Fragment order: 16-row x 32-k blocks of 1 KB, block (m / 16, k / 32) at
-// ((m / 16) * (K / 32) + k / 32) * 1 KB, lane l's 16 bytes (row l % 16, k
-// 8 (l / 16) .. + 8: exactly the lane's A operand of one
-// v_mfma_f32_16x16x32_bf16) at byte 16 l of the block. One fragment load is
-// one fully used 1 KB block (eight 128-byte lines); reading the same
-// fragments from the row-major H touches 16 rows per 16 lanes and ran at
-// 0.40 MFMA busy, limited by the vector cache's line rate. Rows past n are
-// stored as zeros, so a tile never reads past its operand.
-//
+// A is read from a copy in MFMA fragment order: 16-row x 32-k blocks of
+// 1 KB, lane l's 16 bytes (row l % 16, k 8 (l / 16) .. + 8: exactly the
+// lane's A operand of one v_mfma_f32_16x16x32_bf16) in one 16-byte slot of
+// the block. One fragment load is one fully used 1 KB block (eight 128-byte
+// lines); reading the same fragments from a row-major operand touches 16
+// rows per 16 lanes and ran at 0.40 MFMA busy, limited by the vector cache's
+// line rate. Block orders (rows past the operand are stored as zeros):
+//   kATile: block (m / 16, k / 32) at ((m / 16) (K / 32) + k / 32) KB, one
+//           descriptor per tile (256 rows x K x 2 bytes < 2^31 by the shape
+//           limits). With `perm`, lane l sits in slot pslot(l) (dL/dz, so
+//           that the dW contraction's transposing reads of the same blocks
+//           are conflict-free).
+//   kAStep: block (k / 32, m / 16) at ((k / 32) (M / 16) + m / 16) KB, one
+//           descriptor per K step, so any K fits 32-bit offsets (H^T in dW,
+//           where K is the row count).
 // Register ring: fragments of K steps kt and kt + 1 (2 x 2 substeps x 8
-// blocks x 4 registers = 128 VGPRs); the fragment of step kt is reloaded with
-// step kt + 2's right after its last MFMA, so each load has two K steps to
-// land. LDS ring: four B stages of 32 KB (K-major tile rows of 128 bytes,
-// 16-byte chunk q of row r at q ^ ((r >> 1) & 7), the layout of the staged
-// core); during step kt each wave issues eight 1 KB loads of step kt + 3 into
-// the stage step kt - 1 released. The stage barrier (mid-step, between the
-// passes of the second substep) waits only for this wave's loads of step
-// kt + 1: 48 loads were issued after them (the rest of step kt - 2, all of
-// step kt - 1 and step kt up to the barrier, 24 per step), so vmcnt(48)
-// leaves the later ones in flight; the compiler's own barrier fence would
-// wait for every load, since it counts the LDS-writing loads as LDS stores.
-constexpr int kDaStage = kTile * kTileK * 2;   // one K-major B tile: 32 KB
+// blocks x 4 registers = 128 VGPRs); the fragment of step kt is reloaded
+// with step kt + 2's right after its last MFMA, so each load has two K steps
+// to land.
+//
+// B stage layouts (one K step: 64 k x 256 mn), four stages in a ring; during
+// step kt each wave issues eight 1 KB loads of step kt + 3 into the stage
+// step kt - 1 released:
+//   kBK:    K-major [mn][k] operand (W, a chunk of W): 256 rows of 128 bytes,
+//           16-byte chunk q of row r at q ^ ((r >> 1) & 7) (the staged
+//           core's layout); 32 KB.
+//   kBRow:  MN-major row-major [k][mn] operand (a chunk of W in dH): blocks
+//           of two 512-byte k rows, block b = 8 (r / 16) + (r % 4) + 4 ((r / 8)
+//           % 2) holding rows r (first half) and r + 4 (second half) for
+//           r % 8 < 4, at b x 1056 bytes; 33 KB. A 32-lane transposing read
+//           takes k rows {0..3, 8..11} (or {4..7, 12..15}) + 16 q: eight
+//           distinct blocks, 32 bytes apart modulo 256, so its 32-byte pieces
+//           fill the 64 banks once; every fragment address is one per-lane
+//           base plus immediates.
+//   kBFrag: MN-major operand stored as fragment blocks (dL/dz as B of dW:
+//           mn = chunk column, k = row): the step's 4 x 8 blocks copied
+//           verbatim (slot 8 (k / 16) + mn / 32, 32 KB); pslot makes the
+//           transposing reads of a block conflict-free.
+//
+// The stage barrier (mid-step, between the passes of the second substep)
+// waits only for this wave's loads of step kt + 1: 48 loads were issued
+// after them (the rest of step kt - 2, all of step kt - 1 and step kt up to
+// the barrier, 24 per step), so vmcnt(48) leaves the later ones in flight;
+// the compiler's own barrier fence would wait for every load, since it
+// counts the LDS-writing loads as LDS stores.
+constexpr int kATile = 0, kAStep = 1;
+constexpr int kBK = 0, kBRow = 1, kBFrag = 2;
 constexpr int kDaStages = 4;
-static_assert(kDaStages * kDaStage <= kLdsBytes, "B ring must fit the LDS");
+constexpr int kRowBlock = 1024 + 32;   // kBRow: two k rows plus the 32-byte bank shift
+constexpr int kDaStageMax = 32 * kRowBlock;
+static_assert(kDaStages * kDaStageMax <= kLdsBytes, "B ring must fit the LDS");
+
+__host__ __device__ constexpr int da_stage_bytes(int bl) { return bl == kBRow ? 32 * kRowBlock : 32 * 1024; }
+
+// Fragment-order slot of lane l in a dL/dz block: bit 2 flipped when bit 4
+// is set (an involution). A dW transposing read takes rows {0..3, 8..11}
+// (+ 4) of a block at two consecutive 8-column groups g, g + 1 (lanes
+// n + 16 g); flipping bit 2 for odd g puts those 16 lanes' slots in 16
+// distinct positions modulo 256 bytes.
+__host__ __device__ constexpr int pslot(int l) { return l ^ (((l >> 4) & 1) << 2); }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+struct DaA {
+    const char* base;   // kATile: the tile's first block; kAStep: the tile's first block of K step 0
+    int64_t kblk;       // kATile: bytes per 16-row block (K / 32 KB); kAStep: bytes per K block (M / 16 KB)
+    int64_t koff;       // kATile: byte offset of the first K block (K slices)
+    int perm;           // kATile: lanes in pslot order
+};
+
+struct DaB {
+    const char* base;   // kBK: the tile's first row; kBRow: k row 0; kBFrag: block (0, tile's first mn block)
+    int64_t ld;         // kBK / kBRow: elements per row; kBFrag: bytes per 16-row block row (mn extent / 32 KB)
+    int64_t rows;       // kBK: mn rows in the tile (rest read zero); kBRow: k rows that exist
+    int64_t n0;         // kBRow: the tile's first mn column
+};
+
 struct DaCtx {
-    __amdgpu_buffer_rsrc_t ra;   // A: the tile's 256 rows of the fragment-order copy
-    uint32_t va;                 // lane offset in A: the wave's row half, lane's 16 bytes
-    uint32_t kblk;               // bytes per 16-row block of A (K / 32 KB)
-    __amdgpu_buffer_rsrc_t rb;   // B: the tile's rows, range ending at the operand's last row
-    uint32_t vb[2];              // lane offset in B for even / odd chunk u (swizzle parity)
-    uint32_t brow8;              // bytes per 8 rows of B
+    DaA A;
+    DaB B;
+    __amdgpu_buffer_rsrc_t ra;    // kATile only
+    uint32_t va;                  // lane offset in A
+    __amdgpu_buffer_rsrc_t rb;    // kBK only
+    uint32_t vb[2];               // lane offsets in B (kBK: even / odd chunk u)
     int64_t KT;
     char* smem;
     int wave, lane;
 };
 
-// Fragment (substep s, block i) of K step kt (clamped to the last step).
-__device__ __forceinline__ bf16x8 da_a(const DaCtx& c, int64_t kt, int s, int i) {
+template <int AM>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t da_a_rsrc(const DaCtx& c, int64_t kt) {
+    if (AM == kATile) return c.ra;
     const int64_t ktc = kt < c.KT ? kt : c.KT - 1;
-    const uint32_t soff = (uint32_t)i * c.kblk + (uint32_t)(ktc * 2048 + s * 1024);
-    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(c.ra, c.va, soff, 0));
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(c.A.base + 2 * ktc * c.A.kblk), 0, (int)(2 * c.A.kblk),
+                                             0x00020000);
 }
 
-// Load u (0..7) of a wave for B step kt into stage ST: LDS rows
-// 64 w + 8 u .. + 8 of the stage, 1 KB written in lane order; lane p loads
-// the global chunk that belongs at its position ((p % 8) ^ swizzle of its row).
-template <int ST>
+// Fragment (substep s, block i) of K step kt (clamped to the last step).
+template <int AM>
+__device__ __forceinline__ bf16x8 da_a(const DaCtx& c, __amdgpu_buffer_rsrc_t r, int64_t kt, int s, int i) {
+    const int64_t ktc = kt < c.KT ? kt : c.KT - 1;
+    const uint32_t soff = AM == kATile ? (uint32_t)(i * c.A.kblk + c.A.koff + ktc * 2048 + s * 1024)
+                                       : (uint32_t)(s * c.A.kblk + i * 1024);
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, c.va, soff, 0));
+}
+
+// One LDS-writing buffer load issued from assembly: each lane's 16 bytes at
+// rsrc + voff + soff go to LDS at m0 + 16 lane. The MN-major layouts load B
+// this way: with the compiler's LDS-writing builtin the compiler cannot tell
+// the transposing LDS reads (an intrinsic) from the loads in flight and
+// drains every load before each read. The instruction has no register
+// output; its completion is covered by the explicit vmcnt waits at the stage
+// barrier and before the epilogue, which count every load in issue order.
+// The descriptor is built by hand: base address, the range in bytes, and the
+// same format word as __builtin_amdgcn_make_buffer_rsrc(..., 0x00020000).
+__device__ __forceinline__ u32x4_t rsrc_words(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    u32x4_t r;
+    r[0] = (uint32_t)a;
+    r[1] = (uint32_t)(a >> 32) & 0xffffu;
+    r[2] = bytes;
+    r[3] = 0x00020000u;
+    return r;
+}
+__device__ __forceinline__ void dma16(const u32x4_t& rsrc, uint32_t voff, uint32_t soff, const char* lds) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)lds);
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(soff), "s"(m0)
+                 : "memory", "m0");
+}
+
+// B load u (0..7) of a wave for K step kt into stage ST.
+template <int BL, int ST>
 __device__ __forceinline__ void da_b(const DaCtx& c, int64_t kt, int u) {
     const int64_t ktc = kt < c.KT ? kt : c.KT - 1;
-    char* dst = c.smem + ST * kDaStage + (c.wave * 64 + u * 8) * 128;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rb, (lds_void_t*)dst, 16, c.vb[u & 1],
-                                             (uint32_t)u * c.brow8 + (uint32_t)(ktc * 128), 0, 0);
+    char* stage = c.smem + ST * da_stage_bytes(BL);
+    if (BL == kBK) {
+        // LDS rows 64 w + 8 u .. + 8 in lane order; lane p loads the chunk that
+        // belongs at its position
+        char* dst = stage + (c.wave * 64 + u * 8) * 128;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rb, (lds_void_t*)dst, 16, c.vb[u & 1],
+                                                 (uint32_t)(u * 8 * c.B.ld * 2 + ktc * 128), 0, 0);
+    } else if (BL == kBRow) {
+        // block 8 w + u: k rows r1 = 16 w + u % 4 + 8 (u / 4) (lanes 0-31) and
+        // r1 + 4 (lanes 32-63), 512 bytes each from the tile's first column;
+        // k rows past the operand read as zero
+        const int64_t k0 = ktc * kTileK;
+        int64_t left = c.B.rows - k0;
+        left = left < 0 ? 0 : (left > kTileK ? kTileK : left);
+        const u32x4_t r = rsrc_words(c.B.base + k0 * c.B.ld * 2, (uint32_t)(left * c.B.ld * 2));
+        const int r1 = c.wave * 16 + (u & 3) + 8 * (u >> 2);
+        dma16(r, c.vb[0], (uint32_t)(r1 * c.B.ld * 2), stage + (c.wave * 8 + u) * kRowBlock);
+    } else {
+        // block (4 kt + w, u) of the tile's columns, 1 KB verbatim
+        const u32x4_t r = rsrc_words(c.B.base + 4 * ktc * c.B.ld, (uint32_t)(4 * c.B.ld));
+        dma16(r, c.vb[0], (uint32_t)(c.wave * c.B.ld + u * 1024), stage + (c.wave * 8 + u) * 1024);
+    }
 }
 
-// K step kt, reading B stage ST = kt % 4; same MFMA order and fragment reads
-// as pg_step. B loads of step kt + 3 go out every 12 MFMAs from the first.
-template <int ST>
+// B fragment (block j: mn br + 16 j .. + 16, substep s) from a stage.
+template <int BL>
+__device__ __forceinline__ bf16x8 da_bfrag(const char* stage, const DaCtx& c, uint32_t lo, uint32_t hi, int br,
+                                           int j, int s) {
+    if (BL == kBK) return frag16(stage, br + 16 * j, s, c.lane);
+    const int imm = BL == kBRow ? s * 16 * kRowBlock + 32 * j : s * 16384 + (j >> 1) * 1024 + (j & 1) * 512;
+    const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + lo + imm));
+    const i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + hi + imm));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// K step kt, reading B stage ST = kt % 4; same MFMA order as pg_step. B loads
+// of step kt + 3 go out every 12 MFMAs from the first.
+template <int AM, int BL, int ST>
 __device__ __forceinline__ void da_step(const DaCtx& c, int64_t kt, AccTile& acc, bf16x8 (&fa)[2][2][8],
-                                        bf16x8 (&fb)[8]) {
+                                        bf16x8 (&fb)[8], uint32_t blo, uint32_t bhi) {
     constexpr int P = ST & 1;
-    const char* cur = c.smem + ST * kDaStage;
-    const char* nxt = c.smem + ((ST + 1) & 3) * kDaStage;
+    constexpr int SB = da_stage_bytes(BL);
+    const char* cur = c.smem + ST * SB;
+    const char* nxt = c.smem + ((ST + 1) & 3) * SB;
     const int br = (c.wave & 1) * 128;
+    const __amdgpu_buffer_rsrc_t ra2 = da_a_rsrc<AM>(c, kt + 2);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
         for (int t = 0; t < 32; ++t) {
             const int bi = t >> 2, bj = t & 3;
             mma16(acc[bi][bj], fa[P][s][bi], fb[bj]);
-            if ((t & 1) && t < 8) fb[4 + (t >> 1)] = frag16(cur, br + 16 * (4 + (t >> 1)), s, c.lane);
+            if ((t & 1) && t < 8) fb[4 + (t >> 1)] = da_bfrag<BL>(cur, c, blo, bhi, br, 4 + (t >> 1), s);
             const int pos = s * 64 + t;
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                if (u * 12 == pos) da_b<(ST + 3) & 3>(c, kt + 3, u);
+                if (u * 12 == pos) da_b<BL, (ST + 3) & 3>(c, kt + 3, u);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (s == 1) {
@@ -473,43 +588,69 @@ __device__ __forceinline__ void da_step(const DaCtx& c, int64_t kt, AccTile& acc
         for (int t = 0; t < 32; ++t) {
             const int bi = t >> 2, bj = 4 + (t & 3);
             mma16(acc[bi][bj], fa[P][s][bi], fb[bj]);
-            if ((t & 3) == 3) fa[P][s][bi] = da_a(c, kt + 2, s, bi);
-            if ((t & 1) && t < 8) fb[t >> 1] = frag16(src, br + 16 * (t >> 1), s2, c.lane);
+            if ((t & 3) == 3) fa[P][s][bi] = da_a<AM>(c, ra2, kt + 2, s, bi);
+            if ((t & 1) && t < 8) fb[t >> 1] = da_bfrag<BL>(src, c, blo, bhi, br, t >> 1, s2);
             const int pos = s * 64 + 32 + t;
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                if (u * 12 == pos) da_b<(ST + 3) & 3>(c, kt + 3, u);
+                if (u * 12 == pos) da_b<BL, (ST + 3) & 3>(c, kt + 3, u);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
 
-// C[m0.., n0..] = sum_k A(m, k) B(n, k) for one 256 x 256 tile. Af: the
-// fragment-order copy of A (row count a multiple of 256, rows past the
-// operand zero); B K-major (rows at or past B.rows read as zero). K: a
-// multiple of 64. Every accumulator gets the same products in the same MFMA
-// slots as gemm_mainloop<false, false>, so the two give identical bits.
-__device__ __forceinline__ void gemm_mainloop_da(const bf16_bits* Af, int64_t m0, const Operand& B, int64_t n0,
-                                                 int64_t K, char* smem, AccTile& acc) {
+// acc = sum over K of A(m, k) B(n, k) for one 256 x 256 tile: A in fragment
+// order (AM), B in layout BL (see above). K: a multiple of 64. For AM =
+// kATile and BL = kBK every accumulator gets the same products in the same
+// MFMA slots as gemm_mainloop<false, false>, so the two give identical bits.
+template <int AM, int BL>
+__device__ __forceinline__ void gemm_mainloop_da(const DaA& A, const DaB& B, int64_t K, char* smem, AccTile& acc) {
     const int tid = threadIdx.x;
     DaCtx c;
+    c.A = A;
+    c.B = B;
     c.KT = K / kTileK;
     c.smem = smem;
     c.lane = tid & 63;
     c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    c.ra = __builtin_amdgcn_make_buffer_rsrc((void*)(Af + m0 * K), 0, (int)(kTile * K * 2), 0x00020000);
-    c.kblk = (uint32_t)(K / 32 * 1024);
-    c.va = (uint32_t)((c.wave >> 1) * 8 * c.kblk + c.lane * 16);
-    {
-        const int64_t rows = B.rows - n0 < kTile ? B.rows - n0 : kTile;
-        c.rb = __builtin_amdgcn_make_buffer_rsrc((void*)(B.ptr + n0 * B.ld), 0, (int)(rows * B.ld * 2),
-                                                 0x00020000);
+    const int wr = c.wave >> 1;
+    if (AM == kATile) {
+        c.ra = __builtin_amdgcn_make_buffer_rsrc((void*)A.base, 0, (int)(16 * A.kblk), 0x00020000);
+        c.va = (uint32_t)(wr * 8 * A.kblk + (A.perm ? pslot(c.lane) : c.lane) * 16);
+    } else {
+        c.ra = c.rb;   // unused
+        c.va = (uint32_t)((wr * 8 + 0) * 1024 + c.lane * 16);
+    }
+    uint32_t blo = 0, bhi = 0;
+    const int p = c.lane & 15, G = c.lane >> 4;
+    if (BL == kBK) {
+        c.rb = __builtin_amdgcn_make_buffer_rsrc((void*)B.base, 0, (int)(B.rows * B.ld * 2), 0x00020000);
         // row r + 8 u has swizzle(r) ^ 4 for odd u
         const int r = c.wave * 64 + (c.lane >> 3);
         const int q = (c.lane & 7) ^ swizzle(r);
         c.vb[0] = (uint32_t)((r * B.ld + q * 8) * 2);
         c.vb[1] = (uint32_t)((r * B.ld + (q ^ 4) * 8) * 2);
-        c.brow8 = (uint32_t)(8 * B.ld * 2);
+    } else if (BL == kBRow) {
+        c.rb = c.ra;
+        c.vb[0] = (uint32_t)(((c.lane >> 5) * 4 * B.ld + B.n0) * 2 + (c.lane & 31) * 16);
+        c.vb[1] = c.vb[0];
+        // k row 32 s + 8 G + p / 4 of the group's 16-lane half: block
+        // 8 (G / 2) + 4 (G % 2) + p / 4 (+ 16 s), first half; + 4 rows: second half
+        const int br = (c.wave & 1) * 128;
+        blo = (uint32_t)(((G >> 1) * 8 + 4 * (G & 1) + (p >> 2)) * kRowBlock + (br + 4 * (p & 3)) * 2);
+        bhi = blo + 512;
+    } else {
+        c.rb = c.ra;
+        c.vb[0] = (uint32_t)(c.lane * 16);
+        c.vb[1] = c.vb[0];
+        // rows n = 8 (G % 2) + p / 4 of k block G / 2, columns 4 (p % 4) .. + 4 of
+        // the 16-column group: lane slot pslot(n + 16 g), g = 2 (j % 2) + (p % 4) / 2
+        const int br = (c.wave & 1) * 128;
+        const int n = 8 * (G & 1) + (p >> 2), gb = (p & 3) >> 1;
+        const int slot_lo = pslot(n + 16 * gb), slot_hi = pslot(n + 4 + 16 * gb);
+        const uint32_t base = (uint32_t)((G >> 1) * 8192 + (br / 32) * 1024 + 8 * (p & 1));
+        blo = base + (uint32_t)slot_lo * 16;
+        bhi = base + (uint32_t)slot_hi * 16;
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -519,35 +660,36 @@ __device__ __forceinline__ void gemm_mainloop_da(const bf16_bits* Af, int64_t m0
             for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
     bf16x8 fa[2][2][8];
     // prologue: B steps 0, 1, 2 into stages 0, 1, 2; A steps 0 and 1 into the ring
+    const __amdgpu_buffer_rsrc_t r0 = da_a_rsrc<AM>(c, 0), r1 = da_a_rsrc<AM>(c, 1);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) da_b<0>(c, 0, u);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) fa[0][s][i] = da_a(c, 0, s, i);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) da_b<1>(c, 1, u);
+    for (int u = 0; u < 8; ++u) da_b<BL, 0>(c, 0, u);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) fa[1][s][i] = da_a(c, 1, s, i);
+        for (int i = 0; i < 8; ++i) fa[0][s][i] = da_a<AM>(c, r0, 0, s, i);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) da_b<2>(c, 2, u);
+    for (int u = 0; u < 8; ++u) da_b<BL, 1>(c, 1, u);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) fa[1][s][i] = da_a<AM>(c, r1, 1, s, i);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) da_b<BL, 2>(c, 2, u);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     bf16x8 fb[8];
     const int br = (c.wave & 1) * 128;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[j] = frag16(smem, br + 16 * j, 0, c.lane);
+    for (int j = 0; j < 4; ++j) fb[j] = da_bfrag<BL>(smem, c, blo, bhi, br, j, 0);
     int64_t kt = 0;
     for (; kt + 3 < c.KT; kt += 4) {
-        da_step<0>(c, kt, acc, fa, fb);
-        da_step<1>(c, kt + 1, acc, fa, fb);
-        da_step<2>(c, kt + 2, acc, fa, fb);
-        da_step<3>(c, kt + 3, acc, fa, fb);
+        da_step<AM, BL, 0>(c, kt, acc, fa, fb, blo, bhi);
+        da_step<AM, BL, 1>(c, kt + 1, acc, fa, fb, blo, bhi);
+        da_step<AM, BL, 2>(c, kt + 2, acc, fa, fb, blo, bhi);
+        da_step<AM, BL, 3>(c, kt + 3, acc, fa, fb, blo, bhi);
     }
-    if (kt < c.KT) da_step<0>(c, kt, acc, fa, fb);
-    if (kt + 1 < c.KT) da_step<1>(c, kt + 1, acc, fa, fb);
-    if (kt + 2 < c.KT) da_step<2>(c, kt + 2, acc, fa, fb);
+    if (kt < c.KT) da_step<AM, BL, 0>(c, kt, acc, fa, fb, blo, bhi);
+    if (kt + 1 < c.KT) da_step<AM, BL, 1>(c, kt + 1, acc, fa, fb, blo, bhi);
+    if (kt + 2 < c.KT) da_step<AM, BL, 2>(c, kt + 2, acc, fa, fb, blo, bhi);
     mma_drain();
     // every load (the clamped ones past the last step included) has landed
     // before the epilogue reuses the LDS

@@ -46,7 +46,8 @@ struct Layout {
     // forward regions (hfrag_fwd: H in MFMA fragment order, n_pad rows)
     size_t hdr, lse, part, zg, rows, hfrag_fwd;
     size_t hfrag_bwd;                 // the backward's own copy (workspace contents do not survive calls)
-    int64_t hfrag_bytes;
+    size_t htfrag;                    // backward: H^T in fragment order, [n_pad / 32][hid_pad / 16] blocks
+    int64_t hfrag_bytes, htfrag_bytes, hid_pad;
     // backward regions
     size_t coef_a, coef_c, G, dh_acc;
     size_t dh_part;   // fp32 partial dH tiles of the K-split (few row tiles only)
@@ -147,6 +148,9 @@ Layout plan(const lmhead_problem& p, int entry) {
     L.fwd_total = off;
     off = after_hdr;
     L.hfrag_bwd = take(L.hfrag_bytes);
+    L.hid_pad = round_up(L.hidden, kTile);
+    L.htfrag_bytes = 2 * L.n_pad * L.hid_pad;
+    L.htfrag = take(L.htfrag_bytes);
     L.coef_a = take(4 * L.n_pad);
     L.coef_c = take(4 * L.n * L.k);
     L.G = take(2 * L.n_pad * L.w_pad);
@@ -517,6 +521,10 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
     const bf16_bits* Hf = (const bf16_bits*)(w + L.hfrag_bwd);
     frag_pack_kernel<<<grid_1d(L.n_pad * L.hidden / 8, kThreads, 8192), kThreads, 0, s>>>(
         (const bf16_bits*)H, L.n, L.hidden, L.n_pad, (bf16_bits*)Hf);
+    const bf16_bits* HTf = (const bf16_bits*)(w + L.htfrag);
+    if (want_dw)
+        ht_pack_kernel<<<dim3((unsigned)(L.n_pad / 32), (unsigned)(L.hid_pad / kTile)), 256, 0, s>>>(
+            (const bf16_bits*)H, L.n, L.hidden, L.hid_pad, (bf16_bits*)HTf);
     const int32_t* hit_offsets = nullptr;
     const int32_t* hit_list = nullptr;
     if (entry == LMHEAD_ENTRY_SUPPORT) build_hits(L, L.hit_bwd, w, ids, s, &hit_offsets, &hit_list);
@@ -556,15 +564,16 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
         DhArgs ha{};
         if (want_dw) {
             da.G = G;
-            da.H = (const bf16_bits*)H;
+            da.HTf = HTf;
             da.n = L.n;
             da.n_pad = L.n_pad;
             da.hidden = L.hidden;
+            da.hid_pad = L.hid_pad;
             da.v0 = v0;
             da.width = width;
             da.w_pad = w_pad;
-            da.tiles_m = w_pad / kTile;
-            da.tiles_n = tiles_hidden;
+            da.tiles_m = L.hid_pad / kTile;
+            da.tiles_n = w_pad / kTile;
             da.dW = (bf16_bits*)dW;
             da.dw_acc = dW_acc;
         }
@@ -674,7 +683,7 @@ int lmhead_memory_report(const lmhead_problem* p, int entry, int with_backward,
     r.forward_bytes = L.fwd_total;
     const bool kl_only = entry == LMHEAD_ENTRY_SUPPORT_KL;
     r.partials_bytes = kl_only ? 0 : (size_t)(8 * L.tiles_v * L.n);
-    if (!kl_only) r.operand_copy_bytes = (size_t)L.hfrag_bytes;
+    if (!kl_only) r.operand_copy_bytes = (size_t)L.hfrag_bytes + (with_backward ? (size_t)L.htfrag_bytes : 0);
     if (with_backward && !kl_only) {
         r.dz_chunk_bytes = (size_t)(2 * L.n_pad * L.w_pad);
         r.dh_acc_bytes = (size_t)(4 * L.n * L.hidden);

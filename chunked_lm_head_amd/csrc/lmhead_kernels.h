@@ -107,16 +107,16 @@ struct LogitGradArgs {
 };
 
 struct DwArgs {
-    const bf16_bits* G;    // [n_pad, w_pad]
-    const bf16_bits* H;    // [n, hidden]
-    int64_t n, n_pad, hidden, v0, width, w_pad;
-    int64_t tiles_m, tiles_n;
+    const bf16_bits* G;    // dL/dz of the chunk in fragment order [n_pad / 16][w_pad / 32] (pslot lanes)
+    const bf16_bits* HTf;  // H^T in fragment order [n_pad / 32][hid_pad / 16] (ht_pack_kernel)
+    int64_t n, n_pad, hidden, hid_pad, v0, width, w_pad;
+    int64_t tiles_m, tiles_n;   // hidden tiles x chunk-column tiles
     bf16_bits* dW;         // [vocab, hidden] or null
     float* dw_acc;         // caller's fp32 [vocab, hidden] (+=) or null
 };
 
 struct DhArgs {
-    const bf16_bits* G;    // [n_pad, w_pad]
+    const bf16_bits* G;    // dL/dz of the chunk in fragment order [n_pad / 16][w_pad / 32] (pslot lanes)
     const bf16_bits* Wc;   // first row of the chunk: [width, hidden]
     int64_t n, n_pad, hidden, width, w_pad;
     int64_t tiles_m, tiles_n;
@@ -161,6 +161,7 @@ __global__ void scan_labels_kernel(const int32_t* ids, int64_t n, int k, int64_t
                                    Temperature T, int32_t* hdr);
 __global__ void fill_u32_kernel(uint32_t* p, int64_t count, uint32_t value);
 __global__ void frag_pack_kernel(const bf16_bits* H, int64_t n, int64_t hidden, int64_t n_pad, bf16_bits* Hf);
+__global__ void ht_pack_kernel(const bf16_bits* H, int64_t n, int64_t hidden, int64_t hid_pad, bf16_bits* HTf);
 __global__ void fwd_tiles_kernel(FwdTilesArgs a);
 __global__ void finalize_rows_kernel(FinalizeArgs a);
 __global__ void ce_reduce_kernel(const float* rows, int64_t n, const int32_t* hdr, int64_t num_valid,

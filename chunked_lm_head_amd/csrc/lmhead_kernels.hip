@@ -116,6 +116,67 @@ __global__ void frag_pack_kernel(const bf16_bits* H, int64_t n, int64_t hidden, 
     }
 }
 
+// Operand descriptions for the direct-A K loop (gemm_core.h).
+// A = H in fragment order, the 256-row tile at m0 (K = hidden).
+__device__ __forceinline__ DaA hf_tile(const bf16_bits* Hf, int64_t m0, int64_t hidden) {
+    DaA A;
+    A.kblk = hidden / 32 * 1024;
+    A.base = reinterpret_cast<const char*>(Hf) + (m0 / 16) * A.kblk;
+    A.koff = 0;
+    A.perm = 0;
+    return A;
+}
+
+// B = a K-major [rows][ld] operand, the 256-row tile at n0 (rows past `rows` read zero).
+__device__ __forceinline__ DaB kb_tile(const bf16_bits* X, int64_t n0, int64_t ld, int64_t rows) {
+    DaB B;
+    B.base = reinterpret_cast<const char*>(X + n0 * ld);
+    B.ld = ld;
+    B.rows = rows - n0 < kTile ? rows - n0 : kTile;
+    B.n0 = 0;
+    return B;
+}
+
+// HTf = H^T in fragment order (the A operand of the dW contraction: rows =
+// hidden columns, k = rows of H): 16 x 32 blocks in K-block-major order,
+// block (n / 32, h / 16) at ((n / 32) (hid_pad / 16) + h / 16) KB, lane l's 8
+// elements (hidden column h0 + l % 16, rows n0 + 8 (l / 16) .. + 8) at element
+// 8 l; rows past n and columns past hidden are zero. One workgroup per 32
+// rows x 256 columns: the tile goes through LDS (coalesced loads, then each
+// lane gathers its column's 8 rows).
+__global__ __launch_bounds__(256) void ht_pack_kernel(const bf16_bits* H, int64_t n, int64_t hidden, int64_t hid_pad,
+                                                      bf16_bits* HTf) {
+    __shared__ bf16_bits T[32][256 + 8];
+    const int64_t kb = blockIdx.x;        // 32-row block
+    const int64_t hg = blockIdx.y;        // 256-column group
+    const int tid = threadIdx.x;
+    {
+        const int r = tid >> 3, seg = (tid & 7) * 32;   // 32 rows x 8 segments of 32 columns
+        const int64_t row = kb * 32 + r;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t col = hg * 256 + seg + q * 8;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (row < n && col < hidden) v = *reinterpret_cast<const uint4*>(H + row * hidden + col);
+            const bf16_bits* e = reinterpret_cast<const bf16_bits*>(&v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) T[r][seg + q * 8 + i] = e[i];
+        }
+    }
+    __syncthreads();
+    const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int mb = wave * 4 + q;   // 16-column block of the group
+        const int col = mb * 16 + (lane & 15), r0 = 8 * (lane >> 4);
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = (uint32_t)T[r0 + 2 * i][col] | ((uint32_t)T[r0 + 2 * i + 1][col] << 16);
+        const int64_t blk = kb * (hid_pad / 16) + hg * 16 + mb;
+        *reinterpret_cast<uint4*>(HTf + blk * 512 + lane * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
 // ------------------------------------------------------------- forward tiles
 
 // One 256-row x 256-column logits tile: z = H W^T on MFMA, then per row the
@@ -129,7 +190,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTilesArgs a) 
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
 
     AccTile acc;
-    gemm_mainloop_da(a.Hf, m0, Operand{a.W, a.hidden, a.vocab}, n0, a.hidden, smem, acc);
+    gemm_mainloop_da<kATile, kBK>(hf_tile(a.Hf, m0, a.hidden), kb_tile(a.W, n0, a.hidden, a.vocab), a.hidden, smem,
+                                  acc);
 
     float* S = reinterpret_cast<float*>(smem);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -443,8 +505,10 @@ __global__ __launch_bounds__(256) void coeffs_support_kernel(CoeffArgs a) {
 
 // Recompute one chunk's logits tile and write dL/dz in bf16: G[n, j] = a_n
 // exp(z - lse_n) for chunk columns j < width, plus c_nk where v0 + j = id_nk;
-// zero elsewhere. G is written row-major [n_pad, w_pad]; it is the K-major
-// operand of dH and the MN-major operand of dW.
+// zero elsewhere (rows past n, columns past width). G is written in fragment
+// order, 16 x 32 blocks [n_pad / 16][w_pad / 32], lanes in pslot order: the
+// direct A operand of the dH contraction and, block by block, the LDS-staged
+// B operand of dW.
 __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
     int64_t tm, tn;
@@ -452,7 +516,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
 
     AccTile acc;
-    gemm_mainloop_da(a.Hf, m0, Operand{a.Wc, a.hidden, a.width}, n0, a.hidden, smem, acc);
+    gemm_mainloop_da<kATile, kBK>(hf_tile(a.Hf, m0, a.hidden), kb_tile(a.Wc, n0, a.hidden, a.width), a.hidden, smem,
+                                  acc);
 
     float* S = reinterpret_cast<float*>(smem);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -529,29 +594,32 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
         }
         __syncthreads();
         if (a.G != nullptr) {
-            // row-major copy, 64 columns at a time: each thread packs its row's
-            // values to bf16 in registers, the rows go back to LDS as [row][64]
-            // (16-byte chunk q of row r at q ^ ((r >> 1) & 7), over columns
-            // 0..31 of S, which are consumed), and 8 lanes then store one row's
-            // 128 contiguous bytes
-            uint16_t* Gl = reinterpret_cast<uint16_t*>(smem);
+            // dL/dz in fragment order (the direct A operand of the dH
+            // contraction, the block-copied B operand of dW): this half's 16 x 4
+            // blocks of 16 rows x 32 columns, four per wave and pass; lane l of
+            // block (nb, cb) packs row 16 nb + l % 16, columns 32 cb + 8 (l / 16)
+            // .. + 8 and stores them in slot pslot(l) of the block (each block
+            // one contiguous 1 KB store)
+            const int64_t wb = a.w_pad / 32;
+            const int64_t cblk0 = col0 / 32;
+            const int rl = lane & 15, cg = 8 * (lane >> 4);
+            bf16_bits* gdst = a.G + ((m0 / 16) * wb + cblk0) * 512 + pslot(lane) * 8;
+#pragma unroll 1
+            for (int b0 = 0; b0 < 16; b0 += 4) {
+                float v[4][8];
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                uint32_t w[32];
+                for (int q = 0; q < 4; ++q) {
+                    const int blk = (b0 + q) * 4 + wave;   // 64 blocks: nb = blk / 4, cb = blk % 4
+                    const float* src = S + (32 * (blk & 3) + cg) * kEpiStride + 16 * (blk >> 2) + rl;
 #pragma unroll
-                for (int i = 0; i < 32; ++i)
-                    w[i] = pack_bf16x2(Sr[(q * 64 + 2 * i) * kEpiStride], Sr[(q * 64 + 2 * i + 1) * kEpiStride]);
-                __syncthreads();
+                    for (int e = 0; e < 8; ++e) v[q][e] = src[e * kEpiStride];
+                }
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    *reinterpret_cast<uint4*>(Gl + tid * 64 + ((j ^ swizzle(tid)) << 3)) =
-                        make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
-                __syncthreads();
-                for (int it = 0; it < 8; ++it) {
-                    const int r = wave * 64 + it * 8 + (lane >> 3);
-                    const int ch = lane & 7;
-                    const uint4 v = *reinterpret_cast<const uint4*>(Gl + r * 64 + ((ch ^ swizzle(r)) << 3));
-                    *reinterpret_cast<uint4*>(a.G + (m0 + r) * a.w_pad + col0 + q * 64 + ch * 8) = v;
+                for (int q = 0; q < 4; ++q) {
+                    const int blk = (b0 + q) * 4 + wave;
+                    *reinterpret_cast<uint4*>(gdst + ((blk >> 2) * wb + (blk & 3)) * 512) =
+                        make_uint4(pack_bf16x2(v[q][0], v[q][1]), pack_bf16x2(v[q][2], v[q][3]),
+                                   pack_bf16x2(v[q][4], v[q][5]), pack_bf16x2(v[q][6], v[q][7]));
                 }
             }
         }
@@ -561,48 +629,57 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
 
 // dW rows of one chunk: dW[v0 + i, h] = sum_n G[n, i] H[n, h], a single
 // K-loop over every row n in ascending order; bf16 store of the fp32 sum.
-// With a caller accumulator the fp32 sum is first added to it (dw_acc +=),
-// and the bf16 output, if any, is the cast of the updated accumulator.
+// The tile is computed transposed (rows h, columns i): A = H^T from its
+// fragment-order copy, B = dL/dz blocks staged in LDS and read with the
+// transposing reads. With a caller accumulator the fp32 sum is first added
+// to it (dw_acc +=), and the bf16 output, if any, is the cast of the updated
+// accumulator.
 __device__ __forceinline__ void dw_tile(const DwArgs& a, int64_t bid, char* smem) {
     int64_t tm, tn;
     map_tile(bid, a.tiles_m, a.tiles_n, tm, tn);
-    const int64_t m0 = tm * kTile, n0 = tn * kTile;
+    const int64_t m0 = tm * kTile, n0 = tn * kTile;   // m0: hidden, n0: chunk column
+    DaA A;
+    A.kblk = a.hid_pad / 16 * 1024;
+    A.base = reinterpret_cast<const char*>(a.HTf) + (m0 / 16) * 1024;
+    A.koff = 0;
+    A.perm = 0;
+    DaB B;
+    B.ld = a.w_pad / 32 * 1024;
+    B.base = reinterpret_cast<const char*>(a.G) + (n0 / 32) * 1024;
+    B.rows = 0;
+    B.n0 = 0;
     AccTile acc;
-    // both operands MN-major: G [n_pad, w_pad] and H [n, hidden], k = n
-    gemm_mainloop<true, true>(Operand{a.G, a.w_pad, a.n_pad}, m0, Operand{a.H, a.hidden, a.n}, n0, a.n_pad,
-                              smem, acc);
+    gemm_mainloop_da<kAStep, kBFrag>(A, B, a.n_pad, smem, acc);
     float* S = reinterpret_cast<float*>(smem);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
-    // 32 lanes per dW row (4 columns each), two rows per wave and step: coalesced
+    // S = [chunk column 0..127 of the half][hidden 0..255]: 64 lanes per dW row
+    // (4 hidden columns each, one 512-byte bf16 row segment), 4 rows per pass
+    const int hq = 4 * (tid & 63);
+    const int64_t h = m0 + hq;
+    const bool hok = h < a.hidden;   // hidden is a multiple of 64: all four or none
+    const int64_t hc = hok ? h : 0;
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
-        if (wc == half) stage_half_rows(S, acc, wr, lane);
+        if (wc == half) stage_half(S, acc, wr, lane);
         __syncthreads();
-        const int c = 4 * (lane & 31);
-        const int64_t h = n0 + half * 128 + c;
-        const bool hok = h < a.hidden;
-        // 16 rows at a time; with a caller accumulator all 16 of its values
-        // are loaded (unconditionally, from in-bounds places for masked
-        // elements) before the first is used
-        const int64_t hc = hok ? h : 0;
 #pragma unroll 1
-        for (int i0 = 0; i0 < 32; i0 += 16) {
-            float4 p[16];
+        for (int i0 = 0; i0 < 32; i0 += 8) {
+            float4 p[8];
             if (a.dw_acc != nullptr) {
 #pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const int64_t v = m0 + wave * 64 + (i0 + u) * 2 + (lane >> 5);
+                for (int u = 0; u < 8; ++u) {
+                    const int64_t v = n0 + half * 128 + (i0 + u) * 4 + (tid >> 6);
                     const int64_t vc = v < a.width ? v : a.width - 1;
                     p[u] = *reinterpret_cast<const float4*>(a.dw_acc + (a.v0 + vc) * a.hidden + hc);
                 }
             }
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int r = wave * 64 + (i0 + u) * 2 + (lane >> 5);
-                const int64_t v = m0 + r;   // chunk-local vocabulary row
+            for (int u = 0; u < 8; ++u) {
+                const int cl = (i0 + u) * 4 + (tid >> 6);      // column of the half
+                const int64_t v = n0 + half * 128 + cl;        // chunk-local vocabulary row
                 if (v >= a.width || !hok) continue;
-                const float4 x = *reinterpret_cast<const float4*>(S + r * kRowStride + c);
+                const float4 x = *reinterpret_cast<const float4*>(S + cl * kEpiStride + hq);
                 const int64_t o = (a.v0 + v) * a.hidden + h;
                 if (a.dw_acc == nullptr) {
                     *reinterpret_cast<uint2*>(a.dW + o) = make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
@@ -622,6 +699,27 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int64_t bid, char* smem
     }
 }
 
+// A = dL/dz in fragment order for the dH contraction over the chunk's
+// columns [k0, k0 + ...) of the 256-row tile at m0; B = the chunk of W,
+// MN-major (k = chunk row, mn = hidden), from k row k0.
+__device__ __forceinline__ DaA g_tile(const DhArgs& a, int64_t m0, int64_t k0) {
+    DaA A;
+    A.kblk = a.w_pad / 32 * 1024;
+    A.base = reinterpret_cast<const char*>(a.G) + (m0 / 16) * A.kblk;
+    A.koff = (k0 / 32) * 1024;
+    A.perm = 1;
+    return A;
+}
+__device__ __forceinline__ DaB wc_rows(const DhArgs& a, int64_t n0, int64_t k0) {
+    DaB B;
+    const int64_t krows = a.width - k0;   // rows of W_c from k0 on (<= 0: the slice is all padding)
+    B.base = reinterpret_cast<const char*>(a.Wc + (krows > 0 ? k0 : 0) * a.hidden);
+    B.ld = a.hidden;
+    B.rows = krows > 0 ? krows : 0;
+    B.n0 = n0;
+    return B;
+}
+
 // dH contribution of one chunk: acc = sum_j G[n, j] W[v0 + j, h] over the
 // chunk's columns; the fp32 running sum over chunks (chunk order) lives in
 // dh_acc and the last chunk writes the bf16 result. A caller accumulator is
@@ -631,9 +729,7 @@ __device__ __forceinline__ void dh_tile(const DhArgs& a, int64_t bid, char* smem
     map_tile(bid, a.tiles_m, a.tiles_n, tm, tn);
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
     AccTile acc;
-    // B = the chunk of W, MN-major [width, hidden], k = chunk column
-    gemm_mainloop<false, true>(Operand{a.G, a.w_pad, a.n_pad}, m0, Operand{a.Wc, a.hidden, a.width}, n0, a.w_pad,
-                               smem, acc);
+    gemm_mainloop_da<kATile, kBRow>(g_tile(a, m0, 0), wc_rows(a, n0, 0), a.w_pad, smem, acc);
     float* S = reinterpret_cast<float*>(smem);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
@@ -723,11 +819,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_split_kernel(DhArgs a, int
     map_tile(blockIdx.x - sl * tiles, a.tiles_m, a.tiles_n, tm, tn);
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
     const int64_t ks = a.w_pad / slices, k0 = sl * ks;
-    const int64_t krows = a.width - k0;   // rows of W_c from k0 on (<= 0: the slice is all padding)
     AccTile acc;
-    gemm_mainloop<false, true>(Operand{a.G + k0, a.w_pad, a.n_pad}, m0,
-                               Operand{a.Wc + (krows > 0 ? k0 : 0) * a.hidden, a.hidden, krows > 0 ? krows : 0},
-                               n0, ks, smem, acc);
+    gemm_mainloop_da<kATile, kBRow>(g_tile(a, m0, k0), wc_rows(a, n0, k0), ks, smem, acc);
     float* S = reinterpret_cast<float*>(smem);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;

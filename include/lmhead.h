@@ -174,8 +174,9 @@ typedef struct lmhead_memory_figures {
     size_t dh_split_bytes;       /* backward, few row tiles only (else 0): fp32 partial
                                     dH of the K slices a chunk's dH contraction is cut
                                     into, joined in slice order */
-    size_t operand_copy_bytes;   /* forward and backward (not the KL-only entry): H in
-                                    MFMA fragment order, bf16 [n rounded up to 256, hidden] */
+    size_t operand_copy_bytes;   /* (not the KL-only entry) H in MFMA fragment order,
+                                    bf16 [n rounded up to 256, hidden]; the backward adds
+                                    H^T in fragment order, [n, hidden rounded up to 256] */
 } lmhead_memory_figures;
 
 /* Fills *out. Returns LMHEAD_ERR_ARG / LMHEAD_ERR_SHAPE for an invalid

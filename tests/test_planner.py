@@ -24,12 +24,14 @@ def test_report_matches_workspace_and_layout():
         assert r["dz_chunk_bytes"] == 2 * 8192 * 8192              # one chunk of G, bf16
         assert r["dh_acc_bytes"] == 4 * 8192 * 4096
         assert r["partials_bytes"] == 8 * 594 * 8192
-        assert r["operand_copy_bytes"] == 2 * 8192 * 4096          # H in fragment order
+        # H in fragment order, and in the backward H^T too
+        assert r["operand_copy_bytes"] == 2 * (2 * 8192 * 4096)
         parts = r["dz_chunk_bytes"] + r["dh_acc_bytes"] + r["operand_copy_bytes"]
         assert parts <= r["workspace_bytes"] <= parts + (1 << 20) + 4 * 8192 * (k + 2) * 2
         f = lm.memory_report(8192, 4096, 151936, 8192, entry, False, k)
         assert f["workspace_bytes"] == f["forward_bytes"] == r["forward_bytes"]
         assert f["dz_chunk_bytes"] == f["dh_acc_bytes"] == 0
+        assert f["operand_copy_bytes"] == 2 * 8192 * 4096
         assert f["partials_bytes"] + f["operand_copy_bytes"] <= f["forward_bytes"]
     # caller outputs: CE: loss + lse; backward adds bf16 dH and dW
     r = lm.memory_report(8192, 4096, 151936, 8192, 0, True, 1)
