@@ -92,6 +92,7 @@ class lmhead_memory_figures(ctypes.Structure):
         ("caller_output_bytes", ctypes.c_size_t),
         ("dh_split_bytes", ctypes.c_size_t),
         ("operand_copy_bytes", ctypes.c_size_t),
+        ("dz_group", ctypes.c_int64),
     ]
 
 

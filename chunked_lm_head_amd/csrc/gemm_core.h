@@ -174,9 +174,11 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // The stage barrier (mid-step, between the passes of the second substep)
 // waits only for this wave's loads of step kt + 1: 48 loads were issued
 // after them (the rest of step kt - 2, all of step kt - 1 and step kt up to
-// the barrier, 24 per step), so vmcnt(48) leaves the later ones in flight;
-// the compiler's own barrier fence would wait for every load, since it
-// counts the LDS-writing loads as LDS stores.
+// the barrier, 24 per step), so vmcnt(48) leaves the later ones in flight
+// (40 in steps 0 and 1, which follow the prologue); the compiler's own
+// barrier fence would wait for every load, since it counts the LDS-writing
+// loads as LDS stores. The prologue issues B steps 0, 1, 2 and A steps 0, 1
+// and waits only for step 0 (vmcnt(32)) before the first MFMA.
 constexpr int kATile = 0, kAStep = 1;
 constexpr int kBK = 0, kBRow = 1, kBFrag = 2;
 static_assert(kDaStages * kDaStageMax <= kLdsBytes, "B ring must fit the LDS");
@@ -337,7 +339,10 @@ __device__ __forceinline__ void da_step(const DaCtx& c, int64_t kt, AccTile& acc
             __builtin_amdgcn_sched_barrier(0);
         }
         if (s == 1) {
-            asm volatile("s_waitcnt vmcnt(48) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            // steps 0 and 1 follow the prologue, after whose loads of steps
+            // 1 and 2 only 40 loads were issued
+            if (kt < 2) asm volatile("s_waitcnt vmcnt(40) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(48) lgkmcnt(0)\n\ts_barrier" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
         }
         const char* src = s == 0 ? cur : nxt;
@@ -434,7 +439,9 @@ __device__ __forceinline__ void gemm_mainloop_da(const DaA& A, const DaB& B, int
         for (int i = 0; i < 8; ++i) fa[1][s][i] = da_a<AM>(c, r1, 1, s, i);
 #pragma unroll
     for (int u = 0; u < 8; ++u) da_b<BL, 2>(c, 2, u);
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    // the first MFMAs need only step 0: B step 0 of every wave (32 loads were
+    // issued after this wave's) and this wave's A step 0
+    asm volatile("s_waitcnt vmcnt(32)\n\ts_barrier" ::: "memory");
     bf16x8 fb[8];
     const int br = (c.wave & 1) * 128;
 #pragma unroll

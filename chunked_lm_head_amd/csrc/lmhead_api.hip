@@ -48,6 +48,8 @@ struct Layout {
     size_t hfrag_bwd;                 // the backward's own copy (workspace contents do not survive calls)
     size_t htfrag;                    // backward: H^T in fragment order, [n_pad / 32][hid_pad / 16] blocks
     int64_t hfrag_bytes, htfrag_bytes, hid_pad;
+    int64_t group;    // chunks per recompute launch (grad_group)
+    int64_t g_cols;   // columns of the dL/dz region (grad_cols)
     // backward regions
     size_t coef_a, coef_c, G, dh_acc;
     size_t dh_part;   // fp32 partial dH tiles of the K-split (few row tiles only)
@@ -87,6 +89,30 @@ int validate_problem(const lmhead_problem* p, int entry) {
 
 constexpr int kComputeUnits = 256;
 int dh_slices(int64_t n, int64_t n_pad, int64_t hidden, int64_t w_pad);
+
+// Chunks whose dL/dz one recompute launch writes. A chunk of few 256 x 256
+// tiles (small batches) leaves most compute units idle, so consecutive
+// chunks share a launch, up to one workgroup per compute unit, each into a
+// slot of its own; dW and dH then take the chunks one by one in order, so the
+// grouping changes no result. The slots are at most 256 tiles of bf16 dL/dz
+// (32 MiB) beyond a single chunk's.
+int64_t grad_group(int64_t n_pad, int64_t w_pad, int64_t nchunks) {
+    const int64_t tiles = (n_pad / kTile) * (w_pad / kTile);
+    const int64_t g = tiles >= kComputeUnits ? 1 : kComputeUnits / tiles;
+    return g < nchunks ? g : nchunks;
+}
+
+// Columns of the dL/dz region: one chunk, or the compute units' worth of
+// tiles (2^24 / n_pad columns) when the chunks are narrower, never more than
+// all chunks together. It holds grad_group's slots, and unlike their exact
+// sum it never shrinks as the chunk widens from 256, so the smallest
+// chunk's workspace is the floor the chunk planner tests first.
+int64_t grad_cols(int64_t n_pad, int64_t w_pad, int64_t nchunks) {
+    const int64_t all = nchunks * w_pad;
+    const int64_t units = (int64_t)kComputeUnits * kTile * kTile / n_pad;
+    const int64_t c = all < units ? all : units;
+    return c > w_pad ? c : w_pad;
+}
 
 Layout plan(const lmhead_problem& p, int entry) {
     Layout L{};
@@ -153,7 +179,9 @@ Layout plan(const lmhead_problem& p, int entry) {
     L.htfrag = take(L.htfrag_bytes);
     L.coef_a = take(4 * L.n_pad);
     L.coef_c = take(4 * L.n * L.k);
-    L.G = take(2 * L.n_pad * L.w_pad);
+    L.group = grad_group(L.n_pad, L.w_pad, cdiv(L.vocab, L.chunk));
+    L.g_cols = grad_cols(L.n_pad, L.w_pad, cdiv(L.vocab, L.chunk));
+    L.G = take(2 * L.n_pad * L.g_cols);
     L.dh_acc = take(4 * L.n * L.hidden);
     {
         // the first chunk is the widest; the last one may split further
@@ -531,39 +559,46 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
     const int64_t nchunks = cdiv(L.vocab, L.chunk);
     const int64_t tiles_rows = L.n_pad / kTile;
     const int64_t tiles_hidden = cdiv(L.hidden, kTile);
+    const int64_t g_stride = L.n_pad * L.w_pad;
     for (int64_t c = 0; c < nchunks; ++c) {
         const int64_t v0 = c * L.chunk;
         const int64_t width = (L.vocab - v0) < L.chunk ? (L.vocab - v0) : L.chunk;
         const int64_t w_pad = round_up(width, kTile);
         const bf16_bits* Wc = (const bf16_bits*)W + v0 * L.hidden;
-
-        LogitGradArgs ga;
-        ga.T = T;
-        ga.Hf = Hf;
-        ga.Wc = Wc;
-        ga.n = L.n;
-        ga.n_pad = L.n_pad;
-        ga.hidden = L.hidden;
-        ga.v0 = v0;
-        ga.width = width;
-        ga.w_pad = w_pad;
-        ga.tiles_m = tiles_rows;
-        ga.tiles_n = w_pad / kTile;
-        ga.coef_a = ca.coef_a;
-        ga.coef_c = ca.coef_c;
-        ga.ids = ids;
-        ga.k = (int)L.k;
-        ga.lse = lse;
-        ga.G = G;
-        ga.tiles_v = L.tiles_v;
-        ga.hit_offsets = hit_offsets;
-        ga.hit_list = hit_list;
-        bwd_logit_grad_kernel<<<(unsigned)(ga.tiles_m * ga.tiles_n), kThreads, 0, s>>>(ga);
+        const int64_t slot = c % L.group;
+        if (slot == 0) {
+            // dL/dz of this chunk and the next group - 1 ones, one launch
+            LogitGradArgs ga;
+            ga.T = T;
+            ga.Hf = Hf;
+            ga.W = (const bf16_bits*)W;
+            ga.n = L.n;
+            ga.n_pad = L.n_pad;
+            ga.hidden = L.hidden;
+            ga.vocab = L.vocab;
+            ga.v0 = v0;
+            ga.chunk = L.chunk;
+            ga.group = (nchunks - c) < L.group ? (nchunks - c) : L.group;
+            ga.tiles_m = tiles_rows;
+            ga.tiles_n = L.w_pad / kTile;
+            ga.coef_a = ca.coef_a;
+            ga.coef_c = ca.coef_c;
+            ga.ids = ids;
+            ga.k = (int)L.k;
+            ga.lse = lse;
+            ga.G = G;
+            ga.g_stride = g_stride;
+            ga.tiles_v = L.tiles_v;
+            ga.hit_offsets = hit_offsets;
+            ga.hit_list = hit_list;
+            bwd_logit_grad_kernel<<<(unsigned)(ga.tiles_m * ga.tiles_n * ga.group), kThreads, 0, s>>>(ga);
+        }
+        const bf16_bits* Gc = G + slot * g_stride;
 
         DwArgs da{};
         DhArgs ha{};
         if (want_dw) {
-            da.G = G;
+            da.G = Gc;
             da.HTf = HTf;
             da.n = L.n;
             da.n_pad = L.n_pad;
@@ -578,7 +613,7 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
             da.dw_acc = dW_acc;
         }
         if (want_dh) {
-            ha.G = G;
+            ha.G = Gc;
             ha.Wc = Wc;
             ha.width = width;
             ha.n = L.n;
@@ -685,7 +720,8 @@ int lmhead_memory_report(const lmhead_problem* p, int entry, int with_backward,
     r.partials_bytes = kl_only ? 0 : (size_t)(8 * L.tiles_v * L.n);
     if (!kl_only) r.operand_copy_bytes = (size_t)L.hfrag_bytes + (with_backward ? (size_t)L.htfrag_bytes : 0);
     if (with_backward && !kl_only) {
-        r.dz_chunk_bytes = (size_t)(2 * L.n_pad * L.w_pad);
+        r.dz_chunk_bytes = (size_t)(2 * L.n_pad * L.g_cols);
+        r.dz_group = L.group;
         r.dh_acc_bytes = (size_t)(4 * L.n * L.hidden);
         r.dh_split_bytes = (size_t)L.dh_part_bytes;
     }

@@ -88,18 +88,23 @@ struct CoeffArgs {
     Temperature T;
 };
 
+// One launch recomputes dL/dz for `group` consecutive chunks (several when a
+// chunk has fewer 256 x 256 tiles than the chip has compute units): chunk g
+// of the group starts at column v0 + g * chunk, spans min(chunk, vocab -
+// its first column) columns and writes its own slot G + g * g_stride.
 struct LogitGradArgs {
     const bf16_bits* Hf;   // H in MFMA fragment order (frag_pack_kernel), n_pad rows
-    const bf16_bits* Wc;   // first row of the chunk
-    int64_t n, n_pad, hidden;
-    int64_t v0, width, w_pad;
-    int64_t tiles_m, tiles_n;
+    const bf16_bits* W;    // [vocab, hidden]
+    int64_t n, n_pad, hidden, vocab;
+    int64_t v0, chunk, group;   // first column of the group, columns per chunk, chunks
+    int64_t tiles_m, tiles_n;   // row tiles, column tiles of a full chunk
     const float* coef_a;
     const float* coef_c;
     const int32_t* ids;
     int k;
     const float* lse;
-    bf16_bits* G;          // [n_pad, w_pad]
+    bf16_bits* G;          // slot g: chunk g's dL/dz, fragment order [n_pad / 16][w_pad / 32]
+    int64_t g_stride;      // elements between slots (n_pad x a full chunk's w_pad)
     Temperature T;
     int64_t tiles_v;       // vocabulary tiles of the whole vocabulary (bucket index)
     const int32_t* hit_offsets;   // k > 1: as in FwdTilesArgs

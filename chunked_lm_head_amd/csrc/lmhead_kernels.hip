@@ -503,20 +503,28 @@ __global__ __launch_bounds__(256) void coeffs_support_kernel(CoeffArgs a) {
     for (int kk = lane; kk < k; kk += 64) c[kk] *= inv_tau;
 }
 
-// Recompute one chunk's logits tile and write dL/dz in bf16: G[n, j] = a_n
-// exp(z - lse_n) for chunk columns j < width, plus c_nk where v0 + j = id_nk;
-// zero elsewhere (rows past n, columns past width). G is written in fragment
-// order, 16 x 32 blocks [n_pad / 16][w_pad / 32], lanes in pslot order: the
-// direct A operand of the dH contraction and, block by block, the LDS-staged
-// B operand of dW.
+// Recompute one logits tile of a chunk and write dL/dz in bf16: G[n, j] =
+// a_n exp(z - lse_n) for chunk columns j < width, plus c_nk where v0 + j =
+// id_nk; zero elsewhere (rows past n, columns past width). G is written in
+// fragment order, 16 x 32 blocks [n_pad / 16][w_pad / 32], lanes in pslot
+// order: the direct A operand of the dH contraction and, block by block, the
+// LDS-staged B operand of dW. The launch covers the group's chunks side by
+// side (tiles_n column tiles each); a narrower last chunk leaves its excess
+// workgroups idle.
 __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
-    int64_t tm, tn;
-    map_tile(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    int64_t tm, tg;
+    map_tile(blockIdx.x, a.tiles_m, a.tiles_n * a.group, tm, tg);
+    const int64_t g = tg / a.tiles_n, tn = tg - g * a.tiles_n;
+    const int64_t v0 = a.v0 + g * a.chunk;
+    const int64_t width = (a.vocab - v0) < a.chunk ? (a.vocab - v0) : a.chunk;
+    const int64_t w_pad = (width + kTile - 1) / kTile * kTile;
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
+    if (n0 >= w_pad) return;   // whole workgroup: past the last chunk's columns
+    const bf16_bits* Wc = a.W + v0 * a.hidden;
 
     AccTile acc;
-    gemm_mainloop_da<kATile, kBK>(hf_tile(a.Hf, m0, a.hidden), kb_tile(a.Wc, n0, a.hidden, a.width), a.hidden, smem,
+    gemm_mainloop_da<kATile, kBK>(hf_tile(a.Hf, m0, a.hidden), kb_tile(Wc, n0, a.hidden, width), a.hidden, smem,
                                   acc);
 
     float* S = reinterpret_cast<float*>(smem);
@@ -546,7 +554,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
             const floatx4 xs4 = *reinterpret_cast<const floatx4*>(K3 + 2 * kTile + r0);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const bool col_ok = cb + 16 * j < a.width;
+                const bool col_ok = cb + 16 * j < width;
                 floatx4 v = acc[i][j];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -563,18 +571,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
         if (wc == half) stage_half(S, acc, wr, lane);
         __syncthreads();
         const int64_t col0 = n0 + half * 128;   // chunk-local column
-        const int64_t rem = a.width - col0;
+        const int64_t rem = width - col0;
         const int ncol = rem <= 0 ? 0 : (rem >= 128 ? 128 : (int)rem);
         // c_nk at the row's ids in the tile, in ascending k
         if (a.k == 1) {
             int j;
-            if (row_ok && id_in_tile(a.ids + row, (uint32_t)(a.v0 + col0), ncol, j))
+            if (row_ok && id_in_tile(a.ids + row, (uint32_t)(v0 + col0), ncol, j))
                 Sr[j * kEpiStride] += a.coef_c[row];
         } else {
             // the tile's bucket lists its hits by row, column, slot: the first
             // entry of each (row, column) run adds the run's c_nk in ascending
             // slot order, so every element has one writer and a fixed order
-            const int64_t b = tm * a.tiles_v + (a.v0 >> 8) + tn;
+            const int64_t b = tm * a.tiles_v + (v0 >> 8) + tn;
             const int32_t e0 = a.hit_offsets[b], e1 = a.hit_offsets[b + 1];
             for (int32_t i = e0 + tid; i < e1; i += kThreads) {
                 const int32_t key = a.hit_list[i] >> kHitColShift;   // row << 8 | column
@@ -594,16 +602,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
         }
         __syncthreads();
         if (a.G != nullptr) {
+            bf16_bits* Gc = a.G + g * a.g_stride;
             // dL/dz in fragment order (the direct A operand of the dH
             // contraction, the block-copied B operand of dW): this half's 16 x 4
             // blocks of 16 rows x 32 columns, four per wave and pass; lane l of
             // block (nb, cb) packs row 16 nb + l % 16, columns 32 cb + 8 (l / 16)
             // .. + 8 and stores them in slot pslot(l) of the block (each block
             // one contiguous 1 KB store)
-            const int64_t wb = a.w_pad / 32;
+            const int64_t wb = w_pad / 32;
             const int64_t cblk0 = col0 / 32;
             const int rl = lane & 15, cg = 8 * (lane >> 4);
-            bf16_bits* gdst = a.G + ((m0 / 16) * wb + cblk0) * 512 + pslot(lane) * 8;
+            bf16_bits* gdst = Gc + ((m0 / 16) * wb + cblk0) * 512 + pslot(lane) * 8;
 #pragma unroll 1
             for (int b0 = 0; b0 < 16; b0 += 4) {
                 float v[4][8];

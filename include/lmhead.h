@@ -110,8 +110,11 @@ enum lmhead_device_error {
  *              exactly `vocab` columns (no padding of W).
  *   chunk      vocabulary chunk of the backward pass: a multiple of 256,
  *              >= 256. The backward materialises dL/dz for one chunk
- *              ([n x chunk] bf16) at a time; the forward's result does not
- *              depend on it. Every entry but the KL-only one also needs
+ *              ([n x chunk] bf16) at a time, or for a few consecutive
+ *              chunks when one chunk has fewer 256 x 256 tiles than the
+ *              chip's 256 compute units (at most 256 tiles together; the
+ *              gradients are the same either way); the forward's result
+ *              does not depend on it. Every entry but the KL-only one also needs
  *              round_up(min(chunk, vocab), 256) <= 4,194,048 (2^22 - 256:
  *              dL/dz is read with that row pitch, 256 rows per buffer
  *              range of at most 2^31 - 1 bytes); vocabularies above that
@@ -149,9 +152,9 @@ typedef struct lmhead_problem {
 /*
  * Bytes of device workspace an entry needs ("workspace reporting",
  * [PR8059]). Pure host function: no device is touched. `with_backward`
- * != 0 sizes the workspace for lmhead_loss_bwd (which needs more: one
- * chunk of dL/dz and the fp32 dH accumulator). Returns 0 for an invalid
- * problem or entry.
+ * != 0 sizes the workspace for lmhead_loss_bwd (which needs more: dL/dz
+ * of one chunk, or of a few at small n, and the fp32 dH accumulator).
+ * Returns 0 for an invalid problem or entry.
  */
 size_t lmhead_workspace_size(const lmhead_problem* p, int entry, int with_backward);
 
@@ -166,7 +169,8 @@ typedef struct lmhead_memory_figures {
     size_t workspace_bytes;      /* = lmhead_workspace_size(p, entry, with_backward) */
     size_t forward_bytes;        /* workspace the forward uses */
     size_t partials_bytes;       /* forward: (max, sum-exp) per 256-column tile and row */
-    size_t dz_chunk_bytes;       /* backward: one chunk of dL/dz, bf16, row-major */
+    size_t dz_chunk_bytes;       /* backward: dL/dz of the chunks one recompute launch
+                                    covers (dz_group of them), bf16 */
     size_t dh_acc_bytes;         /* backward: fp32 running sum of dH over the chunks */
     size_t caller_output_bytes;  /* buffers the caller allocates: the entry's fp32 outputs
                                     (loss / logp / lp, kl, lse), plus bf16 dH and dW
@@ -177,6 +181,8 @@ typedef struct lmhead_memory_figures {
     size_t operand_copy_bytes;   /* (not the KL-only entry) H in MFMA fragment order,
                                     bf16 [n rounded up to 256, hidden]; the backward adds
                                     H^T in fragment order, [n, hidden rounded up to 256] */
+    int64_t dz_group;            /* backward: chunks one recompute launch covers (1 unless
+                                    a chunk has fewer than 256 tiles of 256 x 256) */
 } lmhead_memory_figures;
 
 /* Fills *out. Returns LMHEAD_ERR_ARG / LMHEAD_ERR_SHAPE for an invalid

@@ -252,15 +252,20 @@ def test_mutation_gate_catches_two_percent():
 
 
 def test_planned_chunk_against_oracle():
-    """A workspace budget that forces several small chunks: the planned chunk
+    """A workspace budget that forces many small chunks: the planned chunk
     runs, fits, and matches the oracle (the result does not depend on the plan
-    beyond rounding of the bf16 dL/dz operand)."""
-    inp = _ragged(0)
+    beyond rounding of the bf16 dL/dz operand). n = 300, V = 40000 and the
+    256-chunk workspace as the budget plan chunk 1536: 27 chunks, whose
+    dL/dz is recomputed 21 at a time (two row tiles x six column tiles each),
+    the last group holding the 64-wide tail chunk."""
+    inp = _ragged(0, hidden=256, vocab=40000)
     d = Dev(inp)
     p = lm.problem(inp.wl.n, inp.wl.hidden, inp.wl.vocab, 256)
-    budget = lm.lmhead_workspace_size(p, 0, 1) + 1000   # fits 256, not 512
+    budget = lm.lmhead_workspace_size(p, 0, 1) + 1000
     chunk = lm.plan_chunk(inp.wl.n, inp.wl.hidden, inp.wl.vocab, budget)
-    assert chunk == 256
+    r = lm.memory_report(inp.wl.n, inp.wl.hidden, inp.wl.vocab, chunk, 0, True, 1)
+    assert r["workspace_bytes"] <= budget
+    assert (chunk, r["chunks"], r["dz_group"]) == (1536, 27, 21)
     H = d.H.clone().requires_grad_(True)
     W = d.W.clone().requires_grad_(True)
     loss = lm.ce_loss(H, W, d.t, memory_budget=budget)

@@ -110,3 +110,41 @@ def test_dh_split_slices_are_capped():
         r = lm.memory_report(256, 256, 151936, chunk, 0, True, 1)
         assert 0 < r["dh_split_bytes"] <= 16 * 4 * 256 * 256, (chunk, r["dh_split_bytes"])
     assert lm.memory_report(256, 256, 151936, 32768, 0, True, 1)["dh_split_bytes"] == 16 * 4 * 256 * 256
+
+
+def test_small_batch_groups_chunks_per_recompute():
+    """A chunk of fewer than 256 tiles of 256 x 256 shares its recompute launch
+    with the chunks after it, up to 256 tiles, each in a dL/dz slot of its
+    own: n = 256, chunk 8192 has 32 tiles, so 8 chunks (4 MiB of bf16 dL/dz
+    each) go together; the headline's 1024 tiles stay one per launch; the
+    group never exceeds the chunk count. The region holding the slots is
+    sized so that the smallest chunk still needs the least workspace."""
+    r = lm.memory_report(256, 4096, 151936, 8192, 0, True, 1)
+    assert r["dz_group"] == 8
+    assert r["dz_chunk_bytes"] == 8 * 2 * 256 * 8192
+    h = lm.memory_report(8192, 4096, 151936, 8192, 0, True, 1)
+    assert h["dz_group"] == 1 and h["dz_chunk_bytes"] == 2 * 8192 * 8192
+    # 3 tiles per chunk (n = 256, chunk 768): 85 chunks, 255 tiles
+    assert lm.memory_report(256, 4096, 151936, 768, 0, True, 1)["dz_group"] == 85
+    # 1000 columns: 4 chunks of 256 in all
+    t = lm.memory_report(64, 256, 1000, 256, 0, True, 1)
+    assert t["dz_group"] == 4 and t["dz_chunk_bytes"] == 4 * 2 * 256 * 256
+    # 129 .. 255 tiles: alone (no two fit in 256)
+    assert lm.memory_report(2048, 4096, 151936, 4352, 0, True, 1)["dz_group"] == 1    # 136 tiles
+    assert lm.memory_report(2048, 4096, 151936, 4096, 0, True, 1)["dz_group"] == 2    # 128 tiles
+    # the slots together stay within 256 tiles of bf16 (32 MiB) at any chunk
+    for chunk in range(256, 151936 + 256, 256 * 37):
+        g = lm.memory_report(256, 4096, 151936, chunk, 0, True, 1)
+        tiles = math.ceil(chunk / 256)
+        assert 1 <= g["dz_group"] <= g["chunks"]
+        assert g["dz_group"] == 1 or g["dz_group"] * tiles <= 256
+        slots = g["dz_group"] * 2 * 256 * 256 * tiles
+        assert slots <= g["dz_chunk_bytes"] <= max(slots, 32 << 20)
+    # the floor: the chunk-256 workspace is the smallest of any chunk; a budget
+    # of it plans a chunk, and that chunk fits
+    floor = _ws(256, n=256)
+    assert all(_ws(c, n=256) >= floor for c in range(256, 151936 + 256, 256 * 7))
+    c = lm.plan_chunk(256, 4096, 151936, floor)
+    assert c >= 256 and _ws(c, n=256) <= floor
+    with pytest.raises(lm.LMHeadError):
+        lm.plan_chunk(256, 4096, 151936, floor - 1)
