@@ -89,29 +89,37 @@ int validate_problem(const lmhead_problem* p, int entry) {
 
 constexpr int kComputeUnits = 256;
 int dh_slices(int64_t n, int64_t n_pad, int64_t hidden, int64_t w_pad);
+int64_t dh_units(int64_t n_pad, int64_t hidden);
+struct DhGroupPlan {
+    int64_t slices, batch;
+};
+DhGroupPlan dh_group_plan(int64_t n_pad, int64_t hidden, int64_t w_pad, int64_t group);
+
+// Columns of the dL/dz region: one chunk, or, when the chunks are narrower,
+// the compute units' worth of 256 x 256 tiles (2^24 / n_pad columns) but no
+// more than the whole vocabulary. It never shrinks as the chunk widens, so
+// the workspace grows with the chunk and the 256-column chunk needs least.
+int64_t grad_cols(int64_t n_pad, int64_t w_pad, int64_t vocab) {
+    const int64_t all = round_up(vocab, kTile);
+    const int64_t units = (int64_t)kComputeUnits * kTile * kTile / n_pad;
+    const int64_t c = all < units ? all : units;
+    return c > w_pad ? c : w_pad;
+}
 
 // Chunks whose dL/dz one recompute launch writes. A chunk of few 256 x 256
 // tiles (small batches) leaves most compute units idle, so consecutive
 // chunks share a launch, up to one workgroup per compute unit, each into a
-// slot of its own; dW and dH then take the chunks one by one in order, so the
-// grouping changes no result. The slots are at most 256 tiles of bf16 dL/dz
-// (32 MiB) beyond a single chunk's.
-int64_t grad_group(int64_t n_pad, int64_t w_pad, int64_t nchunks) {
+// slot of its own within the grad_cols columns; dW and dH then take the
+// group's chunks in order and sum each output element exactly as they would
+// one chunk at a time.
+int64_t grad_group(int64_t n_pad, int64_t w_pad, int64_t vocab, int64_t chunk) {
     const int64_t tiles = (n_pad / kTile) * (w_pad / kTile);
-    const int64_t g = tiles >= kComputeUnits ? 1 : kComputeUnits / tiles;
-    return g < nchunks ? g : nchunks;
-}
-
-// Columns of the dL/dz region: one chunk, or the compute units' worth of
-// tiles (2^24 / n_pad columns) when the chunks are narrower, never more than
-// all chunks together. It holds grad_group's slots, and unlike their exact
-// sum it never shrinks as the chunk widens from 256, so the smallest
-// chunk's workspace is the floor the chunk planner tests first.
-int64_t grad_cols(int64_t n_pad, int64_t w_pad, int64_t nchunks) {
-    const int64_t all = nchunks * w_pad;
-    const int64_t units = (int64_t)kComputeUnits * kTile * kTile / n_pad;
-    const int64_t c = all < units ? all : units;
-    return c > w_pad ? c : w_pad;
+    int64_t g = tiles >= kComputeUnits ? 1 : kComputeUnits / tiles;
+    const int64_t fit = grad_cols(n_pad, w_pad, vocab) / w_pad;
+    const int64_t nchunks = cdiv(vocab, chunk);
+    g = g < fit ? g : fit;
+    g = g < nchunks ? g : nchunks;
+    return g > 1 ? g : 1;
 }
 
 Layout plan(const lmhead_problem& p, int entry) {
@@ -179,17 +187,15 @@ Layout plan(const lmhead_problem& p, int entry) {
     L.htfrag = take(L.htfrag_bytes);
     L.coef_a = take(4 * L.n_pad);
     L.coef_c = take(4 * L.n * L.k);
-    L.group = grad_group(L.n_pad, L.w_pad, cdiv(L.vocab, L.chunk));
-    L.g_cols = grad_cols(L.n_pad, L.w_pad, cdiv(L.vocab, L.chunk));
+    L.group = grad_group(L.n_pad, L.w_pad, L.vocab, L.chunk);
+    L.g_cols = grad_cols(L.n_pad, L.w_pad, L.vocab);
     L.G = take(2 * L.n_pad * L.g_cols);
     L.dh_acc = take(4 * L.n * L.hidden);
     {
-        // the first chunk is the widest; the last one may split further
-        const int64_t last = L.vocab - (cdiv(L.vocab, L.chunk) - 1) * L.chunk;
-        const int s0 = dh_slices(L.n, L.n_pad, L.hidden, L.w_pad);
-        const int s1 = dh_slices(L.n, L.n_pad, L.hidden, round_up(last, kTile));
-        const int smax = s0 > s1 ? s0 : s1;
-        L.dh_part_bytes = smax > 1 ? 4 * smax * L.n * L.hidden : 0;
+        // the K-split's partials, whatever the chunk: every split (one chunk's
+        // slices, or a group's chunks x slices) takes at most dh_units planes
+        const int64_t units = L.n > 0 ? dh_units(L.n_pad, L.hidden) : 0;
+        L.dh_part_bytes = units > 1 ? 4 * units * L.n * L.hidden : 0;
         L.dh_part = take(L.dh_part_bytes);
     }
     if (buckets) take_hits(L.hit_bwd);
@@ -267,10 +273,36 @@ int dwdh_plan(int64_t n_dw, int64_t k_dw, int64_t n_dh, int64_t k_dh) {
     return together * 20 <= apart * 19 ? (dh_first ? 1 : 0) : -1;
 }
 
+// fp32 partial dH planes of the K-split (below 2: no split): one per (chunk,
+// slice) unit a launch computes, at most 16 and at most one workgroup per
+// compute unit over all of them (units x dH tiles <= 256), so the partials
+// never exceed 256 tiles of 256 x 256 fp32 (64 MiB). Depends on n and hidden
+// alone.
+int64_t dh_units(int64_t n_pad, int64_t hidden) {
+    const int64_t n_dh = (n_pad / kTile) * cdiv(hidden, kTile);
+    const int64_t u = kComputeUnits / n_dh;
+    return u < kMaxDhSlices ? u : kMaxDhSlices;
+}
+
+// The grouped dH K-split (several chunks per recompute launch): each chunk
+// of the group is cut into `slices` equal K ranges (a power of two dividing
+// a full chunk's K steps, at least 8 steps each) and `batch` chunks go to
+// one launch, so that slices x chunks fills the units (dh_units) and each
+// workgroup runs as many K steps as that allows. slices = 0: no split (one
+// dH launch per chunk). Depends on the shape and the group alone.
+DhGroupPlan dh_group_plan(int64_t n_pad, int64_t hidden, int64_t w_pad, int64_t group) {
+    const int64_t units = dh_units(n_pad, hidden);
+    if (units < 2) return {0, 0};
+    const int64_t kt = w_pad / kTileK;
+    int64_t sl = 1;
+    while (2 * sl * group <= units && kt % (2 * sl) == 0 && kt / (2 * sl) >= 8) sl *= 2;
+    return {sl, units / sl};
+}
+
 // K slices of a chunk's dH contraction (1: no split). With few dH tiles
 // (small batches) each one runs all of the chunk's K steps while most compute
 // units idle; cutting the chunk's columns into S equal slices (S a power of
-// two dividing the K steps, at least 8 steps each, S <= 16) gives S times the tiles,
+// two dividing the K steps, at least 8 steps each, S <= dh_units) gives S times the tiles,
 // whose fp32 partials dh_join_kernel adds in slice order. Chosen from the
 // same estimate as dwdh_plan, plus two steps per tile for the prologue and
 // the partial's store and the join's HBM traffic at 8 MB per step (one K step
@@ -278,7 +310,8 @@ int dwdh_plan(int64_t n_dw, int64_t k_dw, int64_t n_dh, int64_t k_dh) {
 // on the shape alone (dW wanted or not), so one shape always sums in one order.
 int dh_slices(int64_t n, int64_t n_pad, int64_t hidden, int64_t w_pad) {
     const int64_t n_dh = (n_pad / kTile) * cdiv(hidden, kTile);
-    if (n <= 0 || 2 * n_dh > kComputeUnits) return 1;
+    const int64_t units = dh_units(n_pad, hidden);
+    if (n <= 0 || units < 2) return 1;
     const int64_t n_dw = (w_pad / kTile) * cdiv(hidden, kTile), k_dw = n_pad / kTileK;
     const int64_t kt = w_pad / kTileK;
     const int one = dwdh_plan(n_dw, k_dw, n_dh, kt);
@@ -286,7 +319,7 @@ int dh_slices(int64_t n, int64_t n_pad, int64_t hidden, int64_t w_pad) {
                                  : (one == 1 ? list_time(n_dh, kt, n_dw, k_dw) : list_time(n_dw, k_dw, n_dh, kt));
     int best = 1;
     int64_t best_t = base;
-    for (int64_t sl = 2; sl <= kMaxDhSlices && kt % sl == 0 && kt / sl >= 8; sl *= 2) {
+    for (int64_t sl = 2; sl <= units && kt % sl == 0 && kt / sl >= 8; sl *= 2) {
         const int64_t join = cdiv((sl + 2) * n * hidden * 4, (int64_t)8 << 20);
         const int64_t t = rounds_time(n_dw, k_dw) + rounds_time(n_dh * sl, kt / sl + 2) + join;
         if (t * 20 <= base * 19 && t < best_t) {
@@ -560,14 +593,69 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
     const int64_t tiles_rows = L.n_pad / kTile;
     const int64_t tiles_hidden = cdiv(L.hidden, kTile);
     const int64_t g_stride = L.n_pad * L.w_pad;
-    for (int64_t c = 0; c < nchunks; ++c) {
+    const float* part_in = (const float*)(w + L.dh_part);
+    float* part = (float*)(w + L.dh_part);
+    float* dh_sum = dH_acc != nullptr ? dH_acc : (float*)(w + L.dh_acc);
+    // argument blocks of chunk c (dW: `group` chunks from c on; slot: its dL/dz)
+    auto dw_args = [&](int64_t c, int64_t group, const bf16_bits* slot) {
         const int64_t v0 = c * L.chunk;
         const int64_t width = (L.vocab - v0) < L.chunk ? (L.vocab - v0) : L.chunk;
-        const int64_t w_pad = round_up(width, kTile);
-        const bf16_bits* Wc = (const bf16_bits*)W + v0 * L.hidden;
-        const int64_t slot = c % L.group;
-        if (slot == 0) {
-            // dL/dz of this chunk and the next group - 1 ones, one launch
+        DwArgs da{};
+        da.G = slot;
+        da.HTf = HTf;
+        da.n = L.n;
+        da.n_pad = L.n_pad;
+        da.hidden = L.hidden;
+        da.hid_pad = L.hid_pad;
+        da.vocab = L.vocab;
+        da.v0 = v0;
+        da.chunk = L.chunk;
+        da.group = group;
+        da.g_stride = g_stride;
+        da.tiles_m = L.hid_pad / kTile;
+        da.tiles_n = round_up(width, kTile) / kTile;
+        da.dW = (bf16_bits*)dW;
+        da.dw_acc = dW_acc;
+        return da;
+    };
+    // dH of chunks c .. last: the running sum starts at c and ends at last
+    auto dh_args = [&](int64_t c, int64_t last, const bf16_bits* slot) {
+        const int64_t v0 = c * L.chunk;
+        DhArgs ha{};
+        ha.G = slot;
+        ha.Wc = (const bf16_bits*)W + v0 * L.hidden;
+        ha.width = (L.vocab - v0) < L.chunk ? (L.vocab - v0) : L.chunk;
+        ha.n = L.n;
+        ha.n_pad = L.n_pad;
+        ha.hidden = L.hidden;
+        ha.w_pad = round_up(ha.width, kTile);
+        ha.tiles_m = tiles_rows;
+        ha.tiles_n = tiles_hidden;
+        ha.first = c == 0 && dH_acc == nullptr;
+        ha.last = last == nchunks - 1;
+        ha.keep_acc = dH_acc != nullptr;
+        ha.dh_acc = dh_sum;
+        ha.dH = (bf16_bits*)dH;
+        return ha;
+    };
+    auto split_of = [&](int64_t c, int64_t chunks, int64_t slices, int64_t w_pad) {
+        DhSplit q;
+        q.W = (const bf16_bits*)W;
+        q.v0 = c * L.chunk;
+        q.chunk = L.chunk;
+        q.vocab = L.vocab;
+        q.chunks = chunks;
+        q.slices = slices;
+        q.ks = w_pad / slices;
+        q.g_stride = g_stride;
+        return q;
+    };
+    const unsigned join_grid = grid_1d(L.n * L.hidden / 4, kThreads, 4096);
+    const int64_t n_dh = want_dh ? tiles_rows * tiles_hidden : 0;
+    for (int64_t c = 0; c < nchunks; c += L.group) {
+        const int64_t ng = (nchunks - c) < L.group ? (nchunks - c) : L.group;
+        {
+            // dL/dz of chunks c .. c + ng - 1, one launch
             LogitGradArgs ga;
             ga.T = T;
             ga.Hf = Hf;
@@ -576,11 +664,11 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
             ga.n_pad = L.n_pad;
             ga.hidden = L.hidden;
             ga.vocab = L.vocab;
-            ga.v0 = v0;
+            ga.v0 = c * L.chunk;
             ga.chunk = L.chunk;
-            ga.group = (nchunks - c) < L.group ? (nchunks - c) : L.group;
+            ga.group = ng;
             ga.tiles_m = tiles_rows;
-            ga.tiles_n = L.w_pad / kTile;
+            ga.tiles_n = round_up((L.vocab - ga.v0) < L.chunk ? (L.vocab - ga.v0) : L.chunk, kTile) / kTile;
             ga.coef_a = ca.coef_a;
             ga.coef_c = ca.coef_c;
             ga.ids = ids;
@@ -593,49 +681,42 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
             ga.hit_list = hit_list;
             bwd_logit_grad_kernel<<<(unsigned)(ga.tiles_m * ga.tiles_n * ga.group), kThreads, 0, s>>>(ga);
         }
-        const bf16_bits* Gc = G + slot * g_stride;
-
-        DwArgs da{};
-        DhArgs ha{};
-        if (want_dw) {
-            da.G = Gc;
-            da.HTf = HTf;
-            da.n = L.n;
-            da.n_pad = L.n_pad;
-            da.hidden = L.hidden;
-            da.hid_pad = L.hid_pad;
-            da.v0 = v0;
-            da.width = width;
-            da.w_pad = w_pad;
-            da.tiles_m = L.hid_pad / kTile;
-            da.tiles_n = w_pad / kTile;
-            da.dW = (bf16_bits*)dW;
-            da.dw_acc = dW_acc;
+        if (L.group > 1) {
+            // small batches: dW of the whole group in one launch; dH of the
+            // group's chunks K-split in batches, each joined chunk by chunk
+            if (want_dw) {
+                const DwArgs da = dw_args(c, ng, G);
+                bwd_dw_kernel<<<(unsigned)(da.tiles_m * da.tiles_n * ng), kThreads, 0, s>>>(da);
+            }
+            if (!want_dh) continue;
+            const DhGroupPlan dp = dh_group_plan(L.n_pad, L.hidden, L.w_pad, ng);
+            if (dp.slices == 0) {
+                for (int64_t g = 0; g < ng; ++g)
+                    bwd_dh_kernel<<<(unsigned)n_dh, kThreads, 0, s>>>(dh_args(c + g, c + g, G + g * g_stride));
+                continue;
+            }
+            for (int64_t b0 = 0; b0 < ng; b0 += dp.batch) {
+                const int64_t nb = (ng - b0) < dp.batch ? (ng - b0) : dp.batch;
+                const DhArgs ha = dh_args(c + b0, c + b0 + nb - 1, G + b0 * g_stride);
+                const DhSplit q = split_of(c + b0, nb, dp.slices, L.w_pad);
+                bwd_dh_split_kernel<<<(unsigned)(n_dh * nb * dp.slices), kThreads, 0, s>>>(ha, q, part);
+                dh_join_kernel<<<join_grid, kThreads, 0, s>>>(ha, q, part_in);
+            }
+            continue;
         }
-        if (want_dh) {
-            ha.G = Gc;
-            ha.Wc = Wc;
-            ha.width = width;
-            ha.n = L.n;
-            ha.n_pad = L.n_pad;
-            ha.hidden = L.hidden;
-            ha.w_pad = w_pad;
-            ha.tiles_m = tiles_rows;
-            ha.tiles_n = tiles_hidden;
-            ha.first = c == 0 && dH_acc == nullptr;
-            ha.last = c == nchunks - 1;
-            ha.keep_acc = dH_acc != nullptr;
-            ha.dh_acc = dH_acc != nullptr ? dH_acc : (float*)(w + L.dh_acc);
-            ha.dH = (bf16_bits*)dH;
-        }
+        // one chunk per group
+        const int64_t v0 = c * L.chunk;
+        const int64_t width = (L.vocab - v0) < L.chunk ? (L.vocab - v0) : L.chunk;
+        const int64_t w_pad = round_up(width, kTile);
+        const DwArgs da = dw_args(c, 1, G);
+        const DhArgs ha = dh_args(c, c, G);
         const int64_t n_dw = want_dw ? da.tiles_m * da.tiles_n : 0;
-        const int64_t n_dh = want_dh ? ha.tiles_m * ha.tiles_n : 0;
         const int slices = dh_slices(L.n, L.n_pad, L.hidden, w_pad);
         if (want_dh && slices > 1) {
-            float* part = (float*)(w + L.dh_part);
             if (want_dw) bwd_dw_kernel<<<(unsigned)n_dw, kThreads, 0, s>>>(da);
-            bwd_dh_split_kernel<<<(unsigned)(n_dh * slices), kThreads, 0, s>>>(ha, slices, part);
-            dh_join_kernel<<<grid_1d(L.n * L.hidden / 4, kThreads, 4096), kThreads, 0, s>>>(ha, slices, part);
+            const DhSplit q = split_of(c, 1, slices, w_pad);
+            bwd_dh_split_kernel<<<(unsigned)(n_dh * slices), kThreads, 0, s>>>(ha, q, part);
+            dh_join_kernel<<<join_grid, kThreads, 0, s>>>(ha, q, part_in);
             continue;
         }
         const int plan_one = dwdh_plan(n_dw, L.n_pad / kTileK, n_dh, w_pad / kTileK);
@@ -749,7 +830,8 @@ int lmhead_plan_chunk(const lmhead_problem* p, int entry, size_t budget_bytes, i
     };
     if (!fits(256)) return LMHEAD_ERR_WORKSPACE;
     // largest fitting chunk by bisection over multiples of 256 (the workspace
-    // grows with the chunk, up to the dip noted below)
+    // never shrinks as the chunk widens: the dL/dz region is sized by
+    // grad_cols and the dH partials by the shape alone)
     int64_t lo = 1, hi = cdiv(q.vocab, 256);
     if (entry != LMHEAD_ENTRY_SUPPORT_KL && hi > kMaxChunkPad / 256) hi = kMaxChunkPad / 256;
     while (lo < hi) {
@@ -759,9 +841,8 @@ int lmhead_plan_chunk(const lmhead_problem* p, int entry, size_t budget_bytes, i
     }
     const int64_t passes = cdiv(q.vocab, lo * 256);
     const int64_t even = round_up(cdiv(q.vocab, passes), 256);
-    // the dH K-split's partials make the workspace dip where a wider chunk
-    // takes fewer slices (small batches); the even split of the same passes
-    // is taken only if it fits too, else the bisection's own chunk
+    // the even split of the same passes: no wider than the bisection's
+    // chunk, so it fits as well (checked all the same)
     *chunk = fits(even) ? even : lo * 256;
     return LMHEAD_OK;
 }

@@ -111,11 +111,15 @@ struct LogitGradArgs {
     const int32_t* hit_list;
 };
 
+// dW of `group` consecutive chunks in one launch (one, unless the dL/dz of
+// several was recomputed together): chunk g starts at column v0 + g * chunk,
+// is min(chunk, vocab - its first column) wide and reads slot G + g * g_stride.
 struct DwArgs {
-    const bf16_bits* G;    // dL/dz of the chunk in fragment order [n_pad / 16][w_pad / 32] (pslot lanes)
+    const bf16_bits* G;    // slot 0: dL/dz in fragment order [n_pad / 16][w_pad / 32] (pslot lanes)
     const bf16_bits* HTf;  // H^T in fragment order [n_pad / 32][hid_pad / 16] (ht_pack_kernel)
-    int64_t n, n_pad, hidden, hid_pad, v0, width, w_pad;
-    int64_t tiles_m, tiles_n;   // hidden tiles x chunk-column tiles
+    int64_t n, n_pad, hidden, hid_pad, vocab;
+    int64_t v0, chunk, group, g_stride;
+    int64_t tiles_m, tiles_n;   // hidden tiles x column tiles of the first chunk
     bf16_bits* dW;         // [vocab, hidden] or null
     float* dw_acc;         // caller's fp32 [vocab, hidden] (+=) or null
 };
@@ -130,6 +134,18 @@ struct DhArgs {
     int keep_acc;          // the last chunk also stores the fp32 sum (caller's accumulator)
     float* dh_acc;         // [n, hidden]
     bf16_bits* dH;         // [n, hidden] or null
+};
+
+// The K-split dH of `chunks` consecutive chunks (DhArgs::G is the first
+// one's dL/dz slot, DhArgs::first / last refer to the first / last of them):
+// each chunk's columns are cut into `slices` ranges of ks columns (the last
+// ones of a narrower chunk shorter or empty), one fp32 partial per (chunk,
+// slice), which dh_join_kernel adds to the running sum chunk by chunk.
+struct DhSplit {
+    const bf16_bits* W;    // [vocab, hidden]
+    int64_t v0, chunk, vocab;   // first column of the first chunk, columns per chunk
+    int64_t chunks, slices, ks; // ks: a multiple of 64
+    int64_t g_stride;      // elements between dL/dz slots
 };
 
 // KL-only support entry (candidate gathers, lmhead_candidates.hip)
@@ -177,8 +193,8 @@ __global__ void bwd_logit_grad_kernel(LogitGradArgs a);
 __global__ void bwd_dw_kernel(DwArgs a);
 __global__ void bwd_dh_kernel(DhArgs a);
 __global__ void bwd_dwdh_kernel(DwArgs dw, DhArgs dh, int dh_first);
-__global__ void bwd_dh_split_kernel(DhArgs a, int slices, float* partial);
-__global__ void dh_join_kernel(DhArgs a, int slices, const float* partial);
+__global__ void bwd_dh_split_kernel(DhArgs a, DhSplit q, float* partial);
+__global__ void dh_join_kernel(DhArgs a, DhSplit q, const float* partial);
 __global__ void cand_kl_fwd_kernel(CandFwdArgs a);
 __global__ void cand_dh_kernel(CandBwdArgs a);
 __global__ void cand_count_kernel(const int32_t* ids, int64_t nk, int64_t vocab, int32_t* counts);

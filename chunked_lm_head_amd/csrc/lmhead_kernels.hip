@@ -642,19 +642,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
 // fragment-order copy, B = dL/dz blocks staged in LDS and read with the
 // transposing reads. With a caller accumulator the fp32 sum is first added
 // to it (dw_acc +=), and the bf16 output, if any, is the cast of the updated
-// accumulator.
+// accumulator. The launch's column tiles run over the group's chunks side
+// by side; a narrower last chunk leaves its excess workgroups idle.
 __device__ __forceinline__ void dw_tile(const DwArgs& a, int64_t bid, char* smem) {
-    int64_t tm, tn;
-    map_tile(bid, a.tiles_m, a.tiles_n, tm, tn);
+    int64_t tm, tg;
+    map_tile(bid, a.tiles_m, a.tiles_n * a.group, tm, tg);
+    const int64_t g = tg / a.tiles_n, tn = tg - g * a.tiles_n;
+    const int64_t v0 = a.v0 + g * a.chunk;
+    const int64_t width = (a.vocab - v0) < a.chunk ? (a.vocab - v0) : a.chunk;
+    const int64_t w_pad = (width + kTile - 1) / kTile * kTile;
     const int64_t m0 = tm * kTile, n0 = tn * kTile;   // m0: hidden, n0: chunk column
+    if (n0 >= w_pad) return;   // whole workgroup: past the last chunk's columns
     DaA A;
     A.kblk = a.hid_pad / 16 * 1024;
     A.base = reinterpret_cast<const char*>(a.HTf) + (m0 / 16) * 1024;
     A.koff = 0;
     A.perm = 0;
     DaB B;
-    B.ld = a.w_pad / 32 * 1024;
-    B.base = reinterpret_cast<const char*>(a.G) + (n0 / 32) * 1024;
+    B.ld = w_pad / 32 * 1024;
+    B.base = reinterpret_cast<const char*>(a.G + g * a.g_stride) + (n0 / 32) * 1024;
     B.rows = 0;
     B.n0 = 0;
     AccTile acc;
@@ -679,17 +685,17 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int64_t bid, char* smem
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const int64_t v = n0 + half * 128 + (i0 + u) * 4 + (tid >> 6);
-                    const int64_t vc = v < a.width ? v : a.width - 1;
-                    p[u] = *reinterpret_cast<const float4*>(a.dw_acc + (a.v0 + vc) * a.hidden + hc);
+                    const int64_t vc = v < width ? v : width - 1;
+                    p[u] = *reinterpret_cast<const float4*>(a.dw_acc + (v0 + vc) * a.hidden + hc);
                 }
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int cl = (i0 + u) * 4 + (tid >> 6);      // column of the half
                 const int64_t v = n0 + half * 128 + cl;        // chunk-local vocabulary row
-                if (v >= a.width || !hok) continue;
+                if (v >= width || !hok) continue;
                 const float4 x = *reinterpret_cast<const float4*>(S + cl * kEpiStride + hq);
-                const int64_t o = (a.v0 + v) * a.hidden + h;
+                const int64_t o = (v0 + v) * a.hidden + h;
                 if (a.dw_acc == nullptr) {
                     *reinterpret_cast<uint2*>(a.dW + o) = make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
                 } else {
@@ -815,68 +821,97 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dwdh_kernel(DwArgs dw, DhArgs
     else dw_tile(dw, local, smem);
 }
 
-// Few row tiles (small batches): a chunk's dH tiles are split along the
-// chunk's columns into `slices` equal K ranges (multiples of 64), one
-// workgroup per (slice, tile), each writing its fp32 partial tile to
-// partial[slice, n, hidden]; dh_join_kernel then adds the partials in slice
-// order to the running sum. The split depends only on the problem's shape.
-__global__ __launch_bounds__(kThreads, 1) void bwd_dh_split_kernel(DhArgs a, int slices, float* partial) {
+// Few row tiles (small batches): the dH tiles of one or more chunks are
+// split along each chunk's columns into K ranges of q.ks columns, one
+// workgroup per (chunk, slice, tile), each writing its fp32 partial tile to
+// partial[chunk * slices + slice, n, hidden]; dh_join_kernel then adds them
+// to the running sum. The split depends only on the problem's shape.
+__device__ __forceinline__ DhArgs split_chunk(const DhArgs& a, const DhSplit& q, int64_t g) {
+    DhArgs c = a;
+    const int64_t v0 = q.v0 + g * q.chunk;
+    c.width = (q.vocab - v0) < q.chunk ? (q.vocab - v0) : q.chunk;
+    c.w_pad = (c.width + kTile - 1) / kTile * kTile;
+    c.G = a.G + g * q.g_stride;
+    c.Wc = q.W + v0 * a.hidden;
+    return c;
+}
+
+__global__ __launch_bounds__(kThreads, 1) void bwd_dh_split_kernel(DhArgs a, DhSplit q, float* partial) {
     __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
     const int64_t tiles = a.tiles_m * a.tiles_n;
-    const int64_t sl = blockIdx.x / tiles;
+    const int64_t u = blockIdx.x / tiles;   // chunk * slices + slice
+    const int64_t g = u / q.slices, sl = u - g * q.slices;
+    const DhArgs c = split_chunk(a, q, g);
+    const int64_t k0 = sl * q.ks;
+    if (k0 >= c.w_pad) return;   // whole workgroup: an empty slice of a narrower chunk
+    const int64_t klen = (c.w_pad - k0) < q.ks ? (c.w_pad - k0) : q.ks;
     int64_t tm, tn;
-    map_tile(blockIdx.x - sl * tiles, a.tiles_m, a.tiles_n, tm, tn);
+    map_tile(blockIdx.x - u * tiles, a.tiles_m, a.tiles_n, tm, tn);
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
-    const int64_t ks = a.w_pad / slices, k0 = sl * ks;
     AccTile acc;
-    gemm_mainloop_da<kATile, kBRow>(g_tile(a, m0, k0), wc_rows(a, n0, k0), ks, smem, acc);
+    gemm_mainloop_da<kATile, kBRow>(g_tile(c, m0, k0), wc_rows(c, n0, k0), klen, smem, acc);
     float* S = reinterpret_cast<float*>(smem);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
-    float* out = partial + sl * a.n * a.hidden;
+    float* out = partial + u * a.n * a.hidden;
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
         if (wc == half) stage_half_rows(S, acc, wr, lane);
         __syncthreads();
-        const int c = 4 * (lane & 31);
-        const int64_t h = n0 + half * 128 + c;
+        const int c4 = 4 * (lane & 31);
+        const int64_t h = n0 + half * 128 + c4;
         if (h < a.hidden) {
 #pragma unroll 4
-            for (int u = 0; u < 32; ++u) {
-                const int r = wave * 64 + u * 2 + (lane >> 5);
+            for (int u2 = 0; u2 < 32; ++u2) {
+                const int r = wave * 64 + u2 * 2 + (lane >> 5);
                 const int64_t row = m0 + r;
                 if (row < a.n)
                     *reinterpret_cast<float4*>(out + row * a.hidden + h) =
-                        *reinterpret_cast<const float4*>(S + r * kRowStride + c);
+                        *reinterpret_cast<const float4*>(S + r * kRowStride + c4);
             }
         }
         __syncthreads();
     }
 }
 
-// dh_acc (+)= partial[0] + partial[1] + ... in slice order, four elements per
-// thread; the last chunk writes the bf16 dH and, for a caller accumulator,
-// the fp32 sum, exactly as bwd_dh_kernel's epilogue does.
-__global__ void dh_join_kernel(DhArgs a, int slices, const float* partial) {
+// Chunk by chunk in order: p = the chunk's non-empty slice partials added in
+// slice order, then dh_acc (+)= p, four elements per thread; the last chunk
+// writes the bf16 dH and, for a caller accumulator, the fp32 sum, exactly as
+// bwd_dh_kernel's epilogue does. One chunk of S slices adds exactly as S
+// slices of separate launches would.
+__global__ void dh_join_kernel(DhArgs a, DhSplit q, const float* partial) {
     const int64_t count = a.n * a.hidden / 4;
-    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < count;
-         q += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t o = q * 4;
-        float4 p = *reinterpret_cast<const float4*>(partial + o);
-        for (int sl = 1; sl < slices; ++sl) {
-            const float4 x = *reinterpret_cast<const float4*>(partial + sl * a.n * a.hidden + o);
-            p.x += x.x;
-            p.y += x.y;
-            p.z += x.z;
-            p.w += x.w;
-        }
-        float4 v = p;
-        if (!a.first) {
-            const float4 d = *reinterpret_cast<const float4*>(a.dh_acc + o);
-            v.x = d.x + p.x;
-            v.y = d.y + p.y;
-            v.z = d.z + p.z;
-            v.w = d.w + p.w;
+    const int64_t plane = a.n * a.hidden;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < count;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t o = e * 4;
+        float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        bool have = !a.first;
+        if (have) v = *reinterpret_cast<const float4*>(a.dh_acc + o);
+        for (int64_t g = 0; g < q.chunks; ++g) {
+            const int64_t v0 = q.v0 + g * q.chunk;
+            const int64_t width = (q.vocab - v0) < q.chunk ? (q.vocab - v0) : q.chunk;
+            const int64_t w_pad = (width + kTile - 1) / kTile * kTile;
+            int64_t ns = (w_pad + q.ks - 1) / q.ks;   // non-empty slices
+            ns = ns < q.slices ? ns : q.slices;
+            const float* pg = partial + g * q.slices * plane + o;
+            float4 p = *reinterpret_cast<const float4*>(pg);
+            for (int64_t sl = 1; sl < ns; ++sl) {
+                const float4 x = *reinterpret_cast<const float4*>(pg + sl * plane);
+                p.x += x.x;
+                p.y += x.y;
+                p.z += x.z;
+                p.w += x.w;
+            }
+            if (have) {
+                v.x = v.x + p.x;
+                v.y = v.y + p.y;
+                v.z = v.z + p.z;
+                v.w = v.w + p.w;
+            } else {
+                v = p;
+                have = true;
+            }
         }
         if (a.last && a.dH != nullptr)
             *reinterpret_cast<uint2*>(a.dH + o) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));

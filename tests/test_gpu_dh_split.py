@@ -1,10 +1,14 @@
-"""GPU parity of the K-split dH contraction: with fewer dH tiles (row tiles x
-hidden tiles) than half the compute units and a chunk of at least 16 K steps
-(1024 columns), each chunk's dH tiles are cut along the chunk's columns into
-slices whose fp32 partials are added in slice order. These shapes take that
-route (n = 200 and hidden = 512: two dH tiles; chunk 2048: four slices, the
-last chunk 1024 wide: two). Checked against the oracle, with caller-owned
-accumulators, and for a dH-only backward."""
+"""GPU parity of the K-split dH contraction and of the chunk groups of small
+batches. With fewer dH tiles (row tiles x hidden tiles) than half the compute
+units, each chunk's dH tiles are cut along the chunk's columns into slices
+whose fp32 partials are added in slice order, chunk by chunk. Where a chunk
+has fewer tiles than the compute units, several chunks' dL/dz are recomputed
+in one launch, their dW computed in one launch and their dH slices in
+launches of up to 16 (chunk, slice) units. n = 200, hidden = 512, V = 5000,
+chunk 2048: two dH tiles; chunks 0 and 1 form a group cut into four slices
+each, the 904-wide last chunk is a group of its own whose four 512-column
+slices leave the last two empty. Checked against the oracle, with
+caller-owned accumulators, and for a dH-only backward."""
 import numpy as np
 import pytest
 import torch
@@ -44,9 +48,21 @@ def test_split_dh_against_oracle(entry):
 
 
 @pytest.mark.parametrize("shape", [
-    dict(n=1, hidden=64, vocab=3000, chunk=4096),       # one row, one dH tile, 48 K steps: 4 slices
-    dict(n=33, hidden=320, vocab=4100, chunk=1024),     # ragged hidden tile; 4-wide tail chunk: no split
-    dict(n=513, hidden=256, vocab=2600, chunk=2560),    # three row tiles, 40 K steps: 4 slices
+    # one row, one dH tile, a single chunk of 3072 columns: K-split of one chunk
+    dict(n=1, hidden=64, vocab=3000, chunk=4096),
+    # ragged hidden tile; five chunks, the last 4 wide: chunks 0-3 form a
+    # group (16 K steps each: two slices per chunk, one launch of 8 units),
+    # the last chunk a group of its own (one slice of 256 columns, one empty)
+    dict(n=33, hidden=320, vocab=4100, chunk=1024),
+    # three row tiles, 40 K steps: one chunk per group (two chunks do not fit
+    # the 2816 columns of dL/dz), each K-split on its own
+    dict(n=513, hidden=256, vocab=2600, chunk=2560),
+    # one dH tile, 79 chunks of 4 K steps in one group: no slices, five dH
+    # launches of up to 16 chunks, each joined chunk by chunk
+    dict(n=256, hidden=256, vocab=20000, chunk=256),
+    # 130 dH tiles (two row tiles x 65 hidden tiles): no K-split; four chunks
+    # share the recompute and dW launches, dH runs per chunk
+    dict(n=300, hidden=16640, vocab=1000, chunk=256),
 ])
 def test_split_dh_shapes(shape):
     inp = wlmod.make_inputs(wlmod.custom(seed=910, ignore_frac=0.1, **shape))

@@ -252,12 +252,12 @@ def test_mutation_gate_catches_two_percent():
 
 
 def test_planned_chunk_against_oracle():
-    """A workspace budget that forces many small chunks: the planned chunk
-    runs, fits, and matches the oracle (the result does not depend on the plan
-    beyond rounding of the bf16 dL/dz operand). n = 300, V = 40000 and the
-    256-chunk workspace as the budget plan chunk 1536: 27 chunks, whose
-    dL/dz is recomputed 21 at a time (two row tiles x six column tiles each),
-    the last group holding the 64-wide tail chunk."""
+    """The smallest workspace as the budget (that of chunk 256): the planned
+    chunk runs, fits, and matches the oracle (the result does not depend on
+    the plan beyond rounding of the bf16 dL/dz operand). n = 300, V = 40000:
+    that workspace already holds 256 tiles of dL/dz (32768 columns at two row
+    tiles), so the planner takes the fewest passes within it, two chunks of
+    20224 and 19776 columns."""
     inp = _ragged(0, hidden=256, vocab=40000)
     d = Dev(inp)
     p = lm.problem(inp.wl.n, inp.wl.hidden, inp.wl.vocab, 256)
@@ -265,7 +265,7 @@ def test_planned_chunk_against_oracle():
     chunk = lm.plan_chunk(inp.wl.n, inp.wl.hidden, inp.wl.vocab, budget)
     r = lm.memory_report(inp.wl.n, inp.wl.hidden, inp.wl.vocab, chunk, 0, True, 1)
     assert r["workspace_bytes"] <= budget
-    assert (chunk, r["chunks"], r["dz_group"]) == (1536, 27, 21)
+    assert (chunk, r["chunks"], r["dz_group"]) == (20224, 2, 1)
     H = d.H.clone().requires_grad_(True)
     W = d.W.clone().requires_grad_(True)
     loss = lm.ce_loss(H, W, d.t, memory_budget=budget)

@@ -75,12 +75,13 @@ def test_plan_examples_and_errors():
                                    dict(n=200, hidden=512, vocab=5000),
                                    dict(n=1024, hidden=2048, vocab=151936)])
 def test_plan_always_fits_with_dh_split_partials(shape):
-    """Small batches hold the dH K-split's fp32 partials, whose slice count
-    follows the chunk's K steps and can fall as the chunk widens, so the
-    workspace is not monotone in the chunk there. Whatever the budget, the
+    """Small batches hold the dH K-split's fp32 partials (sized by the shape)
+    and the dL/dz of several chunks (sized to grow with the chunk), so the
+    workspace never shrinks as the chunk widens. Whatever the budget, the
     planned chunk's workspace fits it."""
     ws = [_ws(c, **shape) for c in range(256, 256 * math.ceil(shape["vocab"] / 256) + 1, 256)]
     assert all(w > 0 for w in ws)
+    assert all(a <= b for a, b in zip(ws, ws[1:]))
     lo, hi = min(ws), max(ws)
     for i in range(41):
         budget = lo + (hi - lo) * i // 40
@@ -89,17 +90,28 @@ def test_plan_always_fits_with_dh_split_partials(shape):
 
 
 def test_report_lists_dh_split_partials():
-    """Small batches: the fp32 partials of the dH K-split are listed, S slices
-    of [n, hidden] (n = 256, Hd = 4096, chunk 8192: 16 slices; the 4480-wide
-    tail chunk takes fewer); none at the headline or without the backward."""
+    """Small batches: the fp32 partials of the dH K-split are listed, one
+    [n, hidden] plane per (chunk, slice) unit of a launch, at most 16 and at
+    most 256 dH tiles' worth (n = 256, Hd = 4096: 16 dH tiles, so 16 planes,
+    whatever the chunk); none at the headline (512 dH tiles) or without the
+    backward."""
     r = lm.memory_report(256, 4096, 151936, 8192, 0, True, 1)
     assert r["dh_split_bytes"] == 16 * 4 * 256 * 4096
     parts = r["dz_chunk_bytes"] + r["dh_acc_bytes"] + r["dh_split_bytes"] + r["operand_copy_bytes"]
     assert parts <= r["workspace_bytes"] <= parts + (1 << 20)
     assert lm.memory_report(256, 4096, 151936, 8192, 0, False, 1)["dh_split_bytes"] == 0
     assert lm.memory_report(8192, 4096, 151936, 8192, 0, True, 1)["dh_split_bytes"] == 0
-    # chunk 512 has 8 K steps: too few to split
-    assert lm.memory_report(256, 4096, 151936, 512, 0, True, 1)["dh_split_bytes"] == 0
+    for chunk in (256, 512, 4096, 65536):
+        assert lm.memory_report(256, 4096, 151936, chunk, 0, True, 1)["dh_split_bytes"] == 16 * 4 * 256 * 4096
+    # 64 dH tiles (n = 1024): 4 planes; 128 (n = 2048): 2; 129 .. : none
+    assert lm.memory_report(1024, 4096, 151936, 8192, 0, True, 1)["dh_split_bytes"] == 4 * 4 * 1024 * 4096
+    assert lm.memory_report(2048, 4096, 151936, 8192, 0, True, 1)["dh_split_bytes"] == 2 * 4 * 2048 * 4096
+    assert lm.memory_report(2048, 4352, 151936, 8192, 0, True, 1)["dh_split_bytes"] == 0
+    # the planes never exceed 256 fp32 tiles of 256 x 256 (64 MiB)
+    for n in (1, 200, 256, 513, 1024, 2048, 4000):
+        for hidden in (64, 256, 512, 4096, 8192):
+            b = lm.memory_report(n, hidden, 151936, 8192, 0, True, 1)["dh_split_bytes"]
+            assert b <= 64 << 20, (n, hidden, b)
 
 
 def test_dh_split_slices_are_capped():
