@@ -37,7 +37,7 @@ int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 // Per-tile candidate buckets of the dense support entry (hit_count_kernel):
 // one set in the forward's regions and one in the backward's.
 struct HitRegions {
-    size_t counts, cursor, offsets, tsum, tprefix, list, large, n_large;
+    size_t counts, cursor, offsets, tsum, tprefix, list, sort_tmp, large, n_large;
 };
 
 struct Layout {
@@ -55,7 +55,7 @@ struct Layout {
     size_t dh_part;   // fp32 partial dH tiles of the K-split (few row tiles only)
     int64_t dh_part_bytes;
     // backward of the KL-only entry: inverse index of the candidate ids
-    size_t counts, offsets, cursor, list, tsum, tprefix, large, n_large, pieces, piece_off, partial;
+    size_t counts, offsets, cursor, list, sort_tmp, tsum, tprefix, large, n_large, pieces, piece_off, partial;
     size_t fwd_total, bwd_total;
 };
 
@@ -149,6 +149,7 @@ Layout plan(const lmhead_problem& p, int entry) {
         L.offsets = take(4 * (L.vocab + 1));
         L.cursor = take(4 * L.vocab);
         L.list = take(4 * L.n * L.k);
+        L.sort_tmp = take(4 * L.n * L.k);
         L.tsum = take(4 * cdiv(L.vocab, kScanTile));
         L.tprefix = take(4 * (cdiv(L.vocab, kScanTile) + 1));
         L.large = take(4 * L.vocab);
@@ -169,6 +170,7 @@ Layout plan(const lmhead_problem& p, int entry) {
         R.tsum = take(4 * cdiv(nb, kScanTile));
         R.tprefix = take(4 * (cdiv(nb, kScanTile) + 1));
         R.list = take(4 * L.n * L.k);
+        R.sort_tmp = take(4 * L.n * L.k);
         R.large = take(4 * nb);
         R.n_large = take(4);
     };
@@ -370,7 +372,8 @@ void build_hits(const Layout& L, const HitRegions& R, char* w, const int32_t* id
     fill_u32(n_large, 1, 0u, s);
     bucket_sort_wave_kernel<<<(unsigned)cdiv(nb, kThreads / 64), kThreads, 0, s>>>(offsets, nb, list, large,
                                                                                   n_large);
-    bucket_sort_block_kernel<<<kSortBlocks, 1024, 0, s>>>(offsets, list, large, n_large);
+    bucket_sort_block_kernel<<<kSortBlocks, 1024, 0, s>>>(offsets, list, (int32_t*)(w + R.sort_tmp), large,
+                                                          n_large);
     *offsets_out = offsets;
     *list_out = list;
 }
@@ -560,7 +563,8 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
             fill_u32(n_large, 1, 0u, s);
             bucket_sort_kernel<<<grid_1d(L.vocab, kThreads, 4096), kThreads, 0, s>>>(offsets, L.vocab, list,
                                                                                      large, n_large);
-            bucket_sort_block_kernel<<<kSortBlocks, 1024, 0, s>>>(offsets, list, large, n_large);
+            bucket_sort_block_kernel<<<kSortBlocks, 1024, 0, s>>>(offsets, list, (int32_t*)(w + L.sort_tmp), large,
+                                                                  n_large);
             cand_dw_kernel<<<(unsigned)cdiv(L.vocab, kThreads / 64), kThreads, 0, s>>>(cb);
             cand_dw_mid_kernel<<<kSplitBlocks, kThreads, 0, s>>>(cb, large, n_large);
             // buckets above kDwSplitEntries entries: pieces, their offsets, partial rows, join

@@ -337,53 +337,91 @@ __global__ __launch_bounds__(256) void bucket_sort_wave_kernel(const int32_t* of
     if (lane < cnt) list[b + lane] = x;
 }
 
-// The listed large buckets, one workgroup of 1024 threads per bucket: a
-// bitonic sort in LDS over the bucket padded with INT_MAX to a power of two.
-// A bucket beyond kSortLdsMax entries (only a degenerate candidate list
-// makes one) falls back to an insertion sort by one thread.
-__global__ __launch_bounds__(1024) void bucket_sort_block_kernel(const int32_t* offsets, int32_t* list,
+// The listed large buckets, one workgroup of 1024 threads per bucket. Runs
+// of up to kSortLdsMax entries are sorted in LDS by a bitonic network over
+// the run padded with INT_MAX to a power of two; a bucket with more entries
+// (only a heavily skewed candidate list makes one) then merges its sorted
+// runs pairwise, doubling the run length each pass, between the list and the
+// bucket's own range of tmp (merge path: each thread finds by binary search
+// where its share of the output starts in each run, then merges that share),
+// so a bucket of m entries takes O(m log m) work spread over the workgroup.
+__device__ void sort_run_lds(int32_t* sh, int32_t* p, int32_t m) {
+    const int t = threadIdx.x;
+    int32_t P = 64;
+    while (P < m) P <<= 1;
+    for (int32_t i = t; i < P; i += 1024) sh[i] = i < m ? p[i] : INT_MAX;
+    __syncthreads();
+    for (int32_t k = 2; k <= P; k <<= 1)
+        for (int32_t j = k >> 1; j > 0; j >>= 1) {
+            for (int32_t i = t; i < P; i += 1024) {
+                const int32_t l = i ^ j;
+                if (l > i) {
+                    const int32_t x = sh[i], y = sh[l];
+                    const bool up = (i & k) == 0;
+                    if ((x > y) == up) {
+                        sh[i] = y;
+                        sh[l] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    for (int32_t i = t; i < m; i += 1024) p[i] = sh[i];
+    __syncthreads();
+}
+
+// Entries of a (sorted, distinct) taken among the first d of the merge of a
+// and b.
+__device__ __forceinline__ int64_t merge_split(const int32_t* a, int64_t na, const int32_t* b, int64_t nb, int64_t d) {
+    int64_t lo = d > nb ? d - nb : 0, hi = d < na ? d : na;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) / 2;
+        if (a[mid] < b[d - mid - 1]) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// out[0, na + nb) = the merge of the sorted runs a and b, by the workgroup.
+__device__ void merge_runs(const int32_t* a, int64_t na, const int32_t* b, int64_t nb, int32_t* out) {
+    const int64_t L = na + nb;
+    const int64_t t = threadIdx.x;
+    const int64_t d0 = L * t / 1024, d1 = L * (t + 1) / 1024;
+    int64_t i = merge_split(a, na, b, nb, d0), j = d0 - i;
+    for (int64_t d = d0; d < d1; ++d) {
+        const bool take_a = j >= nb || (i < na && a[i] < b[j]);
+        out[d] = take_a ? a[i++] : b[j++];
+    }
+}
+
+__global__ __launch_bounds__(1024) void bucket_sort_block_kernel(const int32_t* offsets, int32_t* list, int32_t* tmp,
                                                                  const int32_t* large, const int32_t* n_large) {
     __shared__ int32_t sh[kSortLdsMax];
     const int t = threadIdx.x;
     const int32_t count = *n_large;
     for (int32_t q = blockIdx.x; q < count; q += gridDim.x) {
         const int32_t v = large[q];
-        const int32_t b = offsets[v], e = offsets[v + 1];
-        const int32_t m = e - b;
-        if (m > kSortLdsMax) {
-            if (t == 0)
-                for (int32_t i = b + 1; i < e; ++i) {
-                    const int32_t x = list[i];
-                    int32_t j = i - 1;
-                    while (j >= b && list[j] > x) {
-                        list[j + 1] = list[j];
-                        --j;
-                    }
-                    list[j + 1] = x;
-                }
-            __syncthreads();
-            continue;
-        }
-        int32_t P = 64;
-        while (P < m) P <<= 1;
-        for (int32_t i = t; i < P; i += 1024) sh[i] = i < m ? list[b + i] : INT_MAX;
-        __syncthreads();
-        for (int32_t k = 2; k <= P; k <<= 1)
-            for (int32_t j = k >> 1; j > 0; j >>= 1) {
-                for (int32_t i = t; i < P; i += 1024) {
-                    const int32_t l = i ^ j;
-                    if (l > i) {
-                        const int32_t x = sh[i], y = sh[l];
-                        const bool up = (i & k) == 0;
-                        if ((x > y) == up) {
-                            sh[i] = y;
-                            sh[l] = x;
-                        }
-                    }
-                }
-                __syncthreads();
+        const int64_t b = offsets[v], e = offsets[v + 1];
+        const int64_t m = e - b;
+        for (int64_t r0 = 0; r0 < m; r0 += kSortLdsMax)
+            sort_run_lds(sh, list + b + r0, (int32_t)(m - r0 < kSortLdsMax ? m - r0 : kSortLdsMax));
+        if (m <= kSortLdsMax) continue;
+        int32_t* src = list + b;
+        int32_t* dst = tmp + b;
+        for (int64_t w = kSortLdsMax; w < m; w *= 2) {
+            for (int64_t p0 = 0; p0 < m; p0 += 2 * w) {
+                const int64_t na = m - p0 < w ? m - p0 : w;
+                const int64_t rest = m - p0 - na;
+                const int64_t nb = rest < w ? rest : w;
+                merge_runs(src + p0, na, src + p0 + na, nb, dst + p0);
             }
-        for (int32_t i = t; i < m; i += 1024) list[b + i] = sh[i];
+            __syncthreads();
+            int32_t* x = src;
+            src = dst;
+            dst = x;
+        }
+        if (src != list + b)
+            for (int64_t i = t; i < m; i += 1024) list[b + i] = src[i];
         __syncthreads();
     }
 }

@@ -209,7 +209,7 @@ __global__ void bucket_sort_kernel(const int32_t* offsets, int64_t buckets, int3
                                    int32_t* n_large);
 __global__ void bucket_sort_wave_kernel(const int32_t* offsets, int64_t buckets, int32_t* list, int32_t* large,
                                         int32_t* n_large);
-__global__ void bucket_sort_block_kernel(const int32_t* offsets, int32_t* list, const int32_t* large,
+__global__ void bucket_sort_block_kernel(const int32_t* offsets, int32_t* list, int32_t* tmp, const int32_t* large,
                                          const int32_t* n_large);
 __global__ void cand_dw_mid_kernel(CandBwdArgs a, const int32_t* large, const int32_t* n_large);
 __global__ void cand_split_counts_kernel(const int32_t* offsets, const int32_t* large, const int32_t* n_large,

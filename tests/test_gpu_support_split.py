@@ -301,3 +301,55 @@ def test_skewed_candidate_lists():
     torch.cuda.synchronize()
     assert torch.equal(ko["dW"], ko2["dW"]) and torch.equal(ko["dH"], ko2["dH"])
     assert torch.equal(dW, dW2) and torch.equal(dH, dH2)
+
+
+def test_bucket_beyond_one_lds_sort_kl_only():
+    """A vocabulary bucket of the KL-only dW with more entries than one
+    workgroup sorts in LDS (32768): n = 33000 rows all list id 5 (and one
+    other id), so bucket 5 holds 33000 entries, sorted as two LDS runs and one
+    merge pass. dW row 5 sums them in ascending (row, slot) order: against the
+    oracle, plus a bitwise repeat."""
+    inp = _inputs(n=33000, hidden=64, vocab=300, k=2, seed=820)
+    rng = np.random.default_rng(821)
+    inp.ids[:, 0] = 5
+    inp.ids[:, 1] = rng.integers(6, 300, size=inp.ids.shape[0])
+    d = Dev(inp)
+    ko = _kl_only(d)
+    torch.cuda.synchronize()
+    ref = oracle.run(oracle.ENTRY_SUPPORT_KL, inp.H, inp.W, ids=inp.ids, ref_logq=inp.ref_logq,
+                     grad_kl=inp.grad_kl)
+    rel_check("kl-only kl", to_np(ko["kl"]), ref["kl"])
+    grad_check("kl-only dH", bf16_to_np(ko["dH"]), ref["dH"])
+    grad_check("kl-only dW", bf16_to_np(ko["dW"]), ref["dW"])
+    ko2 = _kl_only(d)
+    torch.cuda.synchronize()
+    assert torch.equal(ko["dW"], ko2["dW"]) and torch.equal(ko["dH"], ko2["dH"])
+
+
+def test_hit_bucket_beyond_one_lds_sort():
+    """A per-tile hit bucket of the dense support entry with more entries
+    than one workgroup sorts in LDS: V = 256 (one vocabulary tile) and
+    k = 160 distinct candidates per row, so the first row tile's bucket holds
+    256 x 160 = 40960 (row, column, slot) hits, sorted as two LDS runs and one
+    merge pass: forward and backward against the oracle, plus a bitwise
+    repeat."""
+    inp = _inputs(n=300, hidden=128, vocab=256, k=160, seed=830)
+    rng = np.random.default_rng(831)
+    for i in range(inp.ids.shape[0]):
+        inp.ids[i] = rng.permutation(256)[:160]
+    d = Dev(inp)
+    lp, kl, lse, _ = lm.support_forward(d.H, d.W, d.ids, d.ref_logq, 256)
+    dH, dW = lm.backward(lm.ENTRY_SUPPORT, d.H, d.W, d.ids, lse, d.grad, 256, ref_logq=d.ref_logq,
+                         saved_lp=lp, grad_kl=d.grad_kl)
+    torch.cuda.synchronize()
+    ref = oracle.run(3, inp.H, inp.W, ids=inp.ids, ref_logq=inp.ref_logq, grad=inp.grad,
+                     grad_kl=inp.grad_kl)
+    rel_check("lp", to_np(lp), ref["lp"])
+    rel_check("kl", to_np(kl), ref["kl"])
+    grad_check("dH", bf16_to_np(dH), ref["dH"])
+    grad_check("dW", bf16_to_np(dW), ref["dW"])
+    lp2, kl2, lse2, _ = lm.support_forward(d.H, d.W, d.ids, d.ref_logq, 256)
+    dH2, dW2 = lm.backward(lm.ENTRY_SUPPORT, d.H, d.W, d.ids, lse2, d.grad, 256, ref_logq=d.ref_logq,
+                           saved_lp=lp2, grad_kl=d.grad_kl)
+    torch.cuda.synchronize()
+    assert torch.equal(lp, lp2) and torch.equal(dW, dW2) and torch.equal(dH, dH2)

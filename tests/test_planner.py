@@ -27,7 +27,9 @@ def test_report_matches_workspace_and_layout():
         # H in fragment order, and in the backward H^T too
         assert r["operand_copy_bytes"] == 2 * (2 * 8192 * 4096)
         parts = r["dz_chunk_bytes"] + r["dh_acc_bytes"] + r["operand_copy_bytes"]
-        assert parts <= r["workspace_bytes"] <= parts + (1 << 20) + 4 * 8192 * (k + 2) * 2
+        # the rest: header, per-row coefficients and, with candidates, the
+        # per-tile hit list and its merge-sort buffer (4 N k bytes each)
+        assert parts <= r["workspace_bytes"] <= parts + (1 << 20) + 4 * 8192 * (k + 2) * 3
         f = lm.memory_report(8192, 4096, 151936, 8192, entry, False, k)
         assert f["workspace_bytes"] == f["forward_bytes"] == r["forward_bytes"]
         assert f["dz_chunk_bytes"] == f["dh_acc_bytes"] == 0
