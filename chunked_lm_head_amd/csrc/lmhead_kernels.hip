@@ -665,52 +665,48 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int64_t bid, char* smem
     B.n0 = 0;
     AccTile acc;
     gemm_mainloop_da<kAStep, kBFrag>(A, B, a.n_pad, smem, acc);
-    float* S = reinterpret_cast<float*>(smem);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // Lane l of block (i, j) holds hidden positions 4 (l / 16) .. + 4 of chunk
+    // column l % 16: four consecutive elements of one dW row, stored straight
+    // from the accumulators (8 bytes of bf16; with a caller accumulator 16
+    // bytes of fp32 read, added and written back), no LDS staging
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wr = wave >> 1, wc = wave & 1;
-    // S = [chunk column 0..127 of the half][hidden 0..255]: 64 lanes per dW row
-    // (4 hidden columns each, one 512-byte bf16 row segment), 4 rows per pass
-    const int hq = 4 * (tid & 63);
-    const int64_t h = m0 + hq;
-    const bool hok = h < a.hidden;   // hidden is a multiple of 64: all four or none
-    const int64_t hc = hok ? h : 0;
-#pragma unroll 1
-    for (int half = 0; half < 2; ++half) {
-        if (wc == half) stage_half(S, acc, wr, lane);
-        __syncthreads();
-#pragma unroll 1
-        for (int i0 = 0; i0 < 32; i0 += 8) {
-            float4 p[8];
-            if (a.dw_acc != nullptr) {
+    const int64_t h0 = m0 + wr * 128 + 4 * (lane >> 4);    // hidden position of block row 0
+    const int64_t c0 = n0 + wc * 128 + (lane & 15);        // chunk column of block column 0
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int64_t v = n0 + half * 128 + (i0 + u) * 4 + (tid >> 6);
-                    const int64_t vc = v < width ? v : width - 1;
-                    p[u] = *reinterpret_cast<const float4*>(a.dw_acc + (v0 + vc) * a.hidden + hc);
-                }
+    for (int j = 0; j < 8; ++j) {
+        const int64_t v = c0 + 16 * j;
+        if (v >= width) continue;
+        const int64_t orow = (v0 + v) * a.hidden;
+        if (a.dw_acc == nullptr) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int64_t h = h0 + 16 * i;   // hidden is a multiple of 64: all four or none
+                if (h < a.hidden)
+                    *reinterpret_cast<uint2*>(a.dW + orow + h) =
+                        make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+            }
+        } else {
+            float4 p[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int64_t h = h0 + 16 * i;
+                p[i] = *reinterpret_cast<const float4*>(a.dw_acc + orow + (h < a.hidden ? h : 0));
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int cl = (i0 + u) * 4 + (tid >> 6);      // column of the half
-                const int64_t v = n0 + half * 128 + cl;        // chunk-local vocabulary row
-                if (v >= width || !hok) continue;
-                const float4 x = *reinterpret_cast<const float4*>(S + cl * kEpiStride + hq);
-                const int64_t o = (v0 + v) * a.hidden + h;
-                if (a.dw_acc == nullptr) {
-                    *reinterpret_cast<uint2*>(a.dW + o) = make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
-                } else {
-                    float4 y;
-                    y.x = p[u].x + x.x;
-                    y.y = p[u].y + x.y;
-                    y.z = p[u].z + x.z;
-                    y.w = p[u].w + x.w;
-                    *reinterpret_cast<float4*>(a.dw_acc + o) = y;
-                    if (a.dW != nullptr)
-                        *reinterpret_cast<uint2*>(a.dW + o) = make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
-                }
+            for (int i = 0; i < 8; ++i) {
+                const int64_t h = h0 + 16 * i;
+                if (h >= a.hidden) continue;
+                float4 y;
+                y.x = p[i].x + acc[i][j][0];
+                y.y = p[i].y + acc[i][j][1];
+                y.z = p[i].z + acc[i][j][2];
+                y.w = p[i].w + acc[i][j][3];
+                *reinterpret_cast<float4*>(a.dw_acc + orow + h) = y;
+                if (a.dW != nullptr)
+                    *reinterpret_cast<uint2*>(a.dW + orow + h) = make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
             }
         }
-        __syncthreads();
     }
 }
 
