@@ -146,21 +146,23 @@ __device__ __forceinline__ DaB kb_tile(const bf16_bits* X, int64_t n0, int64_t l
 // lane gathers its column's 8 rows).
 __global__ __launch_bounds__(256) void ht_pack_kernel(const bf16_bits* H, int64_t n, int64_t hidden, int64_t hid_pad,
                                                       bf16_bits* HTf) {
-    __shared__ bf16_bits T[32][256 + 8];
+    __shared__ __attribute__((aligned(16))) bf16_bits T[32][256 + 8];
     const int64_t kb = blockIdx.x;        // 32-row block
     const int64_t hg = blockIdx.y;        // 256-column group
     const int tid = threadIdx.x;
     {
-        const int r = tid >> 3, seg = (tid & 7) * 32;   // 32 rows x 8 segments of 32 columns
-        const int64_t row = kb * 32 + r;
+        // 32 rows x 32 pieces of 8 columns: consecutive threads take
+        // consecutive 16-byte pieces of a row (coalesced), each stored to the
+        // LDS row in one 16-byte write (the row pitch, 528 bytes, keeps them
+        // aligned)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int64_t col = hg * 256 + seg + q * 8;
+            const int idx = q * 256 + tid;
+            const int r = idx >> 5, c8 = (idx & 31) * 8;
+            const int64_t row = kb * 32 + r, col = hg * 256 + c8;
             uint4 v = make_uint4(0u, 0u, 0u, 0u);
             if (row < n && col < hidden) v = *reinterpret_cast<const uint4*>(H + row * hidden + col);
-            const bf16_bits* e = reinterpret_cast<const bf16_bits*>(&v);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) T[r][seg + q * 8 + i] = e[i];
+            *reinterpret_cast<uint4*>(&T[r][c8]) = v;
         }
     }
     __syncthreads();
