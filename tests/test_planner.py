@@ -162,3 +162,21 @@ def test_small_batch_groups_chunks_per_recompute():
     assert c >= 256 and _ws(c, n=256) <= floor
     with pytest.raises(lm.LMHeadError):
         lm.plan_chunk(256, 4096, 151936, floor - 1)
+
+
+@pytest.mark.parametrize("shape", [dict(n=256, hidden=4096, vocab=151936),
+                                   dict(n=200, hidden=512, vocab=5000),
+                                   dict(n=2048, hidden=4352, vocab=151936)])
+def test_plan_takes_fewest_passes_at_small_batches(shape):
+    """The workspace never shrinks as the chunk widens, so the planner's
+    bisection finds the fewest vocabulary passes that fit: no chunk with
+    fewer passes fits the budget, and the planned chunk fits it."""
+    v = shape["vocab"]
+    ws = {c: _ws(c, **shape) for c in range(256, 256 * math.ceil(v / 256) + 1, 256)}
+    lo, hi = min(ws.values()), max(ws.values())
+    for i in range(0, 41, 4):
+        budget = lo + (hi - lo) * i // 40
+        c = lm.plan_chunk(shape["n"], shape["hidden"], v, budget)
+        assert ws[c] <= budget
+        passes = math.ceil(v / c)
+        assert all(w > budget for cc, w in ws.items() if math.ceil(v / cc) < passes), (budget, c)
