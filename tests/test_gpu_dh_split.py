@@ -104,3 +104,27 @@ def test_split_dh_into_accumulator():
     grad_check("dH_acc - X", to_np(dH_acc - x), ref["dH"])
     grad_check("dW_acc", to_np(dW_acc), ref["dW"])
     assert torch.equal(dW_acc.to(torch.bfloat16), plain["dW"])
+
+
+@pytest.mark.parametrize("entry", [0, 2, 3])
+def test_forward_and_dw_do_not_depend_on_the_chunk(entry):
+    """Every dL/dz element comes from the same K loop over the hidden size
+    whatever the chunk, and every dW tile sums the rows in the same order, so
+    the forward outputs and dW are bit for bit the same for any chunk width
+    and any chunk grouping; only dH, summed chunk by chunk, differs (each
+    checked against the oracle). n = 300, V = 5000: chunk 256 (20 chunks in
+    one recompute group), 1024 (5 chunks in one group), 2048 (3 chunks in
+    groups of 2 and 1) and 5120 (one chunk)."""
+    inp = _inputs(entry, n=300, vocab=5000)
+    d = Dev(inp)
+    outs = [run_entry(d, entry, c) for c in (256, 1024, 2048, 5120)]
+    torch.cuda.synchronize()
+    base = outs[0]
+    for o in outs[1:]:
+        for key, val in base.items():
+            if key != "dH":
+                assert torch.equal(val, o[key]), key
+    ref = _ref(entry, inp)
+    for o in outs:
+        grad_check("dH", bf16_to_np(o["dH"]), ref["dH"])
+    grad_check("dW", bf16_to_np(base["dW"]), ref["dW"])
