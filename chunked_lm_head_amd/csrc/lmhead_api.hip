@@ -28,6 +28,7 @@ constexpr int64_t kMaxHidden = 65536;
 // operand of the dH contraction with a row pitch of that width, and a tile's
 // buffer range (256 rows of it, in bytes) must stay below 2^31.
 constexpr int64_t kMaxChunkPad = (int64_t(1) << 22) - 256;
+constexpr int64_t kMaxWorkItems = 0xffffffffLL;   // work-items in one launch
 // Most K slices of a chunk's dH contraction (bounds the fp32 partials)
 constexpr int kMaxDhSlices = 16;
 
@@ -82,8 +83,20 @@ int validate_problem(const lmhead_problem* p, int entry) {
     if (entry != LMHEAD_ENTRY_SUPPORT_KL &&
         round_up(p->chunk < p->vocab ? p->chunk : p->vocab, kTile) > kMaxChunkPad)
         return LMHEAD_ERR_SHAPE;
-    // one workgroup per 256 x 256 tile: keep every grid within 2^31 - 1
-    if (cdiv(p->n, kTile) * cdiv(p->vocab, kTile) > INT_MAX) return LMHEAD_ERR_SHAPE;
+    // A launch holds at most 2^32 - 1 work-items (the dispatch's grid size is
+    // a 32-bit count). The support entries' per-row kernels run 64 threads per
+    // row (n_pad rows), the other entries' at most 8; the KL-only entry's dW
+    // pass runs 64 per vocabulary id; every other entry runs one 256-thread
+    // workgroup per 256 x 256 tile of rows x vocabulary (forward, recompute)
+    // and of rows x hidden (dH). The other launches have capped grids.
+    const int64_t n_pad = round_up(p->n, kTile);
+    if ((is_support(entry) ? 64 : 8) * n_pad > kMaxWorkItems) return LMHEAD_ERR_SHAPE;
+    if (entry == LMHEAD_ENTRY_SUPPORT_KL) {
+        if (64 * round_up(p->vocab, 4) > kMaxWorkItems) return LMHEAD_ERR_SHAPE;
+    } else {
+        const int64_t tv = cdiv(p->vocab, kTile), th = cdiv(p->hidden, kTile);
+        if (cdiv(p->n, kTile) * (tv > th ? tv : th) * kThreads > kMaxWorkItems) return LMHEAD_ERR_SHAPE;
+    }
     return LMHEAD_OK;
 }
 

@@ -125,6 +125,16 @@ enum lmhead_device_error {
  *   k          candidates per row for the support entries (1..1024, and
  *              n * k <= 2^31 - 1: both support entries index their (row,
  *              candidate) entries with int32); ignored by the others.
+ *   Launch sizes: one launch holds at most 2^32 - 1 work-items, so with
+ *              n_pad = round_up(n, 256): 8 * n_pad <= 2^32 - 1 (n <=
+ *              536,870,656), and 64 * n_pad <= 2^32 - 1 for the support
+ *              entries (n <= 67,108,608); every entry but the KL-only one
+ *              also needs ceil(n / 256) * max(ceil(vocab / 256),
+ *              ceil(hidden / 256)) <= 16,777,215 (one 256-thread workgroup
+ *              per 256 x 256 tile; at vocab = 151,936: n <= 7,230,464), and
+ *              the KL-only entry 64 * round_up(vocab, 4) <= 2^32 - 1 (vocab
+ *              <= 67,108,860). Larger problems are a shape error; split
+ *              the rows over several calls.
  *   flags      0, or LMHEAD_FLAG_PADDED_IDS with a support entry.
  *   temperature     scalar temperature t applied to every row; 0 = off
  *                   (t = 1). Must be finite and >= 0.

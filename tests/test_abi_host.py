@@ -80,7 +80,8 @@ def test_workspace_size_rules():
     head = lm.problem(8192, 4096, 151936, 8192, -1, 1, 0)
     b = ws(head, 0, 1)
     assert b > 2 * 2 * 8192 * 8192 and b < 1 << 31
-    big = lm.problem(1 << 20, 8192, 1 << 20, 1 << 20, -1, 1, 0)
+    # the largest vocabulary whose forward grid fits one launch at 2^20 rows
+    big = lm.problem(1 << 20, 8192, 4095 * 256, 1 << 20, -1, 1, 0)
     assert ws(big, 0, 1) > 1 << 40    # no 32-bit wrap
     assert ws(_p(n=0), 0, 0) > 0 and ws(_p(n=0), 0, 1) > 0
 
@@ -234,6 +235,50 @@ def test_support_entries_reject_int32_entry_counts():
     with pytest.raises(lm.LMHeadError) as e:
         lm.memory_report(over["n"], 64, 4096, 4096, lm.ENTRY_SUPPORT, True, 1024)
     assert e.value.status == S
+
+
+def test_launch_sizes_are_bounded():
+    """One launch holds at most 2^32 - 1 work-items: the per-row kernels (8
+    threads per padded row, 64 for the support entries), the tile kernels (one
+    256-thread workgroup per 256 x 256 tile of rows x vocabulary or rows x
+    hidden) and the KL-only entry's per-id dW pass (64 threads per id) must
+    each fit, or the call is a shape error before any launch. Each rule is
+    checked on both sides of its boundary."""
+    ws = lm.lmhead_workspace_size
+    top = (1 << 32) - 1
+    S = lm.LMHEAD_ERR_SHAPE
+    # 8 threads per padded row
+    n8 = top // 8 // 256 * 256
+    assert ws(_p(n=n8, hidden=64, vocab=256), lm.ENTRY_CE_MEAN, 1) > 0
+    assert ws(_p(n=n8 + 1, hidden=64, vocab=256), lm.ENTRY_CE_MEAN, 1) == 0
+    assert ws(_p(n=n8 + 1, hidden=64, vocab=256), lm.ENTRY_LOGPROB, 0) == 0
+    # 64 threads per padded row for the support entries
+    n64 = top // 64 // 256 * 256
+    for e in (lm.ENTRY_SUPPORT, lm.ENTRY_SUPPORT_KL):
+        assert ws(_p(n=n64, hidden=64, vocab=256, k=1), e, 1) > 0
+        assert ws(_p(n=n64 + 1, hidden=64, vocab=256, k=1), e, 1) == 0
+    # one workgroup per tile: rows x vocabulary at the 151,936-id vocabulary
+    tv = -(-151936 // 256)
+    nt = (top // 256) // tv * 256
+    assert nt == 7230464
+    assert ws(_p(n=nt, hidden=4096, vocab=151936, chunk=8192), lm.ENTRY_CE_MEAN, 1) > 0
+    assert ws(_p(n=nt + 1, hidden=4096, vocab=151936, chunk=8192), lm.ENTRY_CE_MEAN, 1) == 0
+    assert ws(_p(n=nt + 1, hidden=4096, vocab=151936, chunk=8192), lm.ENTRY_CE_MEAN, 0) == 0
+    # ... and rows x hidden, when the hidden size has more tiles than the vocabulary
+    nh = (top // 256) // 256 * 256
+    assert ws(_p(n=nh, hidden=65536, vocab=256), lm.ENTRY_LOGPROB, 1) > 0
+    assert ws(_p(n=nh + 1, hidden=65536, vocab=256), lm.ENTRY_LOGPROB, 1) == 0
+    # the KL-only entry has no tile pass (the rows x vocabulary rule does not
+    # apply) but 64 threads per vocabulary id
+    assert ws(_p(n=nt + 1, hidden=4096, vocab=151936, chunk=8192, k=4), lm.ENTRY_SUPPORT_KL, 1) > 0
+    vk = top // 64 // 4 * 4
+    assert ws(_p(n=256, hidden=64, vocab=vk, chunk=256, k=4), lm.ENTRY_SUPPORT_KL, 1) > 0
+    assert ws(_p(n=256, hidden=64, vocab=vk + 1, chunk=256, k=4), lm.ENTRY_SUPPORT_KL, 1) == 0
+    # the entry points return the same shape error before touching a device
+    p = _p(n=nt + 1, hidden=4096, vocab=151936, chunk=8192)
+    assert lm.lmhead_loss_fwd(p, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, BIG, 0) == S
+    assert lm.lmhead_loss_bwd(p, 0, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, FAKE,
+                              BIG, 0) == S
 
 
 def test_chunk_width_is_capped():
