@@ -284,10 +284,19 @@ class Runner:
         if st:
             raise lm.LMHeadError(st, "backward")
 
-    def digest(self):
+    def outputs(self):
+        return (self.loss, self.lse, self.row_out, self.kl, self.dH, self.dW)
+
+    def snapshot(self):
+        """Device copies of the outputs, enqueued on the calls' stream (no host
+        round trip, so the next step starts right behind them)."""
+        with self.torch.cuda.stream(self.stream):
+            return tuple(t.clone() for t in self.outputs())
+
+    def digest(self, tensors=None):
         self.torch.cuda.synchronize()
         h = hashlib.sha256()
-        for t in (self.loss, self.lse, self.row_out, self.kl, self.dH, self.dW):
+        for t in tensors if tensors is not None else self.outputs():
             h.update(t.view(self.torch.uint8).cpu().numpy().tobytes())
         return h.hexdigest()
 
@@ -295,7 +304,9 @@ class Runner:
 def time_steps(torch, run, steps, warmup):
     """`warmup` untimed steps, then `steps` timed ones (HIP events on the calls'
     stream, wall clock between device synchronisations); then one more step
-    must reproduce the last timed step's outputs bit for bit."""
+    must reproduce the last timed step's outputs bit for bit. The last timed
+    step's outputs are copied on the device and the extra step follows at once,
+    so it runs as warm as the timed ones; both are hashed afterwards."""
     for _ in range(warmup):
         run.fwd()
         run.bwd()
@@ -320,10 +331,12 @@ def time_steps(torch, run, steps, warmup):
     ms_per_step = wall * 1e3 / steps
     log(f"timed {steps} steps: wall {ms_per_step:.3f} ms/step; events fwd {np.mean(fwd_ms):.3f} "
         f"bwd {np.mean(bwd_ms):.3f} step {np.mean(step_ms):.3f} ms")
-    d1 = run.digest()
+    snap = run.snapshot()
     run.fwd()
     run.bwd()
     d2 = run.digest()
+    d1 = run.digest(snap)
+    del snap
     log(f"bitwise repeat: {d1 == d2} ({d1[:16]})")
     return {"wall_s": wall, "ms_per_step": ms_per_step, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
             "step_ms": step_ms, "deterministic": d1 == d2}
