@@ -200,8 +200,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTilesArgs a) 
     const int wr = wave >> 1, wc = wave & 1;
     const int64_t row = m0 + tid;
     const bool row_ok = row < a.n;
-    // logits / tau_n (the scale is exactly 1 without a temperature)
+    // logits / tau_n (the scale is exactly 1 without a temperature, and the
+    // multiply is then skipped: x * 1 = x)
     const float inv_tau = row_ok ? 1.0f / row_tau(a.T, row) : 1.0f;
+    const bool unit_tau = a.T.row == nullptr && a.T.t == 1.0f;
     float* Sr = S + tid;
     float run_m = neg_inf(), run_s = 0.0f;
 #pragma unroll 1
@@ -216,8 +218,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTilesArgs a) 
         // read as -inf: they leave the max alone and add exp2(-inf) = +0 to
         // the sum (a half with ncol = 0 is never merged).
         float x[128];
+        if (unit_tau) {
 #pragma unroll
-        for (int c = 0; c < 128; ++c) x[c] = Sr[c * kEpiStride] * inv_tau;
+            for (int c = 0; c < 128; ++c) x[c] = Sr[c * kEpiStride];
+        } else {
+#pragma unroll
+            for (int c = 0; c < 128; ++c) x[c] = Sr[c * kEpiStride] * inv_tau;
+        }
         if (ncol < 128) {
 #pragma unroll
             for (int c = 0; c < 128; ++c) x[c] = c < ncol ? x[c] : neg_inf();
@@ -534,9 +541,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
     const int wr = wave >> 1, wc = wave & 1;
     const int64_t row = m0 + tid;   // < n_pad
     const bool row_ok = row < a.n;
+    // A row with a_n = 0 (past n, ignored, or with a data error or a bad
+    // temperature, whose lse or tau may be NaN, 0 or inf) gets the scale 0 and
+    // the offset +inf, so its exp2 is exactly 0 for any finite logit; the
+    // other rows compute a_n exp2(z log2(e) / tau_n - lse_n log2(e)).
     const float ca = row_ok ? a.coef_a[row] : 0.0f;
-    const float lb = row_ok ? a.lse[row] * kLog2e : 0.0f;
-    const float xs = row_ok ? kLog2e / row_tau(a.T, row) : kLog2e;   // log2(e) / tau_n
+    const bool live = ca != 0.0f;
+    const float lb = live ? a.lse[row] * kLog2e : __builtin_inff();
+    const float xs = live ? kLog2e / row_tau(a.T, row) : 0.0f;   // log2(e) / tau_n
     // a_n exp(z - lse_n) in the accumulators, by all four waves at once: each
     // lane holds 32 rows (4 per block row), whose constants thread t, row t,
     // shares through the LDS past the staging area (the K loop is done with it)
@@ -547,7 +559,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
         K3[kTile + tid] = lb;
         K3[2 * kTile + tid] = xs;
         __syncthreads();
+        // exp2(z / tau_n log2 e - lse_n log2 e) <= 1 up to rounding (lse_n >=
+        // z / tau_n): every product is finite. Only columns past the
+        // vocabulary (the last tile of the last chunk) are masked.
         const int64_t cb = n0 + wc * 128 + (lane & 15);   // chunk-local column of block 0
+        const bool full = n0 + kTile <= width;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int r0 = wr * 128 + i * 16 + 4 * (lane >> 4);
@@ -556,13 +572,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
             const floatx4 xs4 = *reinterpret_cast<const floatx4*>(K3 + 2 * kTile + r0);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const bool col_ok = cb + 16 * j < width;
                 floatx4 v = acc[i][j];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float g = ca4[e] * exp2_fast(__builtin_fmaf(v[e], xs4[e], -lb4[e]));
-                    v[e] = (ca4[e] != 0.0f && col_ok) ? g : 0.0f;
-                }
+                for (int e = 0; e < 4; ++e) v[e] = ca4[e] * exp2_fast(__builtin_fmaf(v[e], xs4[e], -lb4[e]));
+                if (!full && cb + 16 * j >= width) v = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
                 acc[i][j] = v;
             }
         }
