@@ -87,8 +87,8 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t count, uint32_t value) {
 // built before the launch (hit_count_kernel, hit_fill_kernel): a row has about
 // k * 256 / V hits per tile, so scanning every id in every tile cost more
 // than the hits themselves.
-__device__ __forceinline__ bool id_in_tile(const int32_t* idr, uint32_t col0, int ncol, int& j) {
-    const uint32_t d = (uint32_t)idr[0] - col0;
+__device__ __forceinline__ bool id_in_tile(int32_t id, uint32_t col0, int ncol, int& j) {
+    const uint32_t d = (uint32_t)id - col0;
     j = (int)d;
     return d < (uint32_t)ncol;
 }
@@ -200,9 +200,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTilesArgs a) 
     const int wr = wave >> 1, wc = wave & 1;
     const int64_t row = m0 + tid;
     const bool row_ok = row < a.n;
+    // The row's label (used when k = 1) and temperature, loaded together
+    // before the first half and unconditionally, from row n - 1 for rows past
+    // n (not used there): loads under a per-row condition each ended in a
+    // branch join where the compiler waited for every memory operation in
+    // flight.
+    const int64_t rc = row_ok ? row : a.n - 1;
+    const int32_t lid = a.ids[a.k == 1 ? rc : rc * a.k];
     // logits / tau_n (the scale is exactly 1 without a temperature, and the
     // multiply is then skipped: x * 1 = x)
-    const float inv_tau = row_ok ? 1.0f / row_tau(a.T, row) : 1.0f;
+    const float inv_tau = row_ok ? 1.0f / row_tau(a.T, rc) : 1.0f;
     const bool unit_tau = a.T.row == nullptr && a.T.t == 1.0f;
     float* Sr = S + tid;
     float run_m = neg_inf(), run_s = 0.0f;
@@ -246,8 +253,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTilesArgs a) 
         }
         if (a.k == 1) {
             int j;
-            if (row_ok && id_in_tile(a.ids + row, (uint32_t)col0, ncol, j))
-                a.zg[row] = Sr[j * kEpiStride] * inv_tau;
+            if (row_ok && id_in_tile(lid, (uint32_t)col0, ncol, j)) a.zg[row] = Sr[j * kEpiStride] * inv_tau;
         } else {
             // the tile's hits from its bucket, one thread per entry: every
             // (row, slot) has one entry, so each zg element has one writer
@@ -545,10 +551,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
     // temperature, whose lse or tau may be NaN, 0 or inf) gets the scale 0 and
     // the offset +inf, so its exp2 is exactly 0 for any finite logit; the
     // other rows compute a_n exp2(z log2(e) / tau_n - lse_n log2(e)).
-    const float ca = row_ok ? a.coef_a[row] : 0.0f;
-    const bool live = ca != 0.0f;
-    const float lb = live ? a.lse[row] * kLog2e : __builtin_inff();
-    const float xs = live ? kLog2e / row_tau(a.T, row) : 0.0f;   // log2(e) / tau_n
+    // The row's values are loaded together and unconditionally (coef_a covers
+    // the n_pad rows; the others are read at row n - 1 for rows past n and
+    // not used): loads under a per-row condition each ended in a branch join
+    // where the compiler waited for every memory operation in flight.
+    const int64_t rc = row_ok ? row : a.n - 1;
+    const float ca = a.coef_a[row];
+    const float lse_r = a.lse[rc];
+    const float tau_r = row_tau(a.T, rc);
+    const int32_t lid = a.ids[a.k == 1 ? rc : rc * a.k];
+    const float cc = a.coef_c[a.k == 1 ? rc : rc * a.k];
+    const bool live = row_ok && ca != 0.0f;
+    const float lb = live ? lse_r * kLog2e : __builtin_inff();
+    const float xs = live ? kLog2e / tau_r : 0.0f;   // log2(e) / tau_n
     // a_n exp(z - lse_n) in the accumulators, by all four waves at once: each
     // lane holds 32 rows (4 per block row), whose constants thread t, row t,
     // shares through the LDS past the staging area (the K loop is done with it)
@@ -591,8 +606,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
         // c_nk at the row's ids in the tile, in ascending k
         if (a.k == 1) {
             int j;
-            if (row_ok && id_in_tile(a.ids + row, (uint32_t)(v0 + col0), ncol, j))
-                Sr[j * kEpiStride] += a.coef_c[row];
+            if (row_ok && id_in_tile(lid, (uint32_t)(v0 + col0), ncol, j)) Sr[j * kEpiStride] += cc;
         } else {
             // the tile's bucket lists its hits by row, column, slot: the first
             // entry of each (row, column) run adds the run's c_nk in ascending
@@ -688,12 +702,16 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int64_t bid, char* smem
     const int wr = wave >> 1, wc = wave & 1;
     const int64_t h0 = m0 + wr * 128 + 4 * (lane >> 4);    // hidden position of block row 0
     const int64_t c0 = n0 + wc * 128 + (lane & 15);        // chunk column of block column 0
+    // The two forms are separate loops: with the (uniform) test inside the
+    // column loop, every column block ended in a join with the accumulating
+    // form's loads, and the compiler waited there for every memory operation
+    // in flight, this tile's earlier stores included.
+    if (a.dw_acc == nullptr) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int64_t v = c0 + 16 * j;
-        if (v >= width) continue;
-        const int64_t orow = (v0 + v) * a.hidden;
-        if (a.dw_acc == nullptr) {
+        for (int j = 0; j < 8; ++j) {
+            const int64_t v = c0 + 16 * j;
+            if (v >= width) continue;
+            const int64_t orow = (v0 + v) * a.hidden;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int64_t h = h0 + 16 * i;   // hidden is a multiple of 64: all four or none
@@ -701,26 +719,32 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int64_t bid, char* smem
                     *reinterpret_cast<uint2*>(a.dW + orow + h) =
                         make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
             }
-        } else {
-            float4 p[8];
+        }
+        return;
+    }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int64_t h = h0 + 16 * i;
-                p[i] = *reinterpret_cast<const float4*>(a.dw_acc + orow + (h < a.hidden ? h : 0));
-            }
+    for (int j = 0; j < 8; ++j) {
+        const int64_t v = c0 + 16 * j;
+        if (v >= width) continue;
+        const int64_t orow = (v0 + v) * a.hidden;
+        float4 p[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int64_t h = h0 + 16 * i;
-                if (h >= a.hidden) continue;
-                float4 y;
-                y.x = p[i].x + acc[i][j][0];
-                y.y = p[i].y + acc[i][j][1];
-                y.z = p[i].z + acc[i][j][2];
-                y.w = p[i].w + acc[i][j][3];
-                *reinterpret_cast<float4*>(a.dw_acc + orow + h) = y;
-                if (a.dW != nullptr)
-                    *reinterpret_cast<uint2*>(a.dW + orow + h) = make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
-            }
+        for (int i = 0; i < 8; ++i) {
+            const int64_t h = h0 + 16 * i;
+            p[i] = *reinterpret_cast<const float4*>(a.dw_acc + orow + (h < a.hidden ? h : 0));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t h = h0 + 16 * i;
+            if (h >= a.hidden) continue;
+            float4 y;
+            y.x = p[i].x + acc[i][j][0];
+            y.y = p[i].y + acc[i][j][1];
+            y.z = p[i].z + acc[i][j][2];
+            y.w = p[i].w + acc[i][j][3];
+            *reinterpret_cast<float4*>(a.dw_acc + orow + h) = y;
+            if (a.dW != nullptr)
+                *reinterpret_cast<uint2*>(a.dW + orow + h) = make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
         }
     }
 }
