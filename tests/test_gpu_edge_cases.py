@@ -1,7 +1,7 @@
 """More edge cases of the method against the fp64 oracle: a single support
 candidate per row, a vocabulary below one tile with padded candidate lists, a
-one-column last chunk, every row sharing one label, and the caller
-accumulators with a temperature."""
+one-column last chunk, the widest accepted chunk, every row sharing one
+label, and the caller accumulators with a temperature."""
 import numpy as np
 import pytest
 import torch
@@ -64,6 +64,21 @@ def test_one_column_last_chunk(entry):
     got = run_entry(Dev(inp), entry, 256)
     torch.cuda.synchronize()
     _check(entry, got, _ref(entry, inp))
+
+
+def test_widest_chunk():
+    """The widest chunk the shape check accepts, round_up(min(chunk, V), 256) =
+    2^22 - 256 = 4,194,048 columns (V 300 columns wider: a second, 300-wide
+    chunk follows). dL/dz is read with that row pitch, and a 256-row tile of
+    it spans 2,147,352,576 bytes, just under the 2^31-byte buffer range the
+    bound protects. n = 16: the bound depends on the pitch and the 256-row
+    tile only."""
+    cap = (1 << 22) - 256
+    inp = wlmod.make_inputs(wlmod.custom(n=16, hidden=64, vocab=cap + 300, chunk=cap, seed=1606,
+                                         ignore_frac=0.1))
+    got = run_entry(Dev(inp), lm.ENTRY_CE_MEAN, cap)
+    torch.cuda.synchronize()
+    _check(lm.ENTRY_CE_MEAN, got, _ref(lm.ENTRY_CE_MEAN, inp))
 
 
 def test_every_row_has_the_same_label():
