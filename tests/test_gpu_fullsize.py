@@ -95,14 +95,15 @@ def test_fullsize_ce_consistency_and_determinism(name):
     assert torch.all(col_sum <= 1e-2 * col_abs + 1e-12), float((col_sum / col_abs).max())
 
 
-@pytest.mark.parametrize("name", ["headline", "support", "logprob", "mid"])
+@pytest.mark.parametrize("name", ["headline", "support", "logprob", "mid", "small"])
 def test_fullsize_dw_on_row_subset(name):
     """Same shapes and chunk; all but 16 rows carry no gradient, so dW is a sum
     over 16 rows and the oracle forms sampled dW rows exactly. CE (headline,
-    mid): every other row is ignored; log-prob and support: every other row's
-    upstream gradient is 0 (its labels / candidates stay in place). The
+    mid, small): every other row is ignored; log-prob and support: every other
+    row's upstream gradient is 0 (its labels / candidates stay in place). The
     log-prob workload's dW contraction runs 64 K steps over 16,384 rows, the
-    longest of any workload."""
+    longest of any workload; the small one (256 rows) takes eight chunks'
+    dL/dz per recompute and their dW in one launch."""
     wl = wlmod.WORKLOADS[name]
     inp = _inputs(name)
     rng = np.random.default_rng(wl.seed + 23)
