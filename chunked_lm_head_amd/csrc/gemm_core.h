@@ -74,7 +74,6 @@ __device__ __forceinline__ void map_tile(int64_t bid, int64_t tiles_m, int64_t t
 // bank slots: chunk q of row r is stored at position q ^ ((r >> 1) & 7).
 __device__ __forceinline__ int swizzle(int row) { return (row >> 1) & 7; }
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // The accumulators: each wave's 128 x 128 sub-tile as 8 x 8 blocks of
 // v_mfma_f32_16x16x32_bf16 (block (i, j) covers rows wr*128 + 16 i .. +16 and
@@ -194,6 +193,18 @@ __host__ __device__ constexpr int pslot(int l) { return l ^ (((l >> 4) & 1) << 2
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// The four B stages of the ring, as four LDS pointers. The MN-major layouts
+// (kBRow, kBFrag) are loaded with the LDS-writing buffer-load builtin into
+// four separate LDS arrays: the compiler then proves that a transposing read
+// of stage ST (an intrinsic) does not touch the stages the loads in flight
+// write, instead of draining every load before each read, and it counts
+// those loads in its own waits for the A fragments (loads it cannot see would
+// make those waits stricter than the schedule needs). kBK kernels pass one
+// buffer cut into four stages; their plain LDS reads never needed this.
+struct StageSet {
+    char* p[4];
+};
+
 struct DaA {
     const char* base;   // kATile: the tile's first block; kAStep: the tile's first block of K step 0
     int64_t kblk;       // kATile: bytes per 16-row block (K / 32 KB); kAStep: bytes per K block (M / 16 KB)
@@ -216,7 +227,7 @@ struct DaCtx {
     __amdgpu_buffer_rsrc_t rb;    // kBK only
     uint32_t vb[2];               // lane offsets in B (kBK: even / odd chunk u)
     int64_t KT;
-    char* smem;
+    StageSet st;
     int wave, lane;
 };
 
@@ -237,44 +248,11 @@ __device__ __forceinline__ bf16x8 da_a(const DaCtx& c, __amdgpu_buffer_rsrc_t r,
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, c.va, soff, 0));
 }
 
-// One LDS-writing buffer load issued from assembly: each lane's 16 bytes at
-// rsrc + voff + soff go to LDS at m0 + 16 lane. The MN-major layouts load B
-// this way: with the compiler's LDS-writing builtin the compiler cannot tell
-// the transposing LDS reads (an intrinsic) from the loads in flight and
-// drains every load before each read. The instruction has no register
-// output; its completion is covered by the explicit vmcnt waits at the stage
-// barrier and before the epilogue, which count every load in issue order.
-// The descriptor is built by hand: base address, the range in bytes, and the
-// same format word as __builtin_amdgcn_make_buffer_rsrc(..., 0x00020000).
-__device__ __forceinline__ u32x4_t rsrc_words(const void* base, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    u32x4_t r;
-    r[0] = (uint32_t)a;
-    r[1] = (uint32_t)(a >> 32) & 0xffffu;
-    r[2] = bytes;
-    r[3] = 0x00020000u;
-    return r;
-}
-// m0 (a register the compiler reserves) is saved and restored around the
-// load, and one wait state separates the write of m0 from the load that
-// reads it (the compiler keeps the same distance before its own LDS-writing
-// loads).
-__device__ __forceinline__ void dma16(const u32x4_t& rsrc, uint32_t voff, uint32_t soff, const char* lds) {
-    const uint32_t m0v = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)lds);
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\ts_nop 0\n\t"
-        "buffer_load_dwordx4 %1, %2, %3 offen lds\n\ts_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(voff), "s"(rsrc), "s"(soff), "s"(m0v)
-        : "memory");
-}
-
 // B load u (0..7) of a wave for K step kt into stage ST.
 template <int BL, int ST>
 __device__ __forceinline__ void da_b(const DaCtx& c, int64_t kt, int u) {
     const int64_t ktc = kt < c.KT ? kt : c.KT - 1;
-    char* stage = c.smem + ST * da_stage_bytes(BL);
+    char* stage = c.st.p[ST];
     if (BL == kBK) {
         // LDS rows 64 w + 8 u .. + 8 in lane order; lane p loads the chunk that
         // belongs at its position
@@ -288,13 +266,17 @@ __device__ __forceinline__ void da_b(const DaCtx& c, int64_t kt, int u) {
         const int64_t k0 = ktc * kTileK;
         int64_t left = c.B.rows - k0;
         left = left < 0 ? 0 : (left > kTileK ? kTileK : left);
-        const u32x4_t r = rsrc_words(c.B.base + k0 * c.B.ld * 2, (uint32_t)(left * c.B.ld * 2));
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(c.B.base + k0 * c.B.ld * 2), 0, (int)(left * c.B.ld * 2), 0x00020000);
         const int r1 = c.wave * 16 + (u & 3) + 8 * (u >> 2);
-        dma16(r, c.vb[0], (uint32_t)(r1 * c.B.ld * 2), stage + (c.wave * 8 + u) * kRowBlock);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(stage + (c.wave * 8 + u) * kRowBlock), 16,
+                                                 c.vb[0], (uint32_t)(r1 * c.B.ld * 2), 0, 0);
     } else {
         // block (4 kt + w, u) of the tile's columns, 1 KB verbatim
-        const u32x4_t r = rsrc_words(c.B.base + 4 * ktc * c.B.ld, (uint32_t)(4 * c.B.ld));
-        dma16(r, c.vb[0], (uint32_t)(c.wave * c.B.ld + u * 1024), stage + (c.wave * 8 + u) * 1024);
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(c.B.base + 4 * ktc * c.B.ld), 0, (int)(4 * c.B.ld), 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(stage + (c.wave * 8 + u) * 1024), 16, c.vb[0],
+                                                 (uint32_t)(c.wave * c.B.ld + u * 1024), 0, 0);
     }
 }
 
@@ -320,9 +302,8 @@ template <int AM, int BL, int ST>
 __device__ __forceinline__ void da_step(const DaCtx& c, int64_t kt, AccTile& acc, bf16x8 (&fa)[2][2][8],
                                         bf16x8 (&fb)[8], uint32_t blo, uint32_t bhi) {
     constexpr int P = ST & 1;
-    constexpr int SB = da_stage_bytes(BL);
-    const char* cur = c.smem + ST * SB;
-    const char* nxt = c.smem + ((ST + 1) & 3) * SB;
+    const char* cur = c.st.p[ST];
+    const char* nxt = c.st.p[(ST + 1) & 3];
     const int br = (c.wave & 1) * 128;
     const __amdgpu_buffer_rsrc_t ra2 = da_a_rsrc<AM>(c, kt + 2);
 #pragma unroll
@@ -368,13 +349,14 @@ __device__ __forceinline__ void da_step(const DaCtx& c, int64_t kt, AccTile& acc
 // substep in the same MFMA slot, so each output element is one fixed-order
 // sum over ascending K.
 template <int AM, int BL>
-__device__ __forceinline__ void gemm_mainloop_da(const DaA& A, const DaB& B, int64_t K, char* smem, AccTile& acc) {
+__device__ __forceinline__ void gemm_mainloop_da(const DaA& A, const DaB& B, int64_t K, const StageSet& st,
+                                                 AccTile& acc) {
     const int tid = threadIdx.x;
     DaCtx c;
     c.A = A;
     c.B = B;
     c.KT = K / kTileK;
-    c.smem = smem;
+    c.st = st;
     c.lane = tid & 63;
     c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = c.wave >> 1;
@@ -445,7 +427,7 @@ __device__ __forceinline__ void gemm_mainloop_da(const DaA& A, const DaB& B, int
     bf16x8 fb[8];
     const int br = (c.wave & 1) * 128;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[j] = da_bfrag<BL>(smem, c, blo, bhi, br, j, 0);
+    for (int j = 0; j < 4; ++j) fb[j] = da_bfrag<BL>(c.st.p[0], c, blo, bhi, br, j, 0);
     int64_t kt = 0;
     for (; kt + 3 < c.KT; kt += 4) {
         da_step<AM, BL, 0>(c, kt, acc, fa, fb, blo, bhi);
@@ -460,6 +442,15 @@ __device__ __forceinline__ void gemm_mainloop_da(const DaA& A, const DaB& B, int
     // every load (the clamped ones past the last step included) has landed
     // before the epilogue reuses the LDS
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The same with the four stages cut from one LDS buffer (the K-major layout).
+template <int AM, int BL>
+__device__ __forceinline__ void gemm_mainloop_da(const DaA& A, const DaB& B, int64_t K, char* smem, AccTile& acc) {
+    static_assert(BL == kBK, "the MN-major layouts take four separate stage arrays");
+    constexpr int SB = da_stage_bytes(BL);
+    const StageSet st{{smem, smem + SB, smem + 2 * SB, smem + 3 * SB}};
+    gemm_mainloop_da<AM, BL>(A, B, K, st, acc);
 }
 
 // Write the accumulators of the waves whose column half is `half` into the
@@ -480,17 +471,26 @@ __device__ __forceinline__ void stage_half(float* S, const AccTile& acc, int wr,
 // kRowStride floats (4 mod 64 banks: the four row groups one 32-bit store
 // instruction writes, 4 rows apart, fall 16 banks apart). Afterwards 32 lanes
 // can read one row's 128 values as float4s, conflict-free, for coalesced
-// row-major global traffic.
-__device__ __forceinline__ void stage_half_rows(float* S, const AccTile& acc, int wr, int lane) {
+// row-major global traffic. The rows are spread over the four stage arrays of
+// the K loop, 64 rows each (64 x kRowStride x 4 bytes = one kBRow stage):
+// rows 64 q .. 64 q + 63 in array q, so wave w later reads its own rows
+// 64 w .. + 63 from array w alone.
+static_assert(64 * kRowStride * 4 <= kDaStageMax, "64 staged rows must fit one stage array");
+__device__ __forceinline__ float* stage_rows(const StageSet& st, int q) {
+    return reinterpret_cast<float*>(q == 0 ? st.p[0] : q == 1 ? st.p[1] : q == 2 ? st.p[2] : st.p[3]);
+}
+__device__ __forceinline__ void stage_half_rows(const StageSet& st, const AccTile& acc, int wr, int lane) {
+    float* const lo = stage_rows(st, 2 * wr);       // rows wr * 128 + 0 .. 63
+    float* const hi = stage_rows(st, 2 * wr + 1);   // rows wr * 128 + 64 .. 127
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int row = wr * 128 + i * 16 + 4 * (lane >> 4) + e;
+                const int row = (i & 3) * 16 + 4 * (lane >> 4) + e;   // within its 64-row array
                 const int col = j * 16 + (lane & 15);
-                S[row * kRowStride + col] = acc[i][j][e];
+                (i < 4 ? lo : hi)[row * kRowStride + col] = acc[i][j][e];
             }
 }
 

@@ -673,7 +673,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
 // to it (dw_acc +=), and the bf16 output, if any, is the cast of the updated
 // accumulator. The launch's column tiles run over the group's chunks side
 // by side; a narrower last chunk leaves its excess workgroups idle.
-__device__ __forceinline__ void dw_tile(const DwArgs& a, int64_t bid, char* smem) {
+__device__ __forceinline__ void dw_tile(const DwArgs& a, int64_t bid, const StageSet& st) {
     int64_t tm, tg;
     map_tile(bid, a.tiles_m, a.tiles_n * a.group, tm, tg);
     const int64_t g = tg / a.tiles_n, tn = tg - g * a.tiles_n;
@@ -693,7 +693,7 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int64_t bid, char* smem
     B.rows = 0;
     B.n0 = 0;
     AccTile acc;
-    gemm_mainloop_da<kAStep, kBFrag>(A, B, a.n_pad, smem, acc);
+    gemm_mainloop_da<kAStep, kBFrag>(A, B, a.n_pad, st, acc);
     // Lane l of block (i, j) holds hidden positions 4 (l / 16) .. + 4 of chunk
     // column l % 16: four consecutive elements of one dW row, stored straight
     // from the accumulators (8 bytes of bf16; with a caller accumulator 16
@@ -774,20 +774,20 @@ __device__ __forceinline__ DaB wc_rows(const DhArgs& a, int64_t n0, int64_t k0) 
 // chunk's columns; the fp32 running sum over chunks (chunk order) lives in
 // dh_acc and the last chunk writes the bf16 result. A caller accumulator is
 // dh_acc itself: read from chunk 0 on and stored after the last chunk too.
-__device__ __forceinline__ void dh_tile(const DhArgs& a, int64_t bid, char* smem) {
+__device__ __forceinline__ void dh_tile(const DhArgs& a, int64_t bid, const StageSet& st) {
     int64_t tm, tn;
     map_tile(bid, a.tiles_m, a.tiles_n, tm, tn);
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
     AccTile acc;
-    gemm_mainloop_da<kATile, kBRow>(g_tile(a, m0, 0), wc_rows(a, n0, 0), a.w_pad, smem, acc);
-    float* S = reinterpret_cast<float*>(smem);
+    gemm_mainloop_da<kATile, kBRow>(g_tile(a, m0, 0), wc_rows(a, n0, 0), a.w_pad, st, acc);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
+    const float* Sw = stage_rows(st, wave);   // this wave's 64 staged rows
     // 32 lanes per row (4 columns each), two rows per wave and step: the fp32
     // read-modify-write of dh_acc is coalesced
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
-        if (wc == half) stage_half_rows(S, acc, wr, lane);
+        if (wc == half) stage_half_rows(st, acc, wr, lane);
         __syncthreads();
         const int c = 4 * (lane & 31);
         const int64_t h = n0 + half * 128 + c;
@@ -814,7 +814,7 @@ __device__ __forceinline__ void dh_tile(const DhArgs& a, int64_t bid, char* smem
                 const int r = wave * 64 + (i0 + u) * 2 + (lane >> 5);
                 const int64_t row = m0 + r;
                 if (row >= a.n || !hok) continue;
-                float4 v = *reinterpret_cast<const float4*>(S + r * kRowStride + c);
+                float4 v = *reinterpret_cast<const float4*>(Sw + (r - wave * 64) * kRowStride + c);
                 const int64_t o = row * a.hidden + h;
                 if (!a.first) {
                     v.x = p[u].x + v.x;
@@ -831,14 +831,23 @@ __device__ __forceinline__ void dh_tile(const DhArgs& a, int64_t bid, char* smem
     }
 }
 
+// The MN-major kernels take their B stages as four separate LDS arrays (see
+// StageSet).
+#define LMHEAD_STAGE_ARRAYS                                         \
+    __shared__ __attribute__((aligned(16))) char lds0[kDaStageMax]; \
+    __shared__ __attribute__((aligned(16))) char lds1[kDaStageMax]; \
+    __shared__ __attribute__((aligned(16))) char lds2[kDaStageMax]; \
+    __shared__ __attribute__((aligned(16))) char lds3[kDaStageMax]; \
+    const StageSet st{{lds0, lds1, lds2, lds3}}
+
 __global__ __launch_bounds__(kThreads, 1) void bwd_dw_kernel(DwArgs a) {
-    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
-    dw_tile(a, blockIdx.x, smem);
+    LMHEAD_STAGE_ARRAYS;
+    dw_tile(a, blockIdx.x, st);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(DhArgs a) {
-    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
-    dh_tile(a, blockIdx.x, smem);
+    LMHEAD_STAGE_ARRAYS;
+    dh_tile(a, blockIdx.x, st);
 }
 
 // The dW and dH tiles of one chunk in one launch: the first `first_count`
@@ -847,13 +856,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(DhArgs a) {
 // the results do not depend on which launch runs it; the host picks this form
 // when one launch leaves compute units idle that the other kind can fill.
 __global__ __launch_bounds__(kThreads, 1) void bwd_dwdh_kernel(DwArgs dw, DhArgs dh, int dh_first) {
-    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+    LMHEAD_STAGE_ARRAYS;
     const int64_t bid = blockIdx.x;
     const int64_t n_first = dh_first ? dh.tiles_m * dh.tiles_n : dw.tiles_m * dw.tiles_n;
     const bool take_dh = dh_first ? bid < n_first : bid >= n_first;
     const int64_t local = bid < n_first ? bid : bid - n_first;
-    if (take_dh) dh_tile(dh, local, smem);
-    else dw_tile(dw, local, smem);
+    if (take_dh) dh_tile(dh, local, st);
+    else dw_tile(dw, local, st);
 }
 
 // Few row tiles (small batches): the dH tiles of one or more chunks are
@@ -872,7 +881,7 @@ __device__ __forceinline__ DhArgs split_chunk(const DhArgs& a, const DhSplit& q,
 }
 
 __global__ __launch_bounds__(kThreads, 1) void bwd_dh_split_kernel(DhArgs a, DhSplit q, float* partial) {
-    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+    LMHEAD_STAGE_ARRAYS;
     const int64_t tiles = a.tiles_m * a.tiles_n;
     const int64_t u = blockIdx.x / tiles;   // chunk * slices + slice
     const int64_t g = u / q.slices, sl = u - g * q.slices;
@@ -884,14 +893,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_split_kernel(DhArgs a, DhS
     map_tile(blockIdx.x - u * tiles, a.tiles_m, a.tiles_n, tm, tn);
     const int64_t m0 = tm * kTile, n0 = tn * kTile;
     AccTile acc;
-    gemm_mainloop_da<kATile, kBRow>(g_tile(c, m0, k0), wc_rows(c, n0, k0), klen, smem, acc);
-    float* S = reinterpret_cast<float*>(smem);
+    gemm_mainloop_da<kATile, kBRow>(g_tile(c, m0, k0), wc_rows(c, n0, k0), klen, st, acc);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
+    const float* Sw = stage_rows(st, wave);   // this wave's 64 staged rows
     float* out = partial + u * a.n * a.hidden;
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
-        if (wc == half) stage_half_rows(S, acc, wr, lane);
+        if (wc == half) stage_half_rows(st, acc, wr, lane);
         __syncthreads();
         const int c4 = 4 * (lane & 31);
         const int64_t h = n0 + half * 128 + c4;
@@ -902,7 +911,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_split_kernel(DhArgs a, DhS
                 const int64_t row = m0 + r;
                 if (row < a.n)
                     *reinterpret_cast<float4*>(out + row * a.hidden + h) =
-                        *reinterpret_cast<const float4*>(S + r * kRowStride + c4);
+                        *reinterpret_cast<const float4*>(Sw + (r - wave * 64) * kRowStride + c4);
             }
         }
         __syncthreads();
