@@ -186,8 +186,9 @@ typedef struct lmhead_memory_figures {
                                     (loss / logp / lp, kl, lse), plus bf16 dH and dW
                                     with the backward */
     size_t dh_split_bytes;       /* backward, few row tiles only (else 0): fp32 partial
-                                    dH of the K slices a chunk's dH contraction is cut
-                                    into, joined in slice order */
+                                    dH of the (chunk, K slice) units of the dH
+                                    contraction, joined in order; sized by n and hidden
+                                    alone (at most 16 planes of n x hidden) */
     size_t operand_copy_bytes;   /* (not the KL-only entry) H in MFMA fragment order,
                                     bf16 [n rounded up to 256, hidden]; the backward adds
                                     H^T in fragment order, [n, hidden rounded up to 256] */
@@ -207,10 +208,10 @@ int lmhead_memory_report(const lmhead_problem* p, int entry, int with_backward,
  * among those, the smallest chunk (a multiple of 256), which spreads the
  * vocabulary evenly over the passes. Writes it to *chunk. Returns
  * LMHEAD_ERR_WORKSPACE if even a 256-wide chunk does not fit. The chunk
- * returned always fits. With few row tiles (small batches) the workspace
- * holds the fp32 partials of the dH K-split, whose slice count follows the
- * chunk's width and can fall as the chunk grows; there the choice is the
- * bisection's (a fitting chunk, not always the one with the fewest passes).
+ * returned always fits. The backward workspace never shrinks as the chunk
+ * widens (the dL/dz region grows with it; the small-batch dH partials are
+ * sized by n and hidden alone), so a 256-wide chunk is the floor and the
+ * search over chunk widths is exact.
  */
 int lmhead_plan_chunk(const lmhead_problem* p, int entry, size_t budget_bytes, int64_t* chunk);
 
