@@ -278,14 +278,17 @@ int64_t list_time(int64_t n1, int64_t s1, int64_t n2, int64_t s2) {
 }
 
 // 1: one launch with the dH tiles first, 0: one launch with the dW tiles
-// first, -1: two launches. One launch only when it saves at least 5 %.
+// first, -1: two launches. One launch unless the estimate makes it longer:
+// at a tie (both kinds filling whole rounds) it still saves a launch
+// boundary, and the second kind's tiles start on the units the first kind's
+// last round frees.
 int dwdh_plan(int64_t n_dw, int64_t k_dw, int64_t n_dh, int64_t k_dh) {
     // with many rounds the last one's idle units matter little: keep two launches
     if (n_dw == 0 || n_dh == 0 || n_dw + n_dh > 16 * kComputeUnits) return -1;
     const int64_t apart = rounds_time(n_dw, k_dw) + rounds_time(n_dh, k_dh);
     const bool dh_first = k_dh >= k_dw;   // longer tiles first
     const int64_t together = dh_first ? list_time(n_dh, k_dh, n_dw, k_dw) : list_time(n_dw, k_dw, n_dh, k_dh);
-    return together * 20 <= apart * 19 ? (dh_first ? 1 : 0) : -1;
+    return together <= apart ? (dh_first ? 1 : 0) : -1;
 }
 
 // fp32 partial dH planes of the K-split (below 2: no split): one per (chunk,
