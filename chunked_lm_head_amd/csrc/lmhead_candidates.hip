@@ -113,17 +113,37 @@ __global__ __launch_bounds__(kThreads) void cand_kl_fwd_kernel(CandFwdArgs a) {
     float* z = zs[wave];
     for (int k0 = 0; k0 < k; k0 += 4) {
         float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        int32_t id[4];
+        // W rows of the four candidates; a padding slot (or one past k)
+        // reads row 0 and its z is never used (every use below checks the
+        // id), so the five loads of a segment are unconditional and in
+        // flight together instead of each waiting behind a branch join
+        const bf16_bits* wr[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) id[c] = k0 + c < k ? idr[k0 + c] : -1;
-        for (int64_t h = lane * 8; h < a.hidden; h += kSeg) {
+        for (int c = 0; c < 4; ++c) {
+            const int32_t id = k0 + c < k ? idr[k0 + c] : -1;
+            wr[c] = a.W + (int64_t)(id >= 0 ? id : 0) * a.hidden;
+        }
+        // two segments' ten loads at a time, then their products in
+        // ascending segment order (the same sums as one segment at a time)
+        int64_t h = lane * 8;
+        for (; h + kSeg < a.hidden; h += 2 * kSeg) {
+            const uint4 hv0 = *reinterpret_cast<const uint4*>(hrow + h);
+            const uint4 hv1 = *reinterpret_cast<const uint4*>(hrow + h + kSeg);
+            uint4 w0[4], w1[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) w0[c] = *reinterpret_cast<const uint4*>(wr[c] + h);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) w1[c] = *reinterpret_cast<const uint4*>(wr[c] + h + kSeg);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) part[c] = dot8(hv1, w1[c], dot8(hv0, w0[c], part[c]));
+        }
+        if (h < a.hidden) {
             const uint4 hv = *reinterpret_cast<const uint4*>(hrow + h);
+            uint4 wv[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (id[c] >= 0) {
-                    const uint4 wv = *reinterpret_cast<const uint4*>(a.W + (int64_t)id[c] * a.hidden + h);
-                    part[c] = dot8(hv, wv, part[c]);
-                }
+            for (int c = 0; c < 4; ++c) wv[c] = *reinterpret_cast<const uint4*>(wr[c] + h);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) part[c] = dot8(hv, wv[c], part[c]);
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -165,11 +185,27 @@ __global__ __launch_bounds__(kThreads) void cand_dh_kernel(CandBwdArgs a) {
     const float* cr = a.coef_c + row * a.k;
     for (int64_t h = lane * 8; h < a.hidden; h += kSeg) {
         float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-        for (int kk = 0; kk < a.k; ++kk) {
-            const int32_t id = idr[kk];
-            const float c = cr[kk];
-            if (id < 0 || id >= a.vocab || c == 0.0f) continue;
-            fma8(acc, c, *reinterpret_cast<const uint4*>(a.W + (int64_t)id * a.hidden + h));
+        // four candidates at a time: their W rows are loaded together and
+        // unconditionally (a padding slot or a past-k one reads row 0), and
+        // only the products are skipped, so the sum keeps its terms and order
+        for (int k0 = 0; k0 < a.k; k0 += 4) {
+            int32_t id[4];
+            float c[4];
+            uint4 wv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int kk = k0 + u < a.k ? k0 + u : a.k - 1;
+                id[u] = k0 + u < a.k ? idr[kk] : -1;
+                c[u] = cr[kk];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t r = id[u] >= 0 && id[u] < a.vocab ? id[u] : 0;
+                wv[u] = *reinterpret_cast<const uint4*>(a.W + r * a.hidden + h);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (id[u] >= 0 && id[u] < a.vocab && c[u] != 0.0f) fma8(acc, c[u], wv[u]);
         }
         store_row8(acc, a.dH_acc != nullptr ? a.dH_acc + row * a.hidden + h : nullptr,
                    a.dH != nullptr ? a.dH + row * a.hidden + h : nullptr);
@@ -519,12 +555,22 @@ __global__ __launch_bounds__(kThreads) void cand_dw_kernel(CandBwdArgs a) {
     if (e - b > kSmallBucket) return;
     for (int64_t h = lane * 8; h < a.hidden; h += kSeg) {
         float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-        for (int32_t j = b; j < e; ++j) {
-            const int32_t i = a.list[j];
-            const float c = a.coef_c[i];
-            if (c == 0.0f) continue;
-            const int64_t n = i / a.k;
-            fma8(acc, c, *reinterpret_cast<const uint4*>(a.H + n * a.hidden + h));
+        // four entries at a time, their loads together (entries past the
+        // bucket repeat its last one and are not added), products in order
+        for (int32_t j0 = b; j0 < e; j0 += 4) {
+            int32_t i[4];
+            float c[4];
+            uint4 hv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) i[u] = a.list[j0 + u < e ? j0 + u : e - 1];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) c[u] = a.coef_c[i[u]];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                hv[u] = *reinterpret_cast<const uint4*>(a.H + (int64_t)(i[u] / a.k) * a.hidden + h);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (j0 + u < e && c[u] != 0.0f) fma8(acc, c[u], hv[u]);
         }
         store_row8(acc, a.dW_acc != nullptr ? a.dW_acc + v * a.hidden + h : nullptr,
                    a.dW != nullptr ? a.dW + v * a.hidden + h : nullptr);
