@@ -19,6 +19,7 @@ namespace {
 
 constexpr int kWaves = kThreads / 64;   // rows (or vocabulary rows) per workgroup
 constexpr int kSeg = 512;               // hidden elements one wave covers per step (8 per lane)
+constexpr int kHoldSeg = 8;             // segments of an H row the KL forward keeps in registers
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -84,6 +85,30 @@ __device__ __forceinline__ void store_row8(float (&acc)[8], float* acc_row, bf16
                        pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
 }
 
+// W rows of candidates k0 .. k0 + 3 of a row. A padding slot (or one past k)
+// reads row 0 and its z is never used (every use checks the id), so the loads
+// of a segment are unconditional and in flight together instead of each
+// waiting behind a branch join.
+__device__ __forceinline__ void cand_rows4(const CandFwdArgs& a, const int32_t* idr, int k0,
+                                           const bf16_bits* (&wr)[4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int32_t id = k0 + c < a.k ? idr[k0 + c] : -1;
+        wr[c] = a.W + (int64_t)(id >= 0 ? id : 0) * a.hidden;
+    }
+}
+
+// z_k = (wave sum of the lanes' partial dot products) / tau for the real
+// slots among k0 .. k0 + 3, written by lane 0
+__device__ __forceinline__ void store_z4(float* z, const float (&part)[4], int k0, int k,
+                                         float inv_tau, int lane) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float zc = wave_sum(part[c]) * inv_tau;
+        if (lane == 0 && k0 + c < k) z[k0 + c] = zc;
+    }
+}
+
 }  // namespace
 
 // One wave per row: the K candidate logits z_k = H[n] . W[id_k] / tau_n
@@ -111,44 +136,68 @@ __global__ __launch_bounds__(kThreads) void cand_kl_fwd_kernel(CandFwdArgs a) {
     const float inv_tau = 1.0f / tau;
     const bf16_bits* hrow = a.H + row * a.hidden;
     float* z = zs[wave];
-    for (int k0 = 0; k0 < k; k0 += 4) {
-        float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        // W rows of the four candidates; a padding slot (or one past k)
-        // reads row 0 and its z is never used (every use below checks the
-        // id), so the five loads of a segment are unconditional and in
-        // flight together instead of each waiting behind a branch join
-        const bf16_bits* wr[4];
+    if (a.hidden % (2 * kSeg) == 0 && a.hidden <= kHoldSeg * kSeg) {
+        // the row of H stays in registers (at most 8 segments, 32 registers
+        // per lane), so each group of candidates loads only its W rows:
+        // re-reading H for every group added a quarter to the bytes moved
+        const int nseg = a.hidden / kSeg;
+        uint4 hv[kHoldSeg];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int32_t id = k0 + c < k ? idr[k0 + c] : -1;
-            wr[c] = a.W + (int64_t)(id >= 0 ? id : 0) * a.hidden;
+        for (int s = 0; s < kHoldSeg; ++s)
+            hv[s] = s < nseg ? *reinterpret_cast<const uint4*>(hrow + lane * 8 + s * kSeg)
+                             : make_uint4(0, 0, 0, 0);
+        for (int k0 = 0; k0 < k; k0 += 4) {
+            const bf16_bits* wr[4];
+            cand_rows4(a, idr, k0, wr);
+            float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            // two segments' eight W loads at a time, then their products in
+            // ascending segment order
+#pragma unroll
+            for (int s = 0; s < kHoldSeg; s += 2) {
+                if (s < nseg) {
+                    uint4 w0[4], w1[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        w0[c] = *reinterpret_cast<const uint4*>(wr[c] + lane * 8 + s * kSeg);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        w1[c] = *reinterpret_cast<const uint4*>(wr[c] + lane * 8 + (s + 1) * kSeg);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        part[c] = dot8(hv[s + 1], w1[c], dot8(hv[s], w0[c], part[c]));
+                }
+            }
+            store_z4(z, part, k0, k, inv_tau, lane);
         }
-        // two segments' ten loads at a time, then their products in
-        // ascending segment order (the same sums as one segment at a time)
-        int64_t h = lane * 8;
-        for (; h + kSeg < a.hidden; h += 2 * kSeg) {
-            const uint4 hv0 = *reinterpret_cast<const uint4*>(hrow + h);
-            const uint4 hv1 = *reinterpret_cast<const uint4*>(hrow + h + kSeg);
-            uint4 w0[4], w1[4];
+    } else {
+        for (int k0 = 0; k0 < k; k0 += 4) {
+            const bf16_bits* wr[4];
+            cand_rows4(a, idr, k0, wr);
+            float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            // two segments' ten loads (H and four W rows each) at a time, then
+            // their products in ascending segment order: per lane the same sums,
+            // in the same order, as the path above
+            int64_t h = lane * 8;
+            for (; h + kSeg < a.hidden; h += 2 * kSeg) {
+                const uint4 hv0 = *reinterpret_cast<const uint4*>(hrow + h);
+                const uint4 hv1 = *reinterpret_cast<const uint4*>(hrow + h + kSeg);
+                uint4 w0[4], w1[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) w0[c] = *reinterpret_cast<const uint4*>(wr[c] + h);
+                for (int c = 0; c < 4; ++c) w0[c] = *reinterpret_cast<const uint4*>(wr[c] + h);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) w1[c] = *reinterpret_cast<const uint4*>(wr[c] + h + kSeg);
+                for (int c = 0; c < 4; ++c) w1[c] = *reinterpret_cast<const uint4*>(wr[c] + h + kSeg);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) part[c] = dot8(hv1, w1[c], dot8(hv0, w0[c], part[c]));
-        }
-        if (h < a.hidden) {
-            const uint4 hv = *reinterpret_cast<const uint4*>(hrow + h);
-            uint4 wv[4];
+                for (int c = 0; c < 4; ++c) part[c] = dot8(hv1, w1[c], dot8(hv0, w0[c], part[c]));
+            }
+            if (h < a.hidden) {
+                const uint4 hv = *reinterpret_cast<const uint4*>(hrow + h);
+                uint4 wv[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) wv[c] = *reinterpret_cast<const uint4*>(wr[c] + h);
+                for (int c = 0; c < 4; ++c) wv[c] = *reinterpret_cast<const uint4*>(wr[c] + h);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) part[c] = dot8(hv, wv[c], part[c]);
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const float zc = wave_sum(part[c]) * inv_tau;
-            if (lane == 0 && k0 + c < k) z[k0 + c] = zc;
+                for (int c = 0; c < 4; ++c) part[c] = dot8(hv, wv[c], part[c]);
+            }
+            store_z4(z, part, k0, k, inv_tau, lane);
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

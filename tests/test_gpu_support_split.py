@@ -53,7 +53,9 @@ def test_support_logprob_entry_equals_lp_of_the_combined_entry():
     grad_check("dW", bf16_to_np(W.grad), ref["dW"])
 
 
-@pytest.mark.parametrize("hidden", [512, 192, 1088])
+# 1024 and 3072 take the forward path that keeps the row of H in registers
+# (hidden a multiple of 1024, at most 4096); the others stream H with W
+@pytest.mark.parametrize("hidden", [512, 192, 1088, 1024, 3072])
 def test_kl_only_against_oracle(hidden):
     inp = _inputs(hidden=hidden, seed=710 + hidden)
     inp.ids[7, 3] = inp.ids[7, 0]          # a duplicate id: two entries in one dW bucket
@@ -83,8 +85,9 @@ def test_kl_only_matches_the_dense_entry():
     rel_check("kl gather vs dense", to_np(got["kl"]), to_np(kl), rel=2e-4, floor=1e-6)
 
 
-def test_kl_only_with_temperature_and_autograd():
-    inp = _inputs(seed=730)
+@pytest.mark.parametrize("hidden", [512, 2048])
+def test_kl_only_with_temperature_and_autograd(hidden):
+    inp = _inputs(hidden=hidden, seed=730)
     d = Dev(inp)
     r = np.random.default_rng(4).uniform(0.5, 2.0, size=inp.wl.n).astype(np.float32)
     rt = dev_f32(r)
@@ -99,8 +102,9 @@ def test_kl_only_with_temperature_and_autograd():
     grad_check("dW", bf16_to_np(W.grad), ref["dW"])
 
 
-def test_padded_lists_dense_and_kl_only():
-    inp = _inputs(seed=740, pad_frac=0.3)
+@pytest.mark.parametrize("hidden", [512, 2048])
+def test_padded_lists_dense_and_kl_only(hidden):
+    inp = _inputs(hidden=hidden, seed=740, pad_frac=0.3)
     inp.ids[11, :] = -1                    # a row with no real candidate
     d = Dev(inp)
     lp, kl, lse, _ = lm.support_forward(d.H, d.W, d.ids, d.ref_logq, 512, padded=True)
