@@ -497,13 +497,17 @@ def cpu_baseline(wl, inp, target_s, entry=None):
             oracle.grad_weight(dz[:, v0:v0 + 8192], inp.H, rows, threads=threads)
         return time.perf_counter() - t0
 
-    probe_rows = rng.choice(wl.n, size=4, replace=False)
-    t_probe = one(probe_rows)
-    per_row = t_probe / 4
-    n_rows = int(max(4, min(1024, target_s / max(per_row, 1e-6))))
+    # two probes: the slope between them is the cost of a row without the
+    # call's fixed part, so the timed sample lands near target_s
+    t4 = one(rng.choice(wl.n, size=4, replace=False))
+    t16 = one(rng.choice(wl.n, size=16, replace=False))
+    per_row = (t16 - t4) / 12 if t16 > t4 else t16 / 16
+    fixed = max(0.0, t16 - 16 * per_row)
+    n_rows = int(max(4, min(1024, (target_s - fixed) / max(per_row, 1e-6))))
     n_rows = (n_rows // 4) * 4
     rows = rng.choice(wl.n, size=n_rows, replace=False)
-    log(f"cpu baseline: probe {t_probe:.2f}s for 4 rows; timing {n_rows} rows on {threads} threads")
+    log(f"cpu baseline: probes {t4:.2f}s for 4 rows, {t16:.2f}s for 16; "
+        f"timing {n_rows} rows on {threads} threads")
     dt = one(rows)
     return {
         "value": round(n_rows / dt, 4),
