@@ -241,6 +241,33 @@ def test_more_candidates_than_wave_lanes(k, pad):
     assert torch.equal(lp, lp2) and torch.equal(kl, kl2) and torch.equal(dH, dH2) and torch.equal(dW, dW2)
 
 
+@pytest.mark.parametrize("k, pad", [(67, 0.25), (1024, 0.0)])
+def test_kl_only_register_path_candidate_counts(k, pad):
+    """The KL-only forward's path that keeps the row of H in registers
+    (hidden 1024) with a candidate count whose last group of four is ragged
+    (67) and with the largest count (1024); padding slots, a row with no real
+    candidate, and a last workgroup holding only two rows (n = 130)."""
+    padded = pad > 0.0
+    inp = _inputs(n=130, hidden=1024, vocab=3000, k=k, seed=870 + k, pad_frac=pad)
+    if padded:
+        inp.ids[129, :] = -1
+    d = Dev(inp)
+    got = _kl_only(d, padded=padded)
+    torch.cuda.synchronize()
+    ref = oracle.run(oracle.ENTRY_SUPPORT_KL, inp.H, inp.W, ids=inp.ids, ref_logq=inp.ref_logq,
+                     grad_kl=inp.grad_kl, padded=padded)
+    rel_check("kl", to_np(got["kl"]), ref["kl"])
+    rel_check("log p_hat", to_np(got["log_phat"]), ref["log_phat"])
+    grad_check("dH", bf16_to_np(got["dH"]), ref["dH"])
+    grad_check("dW", bf16_to_np(got["dW"]), ref["dW"])
+    if padded:
+        assert got["kl"][129].item() == 0.0 and torch.all(got["dH"][129] == 0)
+    again = _kl_only(d, padded=padded)
+    torch.cuda.synchronize()
+    for key in ("kl", "log_phat", "dH", "dW"):
+        assert torch.equal(got[key], again[key]), key
+
+
 @pytest.mark.parametrize("pad", [0.0, 0.2])
 def test_maximum_candidate_count(pad):
     """k = 1024, the largest count the library accepts: sixteen 64-id batches
