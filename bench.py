@@ -180,8 +180,8 @@ def main():
     bwd_avg_ms = float(np.mean(bwd_ms))
     bwd_achieved = 3.0 * fwd_flops / (bwd_avg_ms * 1e-3) / 1e12
     out["roofline_backward"] = {
-        "kernels": "bwd_logit_grad_kernel + bwd_dw_kernel + bwd_dh_kernel, one of each per vocabulary "
-                   "chunk, with the coefficient pass",
+        "kernels": "per vocabulary chunk bwd_logit_grad_kernel, then the dW and dH contractions (one "
+                   "bwd_dwdh_kernel launch, or bwd_dw_kernel and bwd_dh_kernel), with the coefficient pass",
         "bound": "mfma",
         "achieved": round(bwd_achieved, 2),
         "peak": BF16_PEAK_TFLOPS,
