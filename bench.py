@@ -90,6 +90,10 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
+    import __graft_entry__
+
+    __graft_entry__.ensure_built()   # builds only in a fresh checkout
+
     import torch
 
     import chunked_lm_head_amd as lm

@@ -13,6 +13,14 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long-running CPU test")
 
 
+def pytest_sessionstart(session):
+    # a fresh checkout has no built library: build it once, before any test
+    # loads it (an existing build is used as it is)
+    import __graft_entry__
+
+    __graft_entry__.ensure_built()
+
+
 @pytest.fixture(scope="session")
 def gpu_available():
     import torch
