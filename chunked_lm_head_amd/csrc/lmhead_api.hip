@@ -50,7 +50,8 @@ struct Layout {
     size_t htfrag;                    // backward: H^T in fragment order, [n_pad / 32][hid_pad / 16] blocks
     int64_t hfrag_bytes, htfrag_bytes, hid_pad;
     int64_t group;    // chunks per recompute launch (grad_group)
-    int64_t g_cols;   // columns of the dL/dz region (grad_cols)
+    int64_t g_cols;   // columns of the dL/dz region (grad_cols, or a pair's columns)
+    bool pair;        // consecutive chunks share one dH pass (pair_chunks)
     // backward regions
     size_t coef_a, coef_c, G, dh_acc;
     size_t dh_part;   // fp32 partial dH tiles of the K-split (few row tiles only)
@@ -135,6 +136,34 @@ int64_t grad_group(int64_t n_pad, int64_t w_pad, int64_t vocab, int64_t chunk) {
     return g > 1 ? g : 1;
 }
 
+// Two consecutive chunks share one dH pass when each chunk has enough dH
+// tiles to fill the compute units by itself (no K-split): chunk c (even)
+// and c + 1 keep their dL/dz side by side in one region of both chunks'
+// columns, each chunk's dW runs after its recompute as usual, and after the
+// second recompute one dH contraction runs over both chunks' columns (W rows
+// v0 .. v0 + 2 chunk are contiguous, and an accepted chunk is a multiple of
+// 256 columns, so the region's columns are the W rows in order). The fp32 running sum of dH is then read and written once
+// per pair instead of once per chunk; an odd last chunk has a pass of its
+// own. The pair's dH sum is one K loop over ascending columns, i.e. what a
+// chunk twice as wide would sum; forward outputs and dW are unchanged.
+// pair_cols: the region a pair needs, min(2 padded chunks, V, the widest
+// accepted chunk), sized whenever the dH tiles alone fill the units (also for
+// a chunk too wide to pair), so that the workspace never shrinks as the chunk
+// widens. Both depend on the shape alone.
+bool dh_fills_units(int64_t n_pad, int64_t hidden) {
+    return (n_pad / kTile) * cdiv(hidden, kTile) >= kComputeUnits;
+}
+int64_t pair_cols(int64_t n_pad, int64_t hidden, int64_t vocab, int64_t w_pad) {
+    if (!dh_fills_units(n_pad, hidden)) return 0;
+    int64_t c = 2 * w_pad;
+    const int64_t all = round_up(vocab, kTile);
+    c = c < all ? c : all;
+    return c < kMaxChunkPad ? c : kMaxChunkPad;
+}
+bool pair_chunks(int64_t n_pad, int64_t hidden, int64_t vocab, int64_t chunk, int64_t group) {
+    return group == 1 && dh_fills_units(n_pad, hidden) && chunk < vocab && 2 * chunk <= kMaxChunkPad;
+}
+
 Layout plan(const lmhead_problem& p, int entry) {
     Layout L{};
     L.n = p.n;
@@ -204,6 +233,11 @@ Layout plan(const lmhead_problem& p, int entry) {
     L.coef_c = take(4 * L.n * L.k);
     L.group = grad_group(L.n_pad, L.w_pad, L.vocab, L.chunk);
     L.g_cols = grad_cols(L.n_pad, L.w_pad, L.vocab);
+    L.pair = pair_chunks(L.n_pad, L.hidden, L.vocab, L.chunk, L.group);
+    {
+        const int64_t pc = pair_cols(L.n_pad, L.hidden, L.vocab, L.w_pad);
+        L.g_cols = pc > L.g_cols ? pc : L.g_cols;
+    }
     L.G = take(2 * L.n_pad * L.g_cols);
     L.dh_acc = take(4 * L.n * L.hidden);
     {
@@ -613,6 +647,7 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
     const int64_t tiles_rows = L.n_pad / kTile;
     const int64_t tiles_hidden = cdiv(L.hidden, kTile);
     const int64_t g_stride = L.n_pad * L.w_pad;
+    const int64_t g_pitch = L.pair ? L.g_cols : 0;   // columns per block row of the region (0: per chunk)
     const float* part_in = (const float*)(w + L.dh_part);
     float* part = (float*)(w + L.dh_part);
     float* dh_sum = dH_acc != nullptr ? dH_acc : (float*)(w + L.dh_acc);
@@ -634,6 +669,7 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
         da.g_stride = g_stride;
         da.tiles_m = L.hid_pad / kTile;
         da.tiles_n = round_up(width, kTile) / kTile;
+        da.g_pitch = g_pitch;
         da.dW = (bf16_bits*)dW;
         da.dw_acc = dW_acc;
         return da;
@@ -656,6 +692,7 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
         ha.keep_acc = dH_acc != nullptr;
         ha.dh_acc = dh_sum;
         ha.dH = (bf16_bits*)dH;
+        ha.g_pitch = g_pitch;
         return ha;
     };
     auto split_of = [&](int64_t c, int64_t chunks, int64_t slices, int64_t w_pad) {
@@ -672,8 +709,11 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
     };
     const unsigned join_grid = grid_1d(L.n * L.hidden / 4, kThreads, 4096);
     const int64_t n_dh = want_dh ? tiles_rows * tiles_hidden : 0;
+    // a pair's second chunk: its dL/dz goes C_pad columns into the region (C_pad / 32 blocks of 512)
     for (int64_t c = 0; c < nchunks; c += L.group) {
         const int64_t ng = (nchunks - c) < L.group ? (nchunks - c) : L.group;
+        const bool second = L.pair && (c & 1);
+        bf16_bits* const slot = G + (second ? 16 * L.w_pad : 0);
         {
             // dL/dz of chunks c .. c + ng - 1, one launch
             LogitGradArgs ga;
@@ -694,8 +734,9 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
             ga.ids = ids;
             ga.k = (int)L.k;
             ga.lse = lse;
-            ga.G = G;
+            ga.G = slot;
             ga.g_stride = g_stride;
+            ga.g_pitch = g_pitch;
             ga.tiles_v = L.tiles_v;
             ga.hit_offsets = hit_offsets;
             ga.hit_list = hit_list;
@@ -728,9 +769,30 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
         const int64_t v0 = c * L.chunk;
         const int64_t width = (L.vocab - v0) < L.chunk ? (L.vocab - v0) : L.chunk;
         const int64_t w_pad = round_up(width, kTile);
-        const DwArgs da = dw_args(c, 1, G);
-        const DhArgs ha = dh_args(c, c, G);
+        const DwArgs da = dw_args(c, 1, slot);
         const int64_t n_dw = want_dw ? da.tiles_m * da.tiles_n : 0;
+        if (L.pair) {
+            // the first chunk of a pair: its dW now, its dH with the second's
+            if (!second && c + 1 < nchunks) {
+                if (want_dw) bwd_dw_kernel<<<(unsigned)n_dw, kThreads, 0, s>>>(da);
+                continue;
+            }
+            // dH over the pair (or the odd last chunk) from the region's first column
+            DhArgs ha = dh_args(second ? c - 1 : c, c, G);
+            if (second) {
+                ha.width = L.chunk + width;
+                ha.w_pad = L.w_pad + w_pad;
+            }
+            const int plan_one = dwdh_plan(n_dw, L.n_pad / kTileK, n_dh, ha.w_pad / kTileK);
+            if (plan_one >= 0) {
+                bwd_dwdh_kernel<<<(unsigned)(n_dw + n_dh), kThreads, 0, s>>>(da, ha, plan_one);
+            } else {
+                if (want_dw) bwd_dw_kernel<<<(unsigned)n_dw, kThreads, 0, s>>>(da);
+                if (want_dh) bwd_dh_kernel<<<(unsigned)n_dh, kThreads, 0, s>>>(ha);
+            }
+            continue;
+        }
+        const DhArgs ha = dh_args(c, c, G);
         const int slices = dh_slices(L.n, L.n_pad, L.hidden, w_pad);
         if (want_dh && slices > 1) {
             if (want_dw) bwd_dw_kernel<<<(unsigned)n_dw, kThreads, 0, s>>>(da);

@@ -105,6 +105,7 @@ struct LogitGradArgs {
     const float* lse;
     bf16_bits* G;          // slot g: chunk g's dL/dz, fragment order [n_pad / 16][w_pad / 32]
     int64_t g_stride;      // elements between slots (n_pad x a full chunk's w_pad)
+    int64_t g_pitch;       // columns per block row of the dL/dz region (0: the chunk's own w_pad)
     Temperature T;
     int64_t tiles_v;       // vocabulary tiles of the whole vocabulary (bucket index)
     const int32_t* hit_offsets;   // k > 1: as in FwdTilesArgs
@@ -119,6 +120,7 @@ struct DwArgs {
     const bf16_bits* HTf;  // H^T in fragment order [n_pad / 32][hid_pad / 16] (ht_pack_kernel)
     int64_t n, n_pad, hidden, hid_pad, vocab;
     int64_t v0, chunk, group, g_stride;
+    int64_t g_pitch;            // as in LogitGradArgs
     int64_t tiles_m, tiles_n;   // hidden tiles x column tiles of the first chunk
     bf16_bits* dW;         // [vocab, hidden] or null
     float* dw_acc;         // caller's fp32 [vocab, hidden] (+=) or null
@@ -127,7 +129,8 @@ struct DwArgs {
 struct DhArgs {
     const bf16_bits* G;    // dL/dz of the chunk in fragment order [n_pad / 16][w_pad / 32] (pslot lanes)
     const bf16_bits* Wc;   // first row of the chunk: [width, hidden]
-    int64_t n, n_pad, hidden, width, w_pad;
+    int64_t n, n_pad, hidden, width, w_pad;   // a pair of chunks: both chunks' columns, W rows contiguous
+    int64_t g_pitch;       // as in LogitGradArgs
     int64_t tiles_m, tiles_n;
     int first;             // chunk 0 of a fresh sum: dh_acc is written, not read
     int last;              // last chunk: the bf16 dH is written (if dH is set)

@@ -638,7 +638,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_logit_grad_kernel(LogitGradAr
             // block (nb, cb) packs row 16 nb + l % 16, columns 32 cb + 8 (l / 16)
             // .. + 8 and stores them in slot pslot(l) of the block (each block
             // one contiguous 1 KB store)
-            const int64_t wb = w_pad / 32;
+            const int64_t wb = (a.g_pitch > 0 ? a.g_pitch : w_pad) / 32;
             const int64_t cblk0 = col0 / 32;
             const int rl = lane & 15, cg = 8 * (lane >> 4);
             bf16_bits* gdst = Gc + ((m0 / 16) * wb + cblk0) * 512 + pslot(lane) * 8;
@@ -688,7 +688,7 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int64_t bid, const Stag
     A.koff = 0;
     A.perm = 0;
     DaB B;
-    B.ld = w_pad / 32 * 1024;
+    B.ld = (a.g_pitch > 0 ? a.g_pitch : w_pad) / 32 * 1024;
     B.base = reinterpret_cast<const char*>(a.G + g * a.g_stride) + (n0 / 32) * 1024;
     B.rows = 0;
     B.n0 = 0;
@@ -754,7 +754,7 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int64_t bid, const Stag
 // MN-major (k = chunk row, mn = hidden), from k row k0.
 __device__ __forceinline__ DaA g_tile(const DhArgs& a, int64_t m0, int64_t k0) {
     DaA A;
-    A.kblk = a.w_pad / 32 * 1024;
+    A.kblk = (a.g_pitch > 0 ? a.g_pitch : a.w_pad) / 32 * 1024;
     A.base = reinterpret_cast<const char*>(a.G) + (m0 / 16) * A.kblk;
     A.koff = (k0 / 32) * 1024;
     A.perm = 1;
