@@ -50,8 +50,8 @@ struct Layout {
     size_t htfrag;                    // backward: H^T in fragment order, [n_pad / 32][hid_pad / 16] blocks
     int64_t hfrag_bytes, htfrag_bytes, hid_pad;
     int64_t group;    // chunks per recompute launch (grad_group)
-    int64_t g_cols;   // columns of the dL/dz region (grad_cols, or a pair's columns)
-    bool pair;        // consecutive chunks share one dH pass (pair_chunks)
+    int64_t g_cols;   // columns of the dL/dz region (grad_cols, or a dH pass's columns)
+    bool pair;        // kDhPass consecutive chunks share one dH pass (pair_chunks)
     // backward regions
     size_t coef_a, coef_c, G, dh_acc;
     size_t dh_part;   // fp32 partial dH tiles of the K-split (few row tiles only)
@@ -136,32 +136,34 @@ int64_t grad_group(int64_t n_pad, int64_t w_pad, int64_t vocab, int64_t chunk) {
     return g > 1 ? g : 1;
 }
 
-// Two consecutive chunks share one dH pass when each chunk has enough dH
-// tiles to fill the compute units by itself (no K-split): chunk c (even)
-// and c + 1 keep their dL/dz side by side in one region of both chunks'
-// columns, each chunk's dW runs after its recompute as usual, and after the
-// second recompute one dH contraction runs over both chunks' columns (W rows
-// v0 .. v0 + 2 chunk are contiguous, and an accepted chunk is a multiple of
-// 256 columns, so the region's columns are the W rows in order). The fp32 running sum of dH is then read and written once
-// per pair instead of once per chunk; an odd last chunk has a pass of its
-// own. The pair's dH sum is one K loop over ascending columns, i.e. what a
-// chunk twice as wide would sum; forward outputs and dW are unchanged.
-// pair_cols: the region a pair needs, min(2 padded chunks, V, the widest
+// Four consecutive chunks share one dH pass when each chunk has enough dH
+// tiles to fill the compute units by itself (no K-split): chunks 4p .. 4p + 3
+// keep their dL/dz side by side in one region of the pass's columns, each
+// chunk's dW runs after its recompute as usual, and after the pass's last
+// recompute one dH contraction runs over all of the pass's columns (W rows
+// v0 .. v0 + 4 chunk are contiguous, and an accepted chunk is a multiple of
+// 256 columns, so the region's columns are the W rows in order). The fp32
+// running sum of dH is then read and written once per pass instead of once
+// per chunk; the vocabulary's last pass may hold fewer chunks. A pass's dH
+// sum is one K loop over ascending columns, i.e. what a chunk four times as
+// wide would sum; forward outputs and dW are unchanged.
+// pair_cols: the region a pass needs, min(4 padded chunks, V, the widest
 // accepted chunk), sized whenever the dH tiles alone fill the units (also for
-// a chunk too wide to pair), so that the workspace never shrinks as the chunk
-// widens. Both depend on the shape alone.
+// a chunk too wide to share a pass), so that the workspace never shrinks as
+// the chunk widens. Both depend on the shape alone.
+constexpr int64_t kDhPass = 4;   // chunks per dH pass where they share one
 bool dh_fills_units(int64_t n_pad, int64_t hidden) {
     return (n_pad / kTile) * cdiv(hidden, kTile) >= kComputeUnits;
 }
 int64_t pair_cols(int64_t n_pad, int64_t hidden, int64_t vocab, int64_t w_pad) {
     if (!dh_fills_units(n_pad, hidden)) return 0;
-    int64_t c = 2 * w_pad;
+    int64_t c = kDhPass * w_pad;
     const int64_t all = round_up(vocab, kTile);
     c = c < all ? c : all;
     return c < kMaxChunkPad ? c : kMaxChunkPad;
 }
 bool pair_chunks(int64_t n_pad, int64_t hidden, int64_t vocab, int64_t chunk, int64_t group) {
-    return group == 1 && dh_fills_units(n_pad, hidden) && chunk < vocab && 2 * chunk <= kMaxChunkPad;
+    return group == 1 && dh_fills_units(n_pad, hidden) && chunk < vocab && kDhPass * chunk <= kMaxChunkPad;
 }
 
 Layout plan(const lmhead_problem& p, int entry) {
@@ -709,11 +711,12 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
     };
     const unsigned join_grid = grid_1d(L.n * L.hidden / 4, kThreads, 4096);
     const int64_t n_dh = want_dh ? tiles_rows * tiles_hidden : 0;
-    // a pair's second chunk: its dL/dz goes C_pad columns into the region (C_pad / 32 blocks of 512)
     for (int64_t c = 0; c < nchunks; c += L.group) {
         const int64_t ng = (nchunks - c) < L.group ? (nchunks - c) : L.group;
-        const bool second = L.pair && (c & 1);
-        bf16_bits* const slot = G + (second ? 16 * L.w_pad : 0);
+        // position of chunk c in its dH pass: its dL/dz goes pos x C_pad
+        // columns into the region (C_pad / 32 blocks of 512 elements each)
+        const int64_t pos = L.pair ? c % kDhPass : 0;
+        bf16_bits* const slot = G + pos * 16 * L.w_pad;
         {
             // dL/dz of chunks c .. c + ng - 1, one launch
             LogitGradArgs ga;
@@ -772,17 +775,15 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
         const DwArgs da = dw_args(c, 1, slot);
         const int64_t n_dw = want_dw ? da.tiles_m * da.tiles_n : 0;
         if (L.pair) {
-            // the first chunk of a pair: its dW now, its dH with the second's
-            if (!second && c + 1 < nchunks) {
+            // a chunk before the last of its pass: its dW now, its dH with the pass
+            if (pos + 1 < kDhPass && c + 1 < nchunks) {
                 if (want_dw) bwd_dw_kernel<<<(unsigned)n_dw, kThreads, 0, s>>>(da);
                 continue;
             }
-            // dH over the pair (or the odd last chunk) from the region's first column
-            DhArgs ha = dh_args(second ? c - 1 : c, c, G);
-            if (second) {
-                ha.width = L.chunk + width;
-                ha.w_pad = L.w_pad + w_pad;
-            }
+            // dH over the pass's chunks (the last pass may hold fewer) from the region's first column
+            DhArgs ha = dh_args(c - pos, c, G);
+            ha.width = pos * L.chunk + width;
+            ha.w_pad = pos * L.w_pad + w_pad;
             const int plan_one = dwdh_plan(n_dw, L.n_pad / kTileK, n_dh, ha.w_pad / kTileK);
             if (plan_one >= 0) {
                 bwd_dwdh_kernel<<<(unsigned)(n_dw + n_dh), kThreads, 0, s>>>(da, ha, plan_one);

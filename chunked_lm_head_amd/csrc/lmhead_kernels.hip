@@ -858,7 +858,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(DhArgs a) {
 __global__ __launch_bounds__(kThreads, 1) void bwd_dwdh_kernel(DwArgs dw, DhArgs dh, int dh_first) {
     LMHEAD_STAGE_ARRAYS;
     const int64_t bid = blockIdx.x;
-    const int64_t n_first = dh_first ? dh.tiles_m * dh.tiles_n : dw.tiles_m * dw.tiles_n;
+    const int64_t n_first = dh_first ? dh.tiles_m * dh.tiles_n : dw.tiles_m * dw.tiles_n * dw.group;
     const bool take_dh = dh_first ? bid < n_first : bid >= n_first;
     const int64_t local = bid < n_first ? bid : bid - n_first;
     if (take_dh) dh_tile(dh, local, st);

@@ -163,7 +163,7 @@ typedef struct lmhead_problem {
  * Bytes of device workspace an entry needs ("workspace reporting",
  * [PR8059]). Pure host function: no device is touched. `with_backward`
  * != 0 sizes the workspace for lmhead_loss_bwd (which needs more: dL/dz
- * of one chunk, of two when n and hidden give at least 256 dH tiles of
+ * of one chunk, of four when n and hidden give at least 256 dH tiles of
  * 256 x 256, or of a few at small n, and the fp32 dH accumulator).
  * Returns 0 for an invalid problem or entry.
  */
@@ -181,9 +181,9 @@ typedef struct lmhead_memory_figures {
     size_t forward_bytes;        /* workspace the forward uses */
     size_t partials_bytes;       /* forward: (max, sum-exp) per 256-column tile and row */
     size_t dz_chunk_bytes;       /* backward: dL/dz of the chunks one recompute launch
-                                    covers (dz_group of them), or of the two chunks
+                                    covers (dz_group of them), or of the four chunks
                                     that share a dH pass (at least 256 dH tiles:
-                                    min(2 chunks, vocab) columns), bf16 */
+                                    min(4 chunks, vocab) columns), bf16 */
     size_t dh_acc_bytes;         /* backward: fp32 running sum of dH over the chunks */
     size_t caller_output_bytes;  /* buffers the caller allocates: the entry's fp32 outputs
                                     (loss / logp / lp, kl, lse), plus bf16 dH and dW
@@ -347,9 +347,9 @@ int lmhead_support_kl(const lmhead_problem* p,
  * get exactly zero gradient. n = 0 writes zeros to dW.
  * dH sums each element in fp32 in a fixed order: a K loop over a dH pass's
  * columns in ascending order, added to the running sum pass by pass. A pass
- * is one chunk, or two consecutive chunks (0 and 1, 2 and 3, ...; an odd last
- * chunk alone) when the chunk is a multiple of 256 narrower than vocab and n
- * and hidden give at least 256 dH tiles; at small n a chunk's columns are
+ * is one chunk, or four consecutive chunks (0-3, 4-7, ...; the last pass may
+ * hold fewer) when the chunk is narrower than vocab and n and hidden give at
+ * least 256 dH tiles; at small n a chunk's columns are
  * split into K slices joined in slice order. The pass plan depends on the
  * shape alone. dW sums over all n rows in one K loop, whatever the chunk.
  */

@@ -72,9 +72,10 @@ def test_workspace_size_rules():
     assert ws(_p(k=64), lm.ENTRY_SUPPORT, 0) > ws(_p(k=8), lm.ENTRY_SUPPORT, 0)
     assert ws(_p(chunk=512), 0, 0) == ws(_p(chunk=256), 0, 0)
     # the backward's dL/dz grows with the chunk once a chunk fills the chip
-    # (256 row tiles here); below that, consecutive chunks share a recompute
-    # launch up to 256 tiles, whose dL/dz then takes the same bytes
-    assert ws(_p(n=65536, chunk=512), 0, 1) > ws(_p(n=65536, chunk=256), 0, 1)
+    # (256 row tiles here, whose dL/dz region holds a dH pass of four chunks:
+    # 1024 and 2048 of the 4096 columns); below that, consecutive chunks share
+    # a recompute launch up to 256 tiles, whose dL/dz then takes the same bytes
+    assert ws(_p(n=65536, vocab=4096, chunk=512), 0, 1) > ws(_p(n=65536, vocab=4096, chunk=256), 0, 1)
     assert ws(_p(chunk=512), 0, 1) == ws(_p(chunk=256), 0, 1)
     # headline: 64-bit arithmetic (the dL/dz chunk alone is 2 x 134 MB)
     head = lm.problem(8192, 4096, 151936, 8192, -1, 1, 0)

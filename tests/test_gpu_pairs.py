@@ -1,11 +1,13 @@
-"""GPU parity of the paired dH pass: when a problem has at least 256 dH tiles
-of 256 x 256, two consecutive vocabulary chunks share one dH contraction over
-both chunks' columns (one fp32 running-sum update per pair). The smallest
-shapes where that happens with the full oracle still in reach: 65,536 rows of
-hidden 256 (256 row tiles x 1 hidden tile) and 256-wide chunks, so that each
-chunk fills the 256 compute units with its own recompute tiles. Vocabularies
-of 5 chunks (two pairs and an odd, ragged last chunk) and 4 chunks (the
-second pair ends in the ragged chunk)."""
+"""GPU parity of the shared dH pass: when a problem has at least 256 dH tiles
+of 256 x 256, four consecutive vocabulary chunks share one dH contraction
+over all of their columns (one fp32 running-sum update per pass). The
+smallest shapes where that happens with the full oracle still in reach:
+65,536 rows of hidden 256 (256 row tiles x 1 hidden tile) and 256-wide
+chunks, so that each chunk fills the 256 compute units with its own
+recompute tiles. Vocabularies of 5 chunks (a full pass, then the ragged last
+chunk alone), 7 chunks (a full pass, then a pass of three ending in the
+ragged chunk, as at V = 151,936 with 8192-wide chunks) and 4 chunks (one
+pass ending in the ragged chunk)."""
 import numpy as np
 import pytest
 import torch
@@ -20,13 +22,13 @@ pytestmark = pytest.mark.gpu
 N, HID, CHUNK = 65536, 256, 256
 
 
-@pytest.mark.parametrize("vocab", [1124, 868])
+@pytest.mark.parametrize("vocab", [1124, 1636, 868])
 def test_paired_dh_pass_against_oracle(vocab):
     chunks = -(-vocab // CHUNK)
-    # the dL/dz region holds two chunks: the pairing is on for this shape
+    # the dL/dz region holds four chunks: the shared passes are on for this shape
     r = lm.memory_report(N, HID, vocab, CHUNK, lm.ENTRY_CE_MEAN, True, 1)
-    assert r["dz_group"] == 1 and r["dz_chunk_bytes"] == 2 * N * 2 * CHUNK
-    print(f"[pairs] n={N} hidden={HID} vocab={vocab} chunk={CHUNK} ({chunks} chunks)", flush=True)
+    assert r["dz_group"] == 1 and r["dz_chunk_bytes"] == 2 * N * 4 * CHUNK
+    print(f"[dH passes] n={N} hidden={HID} vocab={vocab} chunk={CHUNK} ({chunks} chunks)", flush=True)
     inp = wlmod.make_inputs(wlmod.custom(n=N, hidden=HID, vocab=vocab, chunk=CHUNK, seed=910,
                                          ignore_frac=0.05))
     d = Dev(inp)
@@ -36,7 +38,7 @@ def test_paired_dh_pass_against_oracle(vocab):
     assert torch.equal(got["dH"], again["dH"]) and torch.equal(got["dW"], again["dW"])
     assert torch.equal(got["loss"], again["loss"])
     ref = oracle.run(lm.ENTRY_CE_MEAN, inp.H, inp.W, targets=inp.targets, grad=inp.grad)
-    rel_check("pairs lse", to_np(got["lse"]), ref["lse"])
-    rel_check("pairs loss", [got["loss"].item()], [ref["loss"]])
-    grad_check("pairs dH", bf16_to_np(got["dH"]), ref["dH"])
-    grad_check("pairs dW", bf16_to_np(got["dW"]), ref["dW"])
+    rel_check("passes lse", to_np(got["lse"]), ref["lse"])
+    rel_check("passes loss", [got["loss"].item()], [ref["loss"]])
+    grad_check("passes dH", bf16_to_np(got["dH"]), ref["dH"])
+    grad_check("passes dW", bf16_to_np(got["dW"]), ref["dW"])

@@ -21,7 +21,7 @@ def test_report_matches_workspace_and_layout():
         r = lm.memory_report(8192, 4096, 151936, 8192, entry, True, k)
         assert r["workspace_bytes"] == _ws(8192, entry, k)
         assert r["chunk"] == 8192 and r["chunks"] == 19
-        assert r["dz_chunk_bytes"] == 2 * 8192 * 16384             # two chunks of G (one dH pass), bf16
+        assert r["dz_chunk_bytes"] == 2 * 8192 * 32768             # four chunks of G (one dH pass), bf16
         assert r["dh_acc_bytes"] == 4 * 8192 * 4096
         assert r["partials_bytes"] == 8 * 594 * 8192
         # H in fragment order, and in the backward H^T too
@@ -127,16 +127,18 @@ def test_dh_split_slices_are_capped():
 
 
 def test_chunk_pairs_share_a_dh_pass_region():
-    """With at least 256 dH tiles (the headline's 512) two consecutive chunks
-    share one dH pass, so the dL/dz region holds min(2 padded chunks, V)
+    """With at least 256 dH tiles (the headline's 512) four consecutive chunks
+    share one dH pass, so the dL/dz region holds min(4 padded chunks, V)
     columns; with fewer dH tiles (n = 2048, hidden 4096: 128) it holds one
     chunk's; the region, and the workspace, never shrink as the chunk widens
     (also past the pairs)."""
     vpad = 152064   # V rounded up to 256
-    assert lm.memory_report(8192, 4096, 151936, 8192, 0, True, 1)["dz_chunk_bytes"] == 2 * 8192 * 16384
+    assert lm.memory_report(8192, 4096, 151936, 8192, 0, True, 1)["dz_chunk_bytes"] == 2 * 8192 * 32768
+    assert lm.memory_report(8192, 4096, 151936, 32768, 0, True, 1)["dz_chunk_bytes"] == 2 * 8192 * 131072
+    assert lm.memory_report(8192, 4096, 151936, 40960, 0, True, 1)["dz_chunk_bytes"] == 2 * 8192 * vpad
     assert lm.memory_report(8192, 4096, 151936, 100096, 0, True, 1)["dz_chunk_bytes"] == 2 * 8192 * vpad
     assert lm.memory_report(8192, 4096, 151936, 152064, 0, True, 1)["dz_chunk_bytes"] == 2 * 8192 * vpad
-    assert lm.memory_report(4096, 4096, 151936, 8192, 0, True, 1)["dz_chunk_bytes"] == 2 * 4096 * 16384
+    assert lm.memory_report(4096, 4096, 151936, 8192, 0, True, 1)["dz_chunk_bytes"] == 2 * 4096 * 32768
     assert lm.memory_report(2048, 4096, 151936, 8192, 0, True, 1)["dz_chunk_bytes"] == 2 * 2048 * 8192
     prev = 0
     for chunk in sorted(set(list(range(256, 151936 + 256, 256 * 13)) + [8192, 75776, 76032, 152064])):
@@ -156,7 +158,7 @@ def test_small_batch_groups_chunks_per_recompute():
     assert r["dz_group"] == 8
     assert r["dz_chunk_bytes"] == 8 * 2 * 256 * 8192
     h = lm.memory_report(8192, 4096, 151936, 8192, 0, True, 1)
-    assert h["dz_group"] == 1 and h["dz_chunk_bytes"] == 2 * 8192 * 16384
+    assert h["dz_group"] == 1 and h["dz_chunk_bytes"] == 2 * 8192 * 32768
     # 3 tiles per chunk (n = 256, chunk 768): 85 chunks, 255 tiles
     assert lm.memory_report(256, 4096, 151936, 768, 0, True, 1)["dz_group"] == 85
     # 1000 columns: 4 chunks of 256 in all
