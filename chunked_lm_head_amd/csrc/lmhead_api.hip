@@ -51,7 +51,7 @@ struct Layout {
     int64_t hfrag_bytes, htfrag_bytes, hid_pad;
     int64_t group;    // chunks per recompute launch (grad_group)
     int64_t g_cols;   // columns of the dL/dz region (grad_cols, or a dH pass's columns)
-    bool pair;        // kDhPass consecutive chunks share one dH pass (pair_chunks)
+    bool dh_pass;     // kDhPass consecutive chunks share one dH pass (shared_dh_pass)
     // backward regions
     size_t coef_a, coef_c, G, dh_acc;
     size_t dh_part;   // fp32 partial dH tiles of the K-split (few row tiles only)
@@ -147,7 +147,7 @@ int64_t grad_group(int64_t n_pad, int64_t w_pad, int64_t vocab, int64_t chunk) {
 // per chunk; the vocabulary's last pass may hold fewer chunks. A pass's dH
 // sum is one K loop over ascending columns, i.e. what a chunk four times as
 // wide would sum; forward outputs and dW are unchanged.
-// pair_cols: the region a pass needs, min(4 padded chunks, V, the widest
+// dh_pass_cols: the region a pass needs, min(4 padded chunks, V, the widest
 // accepted chunk), sized whenever the dH tiles alone fill the units (also for
 // a chunk too wide to share a pass), so that the workspace never shrinks as
 // the chunk widens. Both depend on the shape alone.
@@ -155,14 +155,14 @@ constexpr int64_t kDhPass = 4;   // chunks per dH pass where they share one
 bool dh_fills_units(int64_t n_pad, int64_t hidden) {
     return (n_pad / kTile) * cdiv(hidden, kTile) >= kComputeUnits;
 }
-int64_t pair_cols(int64_t n_pad, int64_t hidden, int64_t vocab, int64_t w_pad) {
+int64_t dh_pass_cols(int64_t n_pad, int64_t hidden, int64_t vocab, int64_t w_pad) {
     if (!dh_fills_units(n_pad, hidden)) return 0;
     int64_t c = kDhPass * w_pad;
     const int64_t all = round_up(vocab, kTile);
     c = c < all ? c : all;
     return c < kMaxChunkPad ? c : kMaxChunkPad;
 }
-bool pair_chunks(int64_t n_pad, int64_t hidden, int64_t vocab, int64_t chunk, int64_t group) {
+bool shared_dh_pass(int64_t n_pad, int64_t hidden, int64_t vocab, int64_t chunk, int64_t group) {
     return group == 1 && dh_fills_units(n_pad, hidden) && chunk < vocab && kDhPass * chunk <= kMaxChunkPad;
 }
 
@@ -235,9 +235,9 @@ Layout plan(const lmhead_problem& p, int entry) {
     L.coef_c = take(4 * L.n * L.k);
     L.group = grad_group(L.n_pad, L.w_pad, L.vocab, L.chunk);
     L.g_cols = grad_cols(L.n_pad, L.w_pad, L.vocab);
-    L.pair = pair_chunks(L.n_pad, L.hidden, L.vocab, L.chunk, L.group);
+    L.dh_pass = shared_dh_pass(L.n_pad, L.hidden, L.vocab, L.chunk, L.group);
     {
-        const int64_t pc = pair_cols(L.n_pad, L.hidden, L.vocab, L.w_pad);
+        const int64_t pc = dh_pass_cols(L.n_pad, L.hidden, L.vocab, L.w_pad);
         L.g_cols = pc > L.g_cols ? pc : L.g_cols;
     }
     L.G = take(2 * L.n_pad * L.g_cols);
@@ -649,7 +649,7 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
     const int64_t tiles_rows = L.n_pad / kTile;
     const int64_t tiles_hidden = cdiv(L.hidden, kTile);
     const int64_t g_stride = L.n_pad * L.w_pad;
-    const int64_t g_pitch = L.pair ? L.g_cols : 0;   // columns per block row of the region (0: per chunk)
+    const int64_t g_pitch = L.dh_pass ? L.g_cols : 0;   // columns per block row of the region (0: per chunk)
     const float* part_in = (const float*)(w + L.dh_part);
     float* part = (float*)(w + L.dh_part);
     float* dh_sum = dH_acc != nullptr ? dH_acc : (float*)(w + L.dh_acc);
@@ -715,7 +715,7 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
         const int64_t ng = (nchunks - c) < L.group ? (nchunks - c) : L.group;
         // position of chunk c in its dH pass: its dL/dz goes pos x C_pad
         // columns into the region (C_pad / 32 blocks of 512 elements each)
-        const int64_t pos = L.pair ? c % kDhPass : 0;
+        const int64_t pos = L.dh_pass ? c % kDhPass : 0;
         bf16_bits* const slot = G + pos * 16 * L.w_pad;
         {
             // dL/dz of chunks c .. c + ng - 1, one launch
@@ -774,7 +774,7 @@ int backward(const lmhead_problem* p, int entry, const void* H, const void* W, c
         const int64_t w_pad = round_up(width, kTile);
         const DwArgs da = dw_args(c, 1, slot);
         const int64_t n_dw = want_dw ? da.tiles_m * da.tiles_n : 0;
-        if (L.pair) {
+        if (L.dh_pass) {
             // a chunk before the last of its pass: its dW now, its dH with the pass
             if (pos + 1 < kDhPass && c + 1 < nchunks) {
                 if (want_dw) bwd_dw_kernel<<<(unsigned)n_dw, kThreads, 0, s>>>(da);

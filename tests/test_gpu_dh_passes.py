@@ -23,7 +23,7 @@ N, HID, CHUNK = 65536, 256, 256
 
 
 @pytest.mark.parametrize("vocab", [1124, 1636, 868])
-def test_paired_dh_pass_against_oracle(vocab):
+def test_shared_dh_pass_against_oracle(vocab):
     chunks = -(-vocab // CHUNK)
     # the dL/dz region holds four chunks: the shared passes are on for this shape
     r = lm.memory_report(N, HID, vocab, CHUNK, lm.ENTRY_CE_MEAN, True, 1)

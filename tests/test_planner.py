@@ -126,7 +126,7 @@ def test_dh_split_slices_are_capped():
     assert lm.memory_report(256, 256, 151936, 32768, 0, True, 1)["dh_split_bytes"] == 16 * 4 * 256 * 256
 
 
-def test_chunk_pairs_share_a_dh_pass_region():
+def test_chunks_share_a_dh_pass_region():
     """With at least 256 dH tiles (the headline's 512) four consecutive chunks
     share one dH pass, so the dL/dz region holds min(4 padded chunks, V)
     columns; with fewer dH tiles (n = 2048, hidden 4096: 128) it holds one
