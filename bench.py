@@ -184,8 +184,9 @@ def main():
     bwd_avg_ms = float(np.mean(bwd_ms))
     bwd_achieved = 3.0 * fwd_flops / (bwd_avg_ms * 1e-3) / 1e12
     out["roofline_backward"] = {
-        "kernels": "per vocabulary chunk bwd_logit_grad_kernel, then the dW and dH contractions (one "
-                   "bwd_dwdh_kernel launch, or bwd_dw_kernel and bwd_dh_kernel), with the coefficient pass",
+        "kernels": "per vocabulary chunk bwd_logit_grad_kernel and its dW tiles; dH once per pass of up to "
+                   "four chunks, with the pass's last dW tiles (bwd_dw_kernel, bwd_dwdh_kernel; small batches "
+                   "split dH), with the coefficient pass",
         "bound": "mfma",
         "achieved": round(bwd_achieved, 2),
         "peak": BF16_PEAK_TFLOPS,
