@@ -42,3 +42,27 @@ def test_shared_dh_pass_against_oracle(vocab):
     rel_check("passes loss", [got["loss"].item()], [ref["loss"]])
     grad_check("passes dH", bf16_to_np(got["dH"]), ref["dH"])
     grad_check("passes dW", bf16_to_np(got["dW"]), ref["dW"])
+
+
+def test_shared_dh_pass_accumulate_and_frozen_sides_bitwise():
+    """At a shape with shared dH passes (a full pass, then a pass of three
+    ending in the ragged chunk): zero-initialised caller accumulators give the
+    plain backward's bits, and a dH-only or dW-only backward (W or H frozen)
+    gives the same dH or dW as the backward of both."""
+    vocab = 1636
+    inp = wlmod.make_inputs(wlmod.custom(n=N, hidden=HID, vocab=vocab, chunk=CHUNK, seed=911,
+                                         ignore_frac=0.05))
+    print(f"[dH passes, accumulate / frozen] n={N} hidden={HID} vocab={vocab} chunk={CHUNK}", flush=True)
+    d = Dev(inp)
+    plain = run_entry(d, lm.ENTRY_CE_MEAN, CHUNK)
+    dh_only = run_entry(d, lm.ENTRY_CE_MEAN, CHUNK, need_dW=False)
+    dw_only = run_entry(d, lm.ENTRY_CE_MEAN, CHUNK, need_dH=False)
+    dH_acc = torch.zeros(d.H.shape, dtype=torch.float32, device="cuda")
+    dW_acc = torch.zeros(d.W.shape, dtype=torch.float32, device="cuda")
+    dH, dW = lm.backward_accumulate(lm.ENTRY_CE_MEAN, d.H, d.W, d.t, plain["lse"], d.grad, CHUNK,
+                                    dH_acc=dH_acc, dW_acc=dW_acc, out_bf16=True)
+    torch.cuda.synchronize()
+    assert dh_only["dW"] is None and dw_only["dH"] is None
+    assert torch.equal(dh_only["dH"], plain["dH"]) and torch.equal(dw_only["dW"], plain["dW"])
+    assert torch.equal(dH, plain["dH"]) and torch.equal(dW, plain["dW"])
+    assert torch.equal(dH, dH_acc.to(torch.bfloat16)) and torch.equal(dW, dW_acc.to(torch.bfloat16))
